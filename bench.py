@@ -1,0 +1,242 @@
+"""Benchmark of the weight-only quantized small-T product on one MI355X.
+
+A step is one qmat_run call (the whole product: stream packed codes and scales, unpack,
+dot products, group scales, reductions, write y) on resident device buffers.  The headline
+workload is the Q4 fused MLP gate+up projection (two 17408 x 5120 matrices as one
+M=34816, K=5120 matrix) at T=1; the other benchmark shapes (Q6 vocab head, Q5 down
+projection with split-K, FP8 row-scaled head and projection, the small Q4 case) at each
+of their token counts are reported in "extra".
+
+Throughput is algorithmic bytes (packed codes + scales read once, x read, y written) per
+second.  Matrices smaller than 512 MB rotate over enough device copies to exceed 512 MB so
+the 256 MB Infinity Cache cannot serve them.  Inputs are seeded synthetic data.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "weight GB/s & % HBM peak, Q4 MLP and Q6 vocab head at T=1 and T=8; µs/call"
+HBM_PEAK_GBS = 8000.0
+PRIMARY = ("q4_gate_up_34816x5120", 1)
+ROTATE_BYTES = 512 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(fmt, M, K, T):
+    """Packed weight information (codes + scales, each read once) + x read + y written."""
+    if fmt == 8:
+        w = M * K + 4 * M
+    else:
+        w = M * K * fmt // 8 + 2 * M * (K // 64)
+    return w + 2 * T * K + 4 * T * M
+
+
+class Resident:
+    """One workload packed and resident on the GPU, with rotation copies."""
+
+    def __init__(self, name, seed=0):
+        import torch
+        import qmat_inputs as qi
+        import weight_only_quant_amd as wq
+        self.name = name
+        t0 = time.time()
+        wl = qi.config(name, seed=seed)
+        self.wl = wl
+        packed = wq.qmat_pack(wl.fmt, wl.codes, wl.scales)
+        dev = torch.from_numpy(packed).cuda()
+        n = max(1, math.ceil(ROTATE_BYTES / packed.size))
+        self.copies = [dev] + [dev.clone() for _ in range(n - 1)]
+        self.handles = [wq.qmat_create(wl.fmt, wl.M, wl.K, c) for c in self.copies]
+        self.x = torch.from_numpy(wl.x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+        self.y = torch.empty((wl.T, wl.M), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] {name}: M={wl.M} K={wl.K} fmt={wl.fmt} packed {packed.size / 1e6:.1f} MB x{len(self.copies)} "
+            f"copies, setup {time.time() - t0:.1f}s")
+
+    def close(self):
+        import weight_only_quant_amd as wq
+        for h in self.handles:
+            wq.qmat_destroy(h)
+        self.handles = []
+        self.copies = []
+
+
+def time_run(res, T, steps, warmup):
+    """Returns (ms_per_step over the timed region, mean per-launch kernel ms from events
+    bracketing each launch on the launch stream)."""
+    import torch
+    import weight_only_quant_amd as wq
+    stream = torch.cuda.current_stream()
+    x, y = res.x[:T], res.y[:T]
+    hs = res.handles
+    for i in range(warmup):
+        wq.qmat_run(hs[i % len(hs)], x, y, T=T, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        wq.qmat_run(hs[i % len(hs)], x, y, T=T, stream=stream)
+        ev[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end)
+    per = [a.elapsed_time(b) for a, b in ev]
+    return total / steps, float(np.mean(per)), float(np.median(per))
+
+
+def cpu_baseline(res, T, target_s=12.0):
+    """The CPU oracle (as it stands) on a bounded sample of rows of the same workload."""
+    import oracle
+    wl = res.wl
+    threads = min(os.cpu_count() or 1, 16)
+    x = wl.x[:T]
+    rows = np.arange(min(wl.M, 512))
+    t0 = time.time()
+    oracle.gemv(wl.fmt, wl.codes, wl.scales, x, rows=rows, nthreads=threads)
+    dt = max(time.time() - t0, 1e-3)
+    n = int(min(wl.M, max(512, len(rows) * target_s / dt)))
+    rows = np.linspace(0, wl.M - 1, n).astype(np.int64)
+    t0 = time.time()
+    oracle.gemv(wl.fmt, wl.codes, wl.scales, x, rows=rows, nthreads=threads)
+    dt = time.time() - t0
+    per_row = alg_bytes(wl.fmt, 1, wl.K, 0)
+    gbs = (n * per_row + 2 * T * wl.K + 4 * T * n) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {wl.M} rows of {wl.name} at T={T} ({dt:.1f} s, fp64 scalar C, {threads} threads)"}
+
+
+def read_ceiling_gbs():
+    """Achieved bandwidth of torch's sum over a 4 GiB buffer (a plain read stream), for context."""
+    import torch
+    buf = torch.ones((1 << 30,), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        buf.sum()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    n = 10
+    for _ in range(n):
+        buf.sum()
+    e.record()
+    torch.cuda.synchronize()
+    gbs = buf.numel() * 4 * n / (s.elapsed_time(e) * 1e-3) / 1e9
+    del buf
+    return round(gbs, 1)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--primary-only", action="store_true", help="skip the other benchmark shapes")
+    ap.add_argument("--only", default=None, help="comma-separated config names for the extra shapes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        log("bench.py: this build runs on one GPU only (the product shards by rows with no "
+            "collective; see the design notes); --gpus must be 1")
+        sys.exit(2)
+
+    import torch
+    import qmat_inputs as qi
+    import weight_only_quant_amd as wq
+    if not os.path.exists(wq.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wq.lib()
+
+    name, T = PRIMARY
+    res = Resident(name)
+    wl = res.wl
+    ms, k_mean, k_med = time_run(res, T, args.steps, args.warmup)
+    ab = alg_bytes(wl.fmt, wl.M, wl.K, T)
+    value = ab / (ms * 1e-3) / 1e9
+    achieved = ab / (k_mean * 1e-3) / 1e9
+    log(f"[bench] {name} T={T}: {ms * 1e3:.2f} us/step, kernel {k_mean * 1e3:.2f} us (median {k_med * 1e3:.2f}), "
+        f"{value:.0f} GB/s step, {achieved:.0f} GB/s kernel")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{name}_T{T}", "format": "Q4 groupwise (64-weight groups, FP16 scales)",
+                   "M": wl.M, "K": wl.K, "T": T, "x": "bf16", "y": "fp32", "global_batch": T,
+                   "parallelism": "single-gpu", "rotation_copies": len(res.copies)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_us_mean": round(k_mean * 1e3, 3), "kernel_us_median": round(k_med * 1e3, 3),
+                     "bytes_per_launch": ab},
+        "us_per_call": round(ms * 1e3, 3),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+    }
+    extra = {}
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline(res, T)
+        log(f"[bench] cpu_baseline {out['cpu_baseline']}")
+    # the same workload at its other token counts
+    for T2 in qi.CONFIGS[name][3]:
+        if T2 == T:
+            continue
+        ms2, km2, _ = time_run(res, T2, args.steps, args.warmup)
+        ab2 = alg_bytes(wl.fmt, wl.M, wl.K, T2)
+        extra[f"{name}_T{T2}"] = {"us_per_call": round(ms2 * 1e3, 3), "kernel_us": round(km2 * 1e3, 3),
+                                  "GBps": round(ab2 / (ms2 * 1e-3) / 1e9, 1),
+                                  "pct_hbm_peak": round(100 * ab2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        log(f"[bench] {name} T={T2}: {extra[f'{name}_T{T2}']}")
+    res.close()
+    del res
+    torch.cuda.empty_cache()
+    if not args.primary_only:
+        names = [n for n in qi.CONFIGS if n != name]
+        if args.only:
+            names = [n for n in names if n in args.only.split(",")]
+        for n in names:
+            r = Resident(n)
+            for T2 in qi.CONFIGS[n][3]:
+                steps = args.steps if r.wl.M * r.wl.K < 1e9 else max(50, args.steps // 4)
+                ms2, km2, _ = time_run(r, T2, steps, args.warmup)
+                ab2 = alg_bytes(r.wl.fmt, r.wl.M, r.wl.K, T2)
+                extra[f"{n}_T{T2}"] = {"us_per_call": round(ms2 * 1e3, 3), "kernel_us": round(km2 * 1e3, 3),
+                                       "GBps": round(ab2 / (ms2 * 1e-3) / 1e9, 1),
+                                       "pct_hbm_peak": round(100 * ab2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+                log(f"[bench] {n} T={T2}: {extra[f'{n}_T{T2}']}")
+            r.close()
+            del r
+            torch.cuda.empty_cache()
+    if not args.no_ceiling:
+        out["read_stream_ceiling_GBps"] = read_ceiling_gbs()
+        log(f"[bench] torch.sum read stream: {out['read_stream_ceiling_GBps']} GB/s")
+    out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+/*
+ * qmat — weight-only quantized small-T matrix-activation product for AMD MI355X (gfx950).
+ *
+ *     y[T][M] = x[T][K] . W^T          1 <= T <= 16, bf16 x, fp32 y
+ *
+ * W is stored in one of two weight-only formats described on the NInfer model cards:
+ *
+ *  - Groupwise Q4 / Q5 / Q6 ("Qwen3.8-27B for NInfer on the RTX 3090", section "What is
+ *    different from the upstream artifact"): every run of 64 weights along a row (along
+ *    K) shares one IEEE binary16 scale; each weight is that scale times a b-bit two's
+ *    complement code c in [-2^(b-1), 2^(b-1)-1].  Scales may be negative (that is how a
+ *    group reaches the most negative code).
+ *        w[i][j] = fp32(scale[i][j/64]) * code[i][j]            (exact in fp32)
+ *  - Row-scaled FP8 ("Qwen3.8-27B NVFP4 for NInfer", introduction and "Artifact"): one
+ *    scale per row times an FP8 value.  The FP8 encoding is OCP E4M3 ("FN": bias 7, no
+ *    infinities, S.1111.111 is NaN, largest finite 448) and the row scale is fp32.
+ *        w[i][j] = fl32(r[i] * e4m3(b[i][j]))
+ *
+ * The library packs W once on the host (qmat_pack) into a layout made for gfx950 wave64
+ * loads, then streams it from HBM once per call (qmat_run).  qmat_dequant expands the
+ * packed matrix back to fp32 for bit-exact checking.
+ *
+ * Conventions for every function:
+ *  - Return value: qmat_status (0 on success).  Nothing throws across this boundary.
+ *    After a failure, qmat_last_error() returns a message for the calling thread.
+ *  - "host" pointers are ordinary CPU memory; "device" pointers are HIP device memory of
+ *    the current device.  The library never frees caller memory.
+ *  - stream: a hipStream_t passed as void* (NULL = the null stream).  qmat_run and
+ *    qmat_dequant are asynchronous on that stream, allocate nothing, never synchronize,
+ *    and may be captured into a HIP graph.
+ *  - Row-major everywhere: x is [T][K] bf16 (K contiguous), y is [T][M] fp32.
+ */
+#ifndef QMAT_H
+#define QMAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QMAT_OK = 0,
+    QMAT_EINVAL = 1, /* bad format, null pointer, bad handle, bad route */
+    QMAT_ESHAPE = 2, /* M < 1, K < 64, K % 64 != 0, T outside [0, 16] */
+    QMAT_ERANGE = 3, /* code outside the format's range, NaN FP8 byte, non-finite scale */
+    QMAT_ESIZE = 4,  /* a buffer is smaller than required, or a launch shape exceeds the workspace */
+    QMAT_EHIP = 5,   /* a HIP runtime call or kernel launch failed */
+    QMAT_ENOMEM = 6  /* host or device allocation failed */
+} qmat_status;
+
+typedef enum {
+    QMAT_Q4 = 4,          /* groupwise 4-bit codes, FP16 scale per 64 weights */
+    QMAT_Q5 = 5,          /* groupwise 5-bit */
+    QMAT_Q6 = 6,          /* groupwise 6-bit */
+    QMAT_FP8_E4M3_ROW = 8 /* OCP E4M3 bytes, fp32 scale per row */
+} qmat_format;
+
+typedef enum {
+    QMAT_ROUTE_AUTO = 0, /* the library's choice for (format, shape, T) */
+    QMAT_ROUTE_VALU = 1, /* vector-ALU dot products; T > 4 runs as several passes */
+    QMAT_ROUTE_MFMA = 2  /* bf16 matrix-core tiles (16 tokens x 16 rows x 32 k) */
+} qmat_route;
+
+typedef struct qmat *qmat_t;
+
+/* Size in bytes of the packed blob for an M x K matrix, or 0 if (fmt, M, K) is invalid.
+ * Layout (all offsets from the start of the blob; 64-row tiles, NT = ceil(M/64);
+ * 128-wide k units, NU = ceil(K/128)):
+ *   codes:  NT * NU * NB blocks of 1024 bytes, NB = 4 (Q4), 5 (Q5), 6 (Q6), 8 (FP8);
+ *   scales: groupwise NT * NU * 256 bytes (fp16 [tile][unit][row%16][group in unit][row/16]);
+ *           FP8 NT * 256 bytes (fp32 [tile][row%16][row/16]).
+ * The byte order inside a block is documented in the repository's design notes.
+ * Rows past M and groups past K/64 are zero-filled. */
+size_t qmat_packed_bytes(int fmt, int64_t M, int64_t K);
+
+/* Pack a matrix into the layout above.  Host only; pure; thread-safe.
+ *   codes:  groupwise: int8 [M][K], each in [-2^(b-1), 2^(b-1)-1];
+ *           FP8: uint8 [M][K] E4M3 bytes (0x7F / 0xFF, the NaNs, are rejected).
+ *   scales: groupwise: uint16 [M][K/64] binary16 bit patterns, finite, any sign;
+ *           FP8: float [M], finite.
+ *   out:    host buffer of out_bytes >= qmat_packed_bytes(fmt, M, K); fully written.
+ * Errors: QMAT_EINVAL (fmt, null), QMAT_ESHAPE (M, K), QMAT_ERANGE (code or scale value,
+ * with the first offending index in the message), QMAT_ESIZE (out_bytes). */
+int qmat_pack(int fmt, int64_t M, int64_t K, const void *codes, const void *scales, void *out,
+              size_t out_bytes);
+
+/* Create a handle over a packed matrix already in device memory.
+ *   packed_dev: device pointer to qmat_pack's output (bytes == qmat_packed_bytes, 16-byte
+ *               aligned).  Borrowed: it must outlive the handle and is never written.
+ * The handle owns a small split-K workspace (device) that it allocates here; calls that
+ * share one handle must therefore be ordered (one stream, or synchronized streams).
+ * Errors: QMAT_EINVAL, QMAT_ESHAPE, QMAT_ESIZE (bytes mismatch), QMAT_ENOMEM, QMAT_EHIP. */
+int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packed_dev, size_t bytes);
+
+/* y = x . W^T.  x: device bf16 [T][K] (16-byte aligned); y: device fp32 [T][M], fully
+ * overwritten.  T == 0 is a no-op.  Asynchronous on stream; no allocation, no sync.
+ * Errors: QMAT_EINVAL (null handle/pointers, misaligned x), QMAT_ESHAPE (T > 16 or T < 0),
+ * QMAT_EHIP (launch failure). */
+int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream);
+
+/* qmat_run with an explicit kernel route and launch shape, for tests and tuning.
+ *   route:  qmat_route.
+ *   waves:  waves per workgroup splitting K inside one workgroup (1, 2, 4 or 8; 0 = auto).
+ *   splits: workgroups splitting K across the grid (>= 1; 0 = auto); the partial sums go
+ *           through the handle's workspace and are added in a fixed order.
+ * Errors: as qmat_run, plus QMAT_EINVAL (route, waves) and QMAT_ESIZE (splits * T * rows
+ * exceeds the workspace reserved at create time, or more splits than k units). */
+int qmat_run_ex(qmat_t handle, const void *x_dev, float *y_dev, int T, int route, int waves,
+                int splits, void *stream);
+
+/* The launch qmat_run would make for T tokens on a route (QMAT_ROUTE_AUTO: the library's
+ * choice): the route taken, waves per workgroup and k splits across workgroups.  Host only.
+ * Errors: QMAT_EINVAL (null argument, bad route), QMAT_ESHAPE (T outside [1, 16]). */
+int qmat_get_plan(qmat_t handle, int T, int route, int *route_out, int *waves, int *splits);
+
+/* Expand the packed matrix to fp32 w [M][K] (device), bit-exact: groupwise
+ * fp32(scale) * code, FP8 fl32(r * e4m3).  For checking; not a fast path. */
+int qmat_dequant(qmat_t handle, float *w_dev, void *stream);
+
+/* Bytes of device workspace the handle holds (0 if none). */
+size_t qmat_workspace_bytes(qmat_t handle);
+
+/* Release the handle and its workspace (not the packed matrix).  NULL is ignored. */
+void qmat_destroy(qmat_t handle);
+
+/* Message describing the calling thread's most recent error ("" if none). */
+const char *qmat_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMAT_H */

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: the library loads, exports every function include/qmat.h
+declares with the binding's signature, and the host-side validation paths return the
+documented status codes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import weight_only_quant_amd as wq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmat.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmat_[a-z_]+)\s*\(", src)))
+
+
+def test_header_lists_the_api():
+    fns = header_functions()
+    assert "qmat_run" in fns and "qmat_pack" in fns and len(fns) >= 9
+
+
+def test_library_exports_every_header_function():
+    L = ctypes.CDLL(wq.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(L, name), name
+    assert set(header_functions()) == set(wq.SIGNATURES)
+
+
+def test_binding_loads():
+    assert wq.lib() is not None
+
+
+def _codes(fmt, M=64, K=128):
+    if fmt == 8:
+        return np.zeros((M, K), np.uint8), np.ones(M, np.float32)
+    return np.zeros((M, K), np.int8), np.zeros((M, K // 64), np.uint16)
+
+
+def _pack_raw(fmt, M, K, codes, scales, out_bytes=None):
+    n = wq.qmat_packed_bytes(fmt, M, K) if out_bytes is None else out_bytes
+    out = np.empty(max(n, 1), np.uint8)
+    st = wq.lib().qmat_pack(fmt, M, K, codes.ctypes.data if codes is not None else None,
+                            scales.ctypes.data if scales is not None else None, out.ctypes.data, n)
+    return st
+
+
+def test_packed_bytes_invalid_is_zero():
+    assert wq.qmat_packed_bytes(3, 64, 128) == 0
+    assert wq.qmat_packed_bytes(4, 0, 128) == 0
+    assert wq.qmat_packed_bytes(4, 64, 100) == 0
+    assert wq.qmat_packed_bytes(4, 64, 0) == 0
+    assert wq.qmat_packed_bytes(4, 64, 64) > 0
+
+
+def test_pack_errors():
+    c, s = _codes(4)
+    assert _pack_raw(7, 64, 128, c, s) == wq.QMAT_EINVAL
+    assert _pack_raw(4, 64, 96, c, s) == wq.QMAT_ESHAPE
+    assert _pack_raw(4, 0, 128, c, s) == wq.QMAT_ESHAPE
+    assert _pack_raw(4, 64, 128, None, s) == wq.QMAT_EINVAL
+    assert _pack_raw(4, 64, 128, c, s, out_bytes=100) == wq.QMAT_ESIZE
+    assert "out_bytes" in wq.qmat_last_error()
+
+
+@pytest.mark.parametrize("fmt,bad", [(4, 8), (4, -9), (5, 16), (5, -17), (6, 32), (6, -33)])
+def test_pack_rejects_out_of_range_codes(fmt, bad):
+    c, s = _codes(fmt)
+    c[3, 77] = bad
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_pack(fmt, c, s)
+    assert e.value.status == wq.QMAT_ERANGE and "row 3 col 77" in str(e.value)
+
+
+def test_pack_accepts_extreme_codes():
+    for fmt in (4, 5, 6):
+        c, s = _codes(fmt)
+        c[0, 0], c[0, 1] = -(1 << (fmt - 1)), (1 << (fmt - 1)) - 1
+        wq.qmat_pack(fmt, c, s)
+
+
+@pytest.mark.parametrize("bits", [0x7C00, 0xFC00, 0x7E00, 0x7C01])
+def test_pack_rejects_nonfinite_half_scales(bits):
+    c, s = _codes(4)
+    s[5, 1] = bits
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_pack(4, c, s)
+    assert e.value.status == wq.QMAT_ERANGE
+
+
+@pytest.mark.parametrize("byte", [0x7F, 0xFF])
+def test_pack_rejects_nan_fp8(byte):
+    c, s = _codes(8)
+    c[2, 9] = byte
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_pack(8, c, s)
+    assert e.value.status == wq.QMAT_ERANGE
+
+
+@pytest.mark.parametrize("val", [np.inf, -np.inf, np.nan])
+def test_pack_rejects_nonfinite_row_scale(val):
+    c, s = _codes(8)
+    s[7] = val
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_pack(8, c, s)
+    assert e.value.status == wq.QMAT_ERANGE
+
+
+def test_create_validation_without_gpu():
+    L = wq.lib()
+    h = ctypes.c_void_p()
+    assert L.qmat_create(None, 4, 64, 128, 16, 100) == wq.QMAT_EINVAL
+    assert L.qmat_create(ctypes.byref(h), 9, 64, 128, 16, 100) == wq.QMAT_EINVAL
+    assert L.qmat_create(ctypes.byref(h), 4, 64, 100, 16, 100) == wq.QMAT_ESHAPE
+    assert L.qmat_create(ctypes.byref(h), 4, 64, 128, None, 100) == wq.QMAT_EINVAL
+    assert L.qmat_create(ctypes.byref(h), 4, 64, 128, 8, wq.qmat_packed_bytes(4, 64, 128)) == wq.QMAT_EINVAL  # misaligned
+    assert L.qmat_create(ctypes.byref(h), 4, 64, 128, 16, 100) == wq.QMAT_ESIZE
+    assert h.value is None
+
+
+def test_run_and_dequant_reject_null_handle():
+    L = wq.lib()
+    assert L.qmat_run(None, 16, 16, 1, None) == wq.QMAT_EINVAL
+    assert L.qmat_run_ex(None, 16, 16, 1, 0, 0, 0, None) == wq.QMAT_EINVAL
+    assert L.qmat_dequant(None, 16, None) == wq.QMAT_EINVAL
+    assert L.qmat_workspace_bytes(None) == 0
+    L.qmat_destroy(None)

@@ -1,0 +1,309 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+  - qmat_dequant must equal the oracle's dequantization bit for bit (sign of zero included);
+  - qmat_run must satisfy |y - y_ref| <= 1e-4 * sum_j |w_ij x_tj| + 1e-6 everywhere, and match
+    bit for bit on inputs where every partial sum is exact in fp32.
+Small shapes span several 64-row tiles with a ragged last tile and odd group counts; the full
+benchmark shapes are checked on sampled rows in the launch configuration the benchmark uses.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qmat_inputs as qi
+import weight_only_quant_amd as wq
+
+pytestmark = pytest.mark.gpu
+
+ROUTES = {"valu": wq.QMAT_ROUTE_VALU, "mfma": wq.QMAT_ROUTE_MFMA}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    wq.lib()
+    return torch.device("cuda:0")
+
+
+def _workload(fmt, M, K, T, seed, mult=0.01):
+    if fmt == 8:
+        return qi.fp8_rows("t", M, K, T, mult, seed)
+    return qi.groupwise("t", fmt, M, K, T, mult, seed)
+
+
+def _x_dev(x_bits):
+    return torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def _check_y(y, wl, label, rows=None):
+    y_ref, A = oracle.gemv(wl.fmt, wl.codes, wl.scales, wl.x, rows=rows)
+    got = y.detach().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        got = got[:, rows]
+    ok, worst, idx = oracle.check(got, y_ref, A)
+    assert ok, f"{label}: worst |err|/(1e-4*A+1e-6) = {worst:.3g} at {idx}: got {got[idx]!r} want {y_ref[idx]!r} A {A[idx]!r}"
+    return worst
+
+
+# ------------------------------------------------------------------ dequant: bit exact
+
+DQ_SHAPES = [(64, 128), (200, 320), (1, 64), (130, 192)]
+
+
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("M,K", DQ_SHAPES)
+def test_dequant_bit_exact(fmt, M, K):
+    say(f"dequant fmt={fmt} M={M} K={K}")
+    wl = _workload(fmt, M, K, 1, 11 + M)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    w = qm.dequant()
+    torch.cuda.synchronize()
+    got = w.cpu().numpy()
+    ref = oracle.dequant_fp8(wl.codes, wl.scales) if fmt == 8 else oracle.dequant_groupwise(fmt, wl.codes, wl.scales)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [4, 5, 6])
+def test_dequant_every_code_edge_scales(fmt):
+    # every code at every position, times +-0, subnormal, largest-normal and ordinary scales
+    say(f"dequant edge fmt={fmt}")
+    lo, hi = -(1 << (fmt - 1)), (1 << (fmt - 1)) - 1
+    n = hi - lo + 1
+    svals = np.array([0.0, -0.0, 2 ** -24, -(2 ** -24), 2 ** -14 - 2 ** -24, 2 ** -14, -1.0, 65504.0,
+                      -65504.0, 0.3333, 1e-3, -7.125], dtype=np.float16).view(np.uint16)
+    G = svals.size
+    M, K = 2 * n + 3, 64 * G
+    r = np.arange(M)[:, None]
+    k = np.arange(K)[None, :]
+    codes = (lo + (r + k) % n).astype(np.int8)
+    scales = np.tile(svals, (M, 1))
+    scales = np.roll(scales, 1, axis=1) if fmt == 5 else scales
+    qm = wq.QMat(fmt, codes, scales)
+    got = qm.dequant().cpu().numpy()
+    ref = oracle.dequant_groupwise(fmt, codes, scales)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_fp8_every_byte_edge_scales():
+    say("dequant fp8 every byte")
+    byts = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    rs = np.array([1.0, -0.75, 0.0123, 3.0e-5, 1.7e-38, 1e-40, 2.5e30, 7.0 / 3.0, 0.0, -0.0], np.float32)
+    M, K = rs.size, 256
+    codes = np.stack([np.roll(np.resize(byts, K), 13 * i) for i in range(M)]).astype(np.uint8)
+    qm = wq.QMat(8, codes, rs)
+    got = qm.dequant().cpu().numpy()
+    ref = oracle.dequant_fp8(codes, rs)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ product: tolerance
+
+RUN_SHAPES = [(200, 320), (64, 1024), (1, 64), (130, 192), (257, 2176)]
+
+
+@pytest.mark.parametrize("route", ["valu", "mfma"])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("M,K", RUN_SHAPES)
+def test_run_parity_small(route, fmt, M, K):
+    wl = _workload(fmt, M, K, 16, 100 + M + K + fmt)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    for T in (1, 2, 3, 4, 5, 8, 13, 16):
+        say(f"run {route} fmt={fmt} M={M} K={K} T={T}")
+        y = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run_ex(qm.handle, xd[:T], y, T, route=ROUTES[route])
+        torch.cuda.synchronize()
+        sub = qi.Workload(wl.name, fmt, M, K, T, wl.codes, wl.scales, wl.x[:T])
+        _check_y(y, sub, f"{route} fmt={fmt} {M}x{K} T={T}")
+
+
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("route", ["valu", "mfma"])
+def test_run_split_shapes_agree(fmt, route):
+    # every (waves, splits) launch shape gives an in-tolerance result; each is deterministic
+    M, K, T = 200, 2176, 4 if route == "valu" else 9
+    wl = _workload(fmt, M, K, T, 7 + fmt)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    for waves in (1, 2, 4, 8):
+        for splits in (1, 2, 3, 5):
+            say(f"split {route} fmt={fmt} waves={waves} splits={splits}")
+            y1 = torch.empty((T, M), device="cuda")
+            y2 = torch.empty((T, M), device="cuda")
+            wq.qmat_run_ex(qm.handle, xd, y1, T, route=ROUTES[route], waves=waves, splits=splits)
+            wq.qmat_run_ex(qm.handle, xd, y2, T, route=ROUTES[route], waves=waves, splits=splits)
+            torch.cuda.synchronize()
+            assert torch.equal(y1, y2)
+            _check_y(y1, wl, f"{route} waves={waves} splits={splits}")
+
+
+def _exact_workload(fmt, M, K, T, seed):
+    """Inputs whose products and partial sums are all exact in fp32: small integer bf16
+    activations and power-of-two scales (FP8: integer-valued E4M3 bytes)."""
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.integers(-4, 5, (T, K)).astype(np.float32)).to(torch.bfloat16)
+    x_bits = x.view(torch.int16).numpy().view(np.uint16)
+    if fmt == 8:
+        ints = rng.integers(-16, 17, (M, K)).astype(np.float32)
+        codes = torch.from_numpy(ints).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        scales = (2.0 ** rng.integers(-6, 3, M)).astype(np.float32)
+    else:
+        lo, hi = -(1 << (fmt - 1)), (1 << (fmt - 1)) - 1
+        codes = rng.integers(lo, hi + 1, (M, K)).astype(np.int8)
+        sg = np.where(rng.random((M, K // 64)) < 0.5, -1.0, 1.0)
+        scales = (sg * 2.0 ** rng.integers(-2, 2, (M, K // 64))).astype(np.float16).view(np.uint16)
+    return qi.Workload("exact", fmt, M, K, T, codes, scales, x_bits)
+
+
+@pytest.mark.parametrize("route", ["valu", "mfma"])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+def test_run_bit_exact_on_exact_inputs(route, fmt):
+    M, K = 130, 1024
+    for T in (1, 4, 8, 16):
+        say(f"exact {route} fmt={fmt} T={T}")
+        wl = _exact_workload(fmt, M, K, T, 3 + T)
+        qm = wq.QMat(fmt, wl.codes, wl.scales)
+        y = torch.empty((T, M), device="cuda")
+        wq.qmat_run_ex(qm.handle, _x_dev(wl.x), y, T, route=ROUTES[route])
+        torch.cuda.synchronize()
+        y_ref, _ = oracle.gemv(fmt, wl.codes, wl.scales, wl.x)
+        assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref)
+
+
+# ------------------------------------------------------------------ degenerate inputs
+
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+def test_zero_and_sparse_codes(fmt):
+    # all-zero codes give exactly zero; one nonzero code per row gives that single product
+    M, K, T = 70, 640, 8
+    wl = _workload(fmt, M, K, T, 21)
+    codes = np.zeros_like(wl.codes)
+    rng = np.random.default_rng(5)
+    cols = rng.integers(0, K, M)
+    for i in range(1, M):
+        codes[i, cols[i]] = (0x38 if fmt == 8 else (-(1 << (fmt - 1)) if i % 2 else (1 << (fmt - 1)) - 1))
+    for route in ("valu", "mfma"):
+        say(f"sparse {route} fmt={fmt}")
+        qm = wq.QMat(fmt, codes, wl.scales)
+        y = torch.empty((T, M), device="cuda")
+        wq.qmat_run_ex(qm.handle, _x_dev(wl.x), y, T, route=ROUTES[route])
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        assert np.all(got[:, 0] == 0)
+        _check_y(y, qi.Workload("s", fmt, M, K, T, codes, wl.scales, wl.x), f"sparse {route}")
+
+
+def test_t_zero_is_noop_and_bad_args():
+    wl = _workload(4, 64, 128, 1, 1)
+    qm = wq.QMat(4, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    y = torch.full((1, 64), 7.0, device="cuda")
+    wq.qmat_run(qm.handle, xd, y, T=0)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_run(qm.handle, xd, y, T=17)
+    assert e.value.status == wq.QMAT_ESHAPE
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_run(qm.handle, xd, y, T=-1)
+    assert e.value.status == wq.QMAT_ESHAPE
+    xbig = torch.zeros(200, dtype=torch.bfloat16, device="cuda")
+    assert wq.lib().qmat_run(qm.handle, xbig.data_ptr() + 2, y.data_ptr(), 1, None) == wq.QMAT_EINVAL
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_run_ex(qm.handle, xd, y, 1, route=5)
+    assert e.value.status == wq.QMAT_EINVAL
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_run_ex(qm.handle, xd, y, 1, waves=3)
+    assert e.value.status == wq.QMAT_EINVAL
+
+
+def test_create_rejects_wrong_size():
+    wl = _workload(6, 64, 128, 1, 1)
+    blob = torch.from_numpy(wq.qmat_pack(6, wl.codes, wl.scales)).cuda()
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_create(6, 64, 192, blob)
+    assert e.value.status == wq.QMAT_ESIZE
+
+
+def test_graph_replay_matches_eager():
+    # the split-K path resets its own arrival counters, so graph replays need no memset.
+    # Garbage from earlier tests is collected first: a handle freed (hipFree) while the
+    # stream captures would invalidate the capture.
+    import gc
+    gc.collect()
+    M, K, T = 320, 4352, 4
+    wl = _workload(5, M, K, T, 77)
+    qm = wq.QMat(5, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    y_eager = torch.empty((T, M), device="cuda")
+    wq.qmat_run_ex(qm.handle, xd, y_eager, T, waves=4, splits=5)
+    torch.cuda.synchronize()
+    y = torch.empty((T, M), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        wq.qmat_run_ex(qm.handle, xd, y, T, waves=4, splits=5, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wq.qmat_run_ex(qm.handle, xd, y, T, waves=4, splits=5)
+    for i in range(4):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i}"
+        wq.qmat_run_ex(qm.handle, xd, y_eager, T, waves=4, splits=5)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ full benchmark shapes
+
+def _sample_rows(M, n=1500, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(64, M))) | set(range(max(0, M - 64), M))
+    rows |= set(rng.integers(0, M, n).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", list(qi.CONFIGS))
+def test_full_size_sampled_rows(name):
+    """Each benchmark shape at every listed T, automatic launch plan (the one the benchmark
+    times): the product on ~1600 sampled rows (first and last tile included) and the
+    dequantization on ~300 sampled rows against the oracle."""
+    _, _, _, Ts, _ = qi.CONFIGS[name]
+    say(f"full {name}: generating")
+    wl = qi.config(name)
+    qm = wq.QMat(wl.fmt, wl.codes, wl.scales)
+    rows = _sample_rows(wl.M)
+    for T in Ts:
+        say(f"full {name} T={T}")
+        xd = _x_dev(wl.x[:T])
+        y = torch.full((T, wl.M), float("nan"), device="cuda")
+        wq.qmat_run(qm.handle, xd, y, T=T)
+        torch.cuda.synchronize()
+        assert not torch.isnan(y).any()
+        sub = qi.Workload(wl.name, wl.fmt, wl.M, wl.K, T, wl.codes, wl.scales, wl.x[:T])
+        worst = _check_y(y, sub, f"{name} T={T}", rows=rows)
+        say(f"  worst ratio {worst:.3g}")
+    say(f"full {name}: dequant")
+    drows = _sample_rows(wl.M, n=200, seed=1)
+    w = qm.dequant()
+    got = w[torch.tensor(drows, device="cuda")].cpu().numpy()
+    del w
+    if wl.fmt == 8:
+        ref = oracle.dequant_fp8(wl.codes[drows], wl.scales[drows])
+    else:
+        ref = oracle.dequant_groupwise(wl.fmt, wl.codes[drows], wl.scales[drows])
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    qm.close()

@@ -1,0 +1,195 @@
+"""weight_only_quant_amd — Python binding of the qmat C ABI (include/qmat.h).
+
+Argument marshalling only: every step of the product runs in the HIP library
+(libqmat.so, built for gfx950).  Host arrays are numpy; device buffers are torch
+tensors (PyTorch supplies device memory and streams, nothing else).  The names are
+those of the C functions.  If the library is missing, importing a function raises:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmat.so")
+
+QMAT_OK, QMAT_EINVAL, QMAT_ESHAPE, QMAT_ERANGE, QMAT_ESIZE, QMAT_EHIP, QMAT_ENOMEM = range(7)
+QMAT_Q4, QMAT_Q5, QMAT_Q6, QMAT_FP8_E4M3_ROW = 4, 5, 6, 8
+QMAT_ROUTE_AUTO, QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA = 0, 1, 2
+FORMATS = (QMAT_Q4, QMAT_Q5, QMAT_Q6, QMAT_FP8_E4M3_ROW)
+MAX_T = 16
+
+# C function name -> (restype, argtypes)
+_i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "qmat_packed_bytes": (_sz, [_int, _i64, _i64]),
+    "qmat_pack": (_int, [_int, _i64, _i64, _vp, _vp, _vp, _sz]),
+    "qmat_create": (_int, [ctypes.POINTER(_vp), _int, _i64, _i64, _vp, _sz]),
+    "qmat_run": (_int, [_vp, _vp, _vp, _int, _vp]),
+    "qmat_run_ex": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _vp]),
+    "qmat_dequant": (_int, [_vp, _vp, _vp]),
+    "qmat_get_plan": (_int, [_vp, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "qmat_workspace_bytes": (_sz, [_vp]),
+    "qmat_destroy": (None, [_vp]),
+    "qmat_last_error": (ctypes.c_char_p, []),
+}
+
+
+class QmatError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"qmat status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libqmat.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950); there is no non-HIP path")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != QMAT_OK:
+        raise QmatError(status, qmat_last_error())
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def qmat_last_error() -> str:
+    return lib().qmat_last_error().decode()
+
+
+def qmat_packed_bytes(fmt: int, M: int, K: int) -> int:
+    return int(lib().qmat_packed_bytes(fmt, M, K))
+
+
+def qmat_pack(fmt: int, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Host pack.  Groupwise: codes int8 [M,K], scales uint16 binary16 bits [M,K/64];
+    FP8: codes uint8 E4M3 bytes [M,K], scales float32 [M].  Returns uint8 [packed_bytes]."""
+    if fmt == QMAT_FP8_E4M3_ROW:
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.float32)
+    else:
+        codes = np.ascontiguousarray(codes, dtype=np.int8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    if codes.ndim != 2:
+        raise ValueError("codes must be 2-D [M, K]")
+    M, K = codes.shape
+    want = (M,) if fmt == QMAT_FP8_E4M3_ROW else (M, K // 64)
+    if scales.shape != want:
+        raise ValueError(f"scales must have shape {want}")
+    n = qmat_packed_bytes(fmt, M, K)
+    out = np.empty(max(n, 1), dtype=np.uint8)
+    _check(lib().qmat_pack(fmt, M, K, codes.ctypes.data, scales.ctypes.data, out.ctypes.data, n))
+    return out[:n]
+
+
+def qmat_create(fmt: int, M: int, K: int, packed_dev) -> int:
+    """packed_dev: a torch uint8 device tensor holding qmat_pack's output (borrowed)."""
+    h = ctypes.c_void_p()
+    _check(lib().qmat_create(ctypes.byref(h), fmt, M, K, packed_dev.data_ptr(), packed_dev.numel()))
+    return h.value
+
+
+def qmat_run(handle: int, x, y, T: Optional[int] = None, stream=None) -> None:
+    """x: bf16 device [T,K]; y: fp32 device [T,M]."""
+    T = x.shape[0] if T is None else T
+    _check(lib().qmat_run(handle, x.data_ptr(), y.data_ptr(), T, _stream_handle(stream)))
+
+
+def qmat_run_ex(handle: int, x, y, T: Optional[int] = None, route: int = QMAT_ROUTE_AUTO,
+                waves: int = 0, splits: int = 0, stream=None) -> None:
+    T = x.shape[0] if T is None else T
+    _check(lib().qmat_run_ex(handle, x.data_ptr(), y.data_ptr(), T, route, waves, splits, _stream_handle(stream)))
+
+
+def qmat_dequant(handle: int, w, stream=None) -> None:
+    """w: fp32 device [M,K]."""
+    _check(lib().qmat_dequant(handle, w.data_ptr(), _stream_handle(stream)))
+
+
+def qmat_get_plan(handle: int, T: int, route: int = QMAT_ROUTE_AUTO):
+    """(route, waves, splits) of the launch qmat_run makes for T tokens."""
+    r, w, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().qmat_get_plan(handle, T, route, ctypes.byref(r), ctypes.byref(w), ctypes.byref(s)))
+    return r.value, w.value, s.value
+
+
+def qmat_workspace_bytes(handle: int) -> int:
+    return int(lib().qmat_workspace_bytes(handle))
+
+
+def qmat_destroy(handle: Optional[int]) -> None:
+    if handle:
+        lib().qmat_destroy(handle)
+
+
+class QMat:
+    """A packed matrix resident on the GPU plus its library handle.
+
+    Holds the device copy of the packed blob (the handle borrows it)."""
+
+    def __init__(self, fmt: int, codes: np.ndarray, scales: np.ndarray, device: str = "cuda"):
+        import torch
+        self.fmt = fmt
+        self.M, self.K = codes.shape
+        packed = qmat_pack(fmt, codes, scales)
+        self.packed = torch.from_numpy(packed).to(device)
+        self.handle = qmat_create(fmt, self.M, self.K, self.packed)
+
+    @classmethod
+    def from_packed(cls, fmt: int, M: int, K: int, packed_dev):
+        self = cls.__new__(cls)
+        self.fmt, self.M, self.K = fmt, M, K
+        self.packed = packed_dev
+        self.handle = qmat_create(fmt, M, K, packed_dev)
+        return self
+
+    def run(self, x, y=None, route: int = QMAT_ROUTE_AUTO, waves: int = 0, splits: int = 0, stream=None):
+        import torch
+        if y is None:
+            y = torch.empty((x.shape[0], self.M), dtype=torch.float32, device=x.device)
+        if route == QMAT_ROUTE_AUTO and not waves and not splits:
+            qmat_run(self.handle, x, y, stream=stream)
+        else:
+            qmat_run_ex(self.handle, x, y, route=route, waves=waves, splits=splits, stream=stream)
+        return y
+
+    def dequant(self, w=None, stream=None):
+        import torch
+        if w is None:
+            w = torch.empty((self.M, self.K), dtype=torch.float32, device=self.packed.device)
+        qmat_dequant(self.handle, w, stream=stream)
+        return w
+
+    def close(self):
+        qmat_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                self.close()
+        except Exception:
+            pass

@@ -1,0 +1,445 @@
+// Host side of the qmat C ABI: argument validation, the packer, launch planning.
+// The public contract is in include/qmat.h; the packed layout in qmat_layout.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <thread>
+#include <vector>
+
+#include "../../include/qmat.h"
+#include "qmat_kernels.h"
+#include "qmat_layout.h"
+
+using namespace qmatk;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return QMAT_OK;
+}
+
+// M and K limits keep every kernel index inside 32-bit tile/unit counts and 64-bit offsets.
+bool shape_ok(int64_t M, int64_t K)
+{
+    return M >= 1 && K >= 64 && K % kGroup == 0 && M <= (1LL << 30) && K <= (1LL << 20) && M * K <= (1LL << 40);
+}
+
+// ------------------------------------------------------------------ packer
+
+struct PackSrc {
+    int fmt;
+    int64_t M, K;
+    const int8_t *codes;    // groupwise
+    const uint8_t *bytes;   // FP8
+    const uint16_t *hs;     // groupwise scales [M][K/64]
+    const float *rs;        // FP8 row scales [M]
+};
+
+// code of (row, k) as the low b bits (two's complement) or the E4M3 byte; 0 outside the matrix
+inline uint32_t code_at(const PackSrc &p, int64_t row, int64_t k)
+{
+    if (row >= p.M || k >= p.K) return 0;
+    if (p.fmt == 8) return p.bytes[row * p.K + k];
+    return (uint32_t)(uint8_t)p.codes[row * p.K + k] & ((1u << p.fmt) - 1u);
+}
+
+void pack_tile(const PackSrc &p, int64_t tile, uint8_t *out)
+{
+    const int fmt = p.fmt, NB = blocks_per_unit(fmt);
+    const int64_t NU = num_units(p.K), NT = num_tiles(p.M);
+    uint8_t *codes = out;
+    uint8_t *scales = out + code_bytes(fmt, p.M, p.K);
+    for (int64_t u = 0; u < NU; ++u) {
+        for (int L = 0; L < 64; ++L) {
+            const int r16 = L & 15, q = L >> 4;
+            auto c = [&](int m, int ka, int e) -> uint32_t {
+                return code_at(p, tile * kTileRows + 16 * m + r16, u * kUnitK + 32 * ka + 8 * q + e);
+            };
+            uint32_t W[32];
+            memset(W, 0, sizeof(W));
+            for (int ka = 0; ka < 4; ++ka) {
+                if (fmt == 4) {
+                    for (int m = 0; m < 4; ++m) {
+                        uint32_t n = 0;
+                        for (int e = 0; e < 8; ++e) n |= c(m, ka, e) << (4 * e);
+                        W[4 * ka + m] = n;
+                    }
+                } else if (fmt == 5) {
+                    // output dword o: row o/2, e = 4*(o%2) + i in byte i, stored as code << 3
+                    auto oc = [&](int o, int i) { return c(o >> 1, ka, 4 * (o & 1) + i); };
+                    uint32_t E = 0;
+                    for (int d = 0; d < 4; ++d) {
+                        uint32_t X = 0;
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t main = oc(d, i), extra = oc(4 + d, i);
+                            X |= ((main << 3) | (extra >> 2)) << (8 * i);
+                            E |= (extra & 3u) << (8 * i + 2 * d);
+                        }
+                        W[5 * ka + d] = X;
+                    }
+                    W[5 * ka + 4] = E;
+                } else if (fmt == 6) {
+                    for (int pp = 0; pp < 2; ++pp) {
+                        const int m0 = 2 * pp, m1 = m0 + 1;
+                        uint32_t A = 0, B = 0, C = 0;
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t x3 = c(m1, ka, 4 + i);
+                            A |= ((c(m0, ka, i) << 2) | ((x3 >> 4) & 3u)) << (8 * i);
+                            B |= ((c(m0, ka, 4 + i) << 2) | ((x3 >> 2) & 3u)) << (8 * i);
+                            C |= ((c(m1, ka, i) << 2) | (x3 & 3u)) << (8 * i);
+                        }
+                        W[6 * ka + 3 * pp + 0] = A;
+                        W[6 * ka + 3 * pp + 1] = B;
+                        W[6 * ka + 3 * pp + 2] = C;
+                    }
+                } else {  // FP8
+                    for (int m = 0; m < 4; ++m)
+                        for (int h = 0; h < 2; ++h) {
+                            uint32_t w = 0;
+                            for (int i = 0; i < 4; ++i) w |= c(m, ka, 4 * h + i) << (8 * i);
+                            W[8 * ka + 2 * m + h] = w;
+                        }
+                }
+            }
+            for (int j = 0; j < NB; ++j)
+                memcpy(codes + ((tile * NU + u) * NB + j) * kBlockBytes + 16 * L, &W[4 * j], 16);
+        }
+        if (fmt != 8) {
+            const int64_t G = p.K / kGroup;
+            uint16_t *sb = reinterpret_cast<uint16_t *>(scales + (tile * NU + u) * kScaleBlockBytes);
+            for (int r16 = 0; r16 < 16; ++r16)
+                for (int g = 0; g < 2; ++g)
+                    for (int m = 0; m < 4; ++m) {
+                        const int64_t row = tile * kTileRows + 16 * m + r16, grp = 2 * u + g;
+                        sb[r16 * 8 + 4 * g + m] = (row < p.M && grp < G) ? p.hs[row * G + grp] : 0;
+                    }
+        }
+    }
+    if (fmt == 8) {
+        float *sb = reinterpret_cast<float *>(scales + tile * kScaleBlockBytes);
+        for (int r16 = 0; r16 < 16; ++r16)
+            for (int m = 0; m < 4; ++m) {
+                const int64_t row = tile * kTileRows + 16 * m + r16;
+                sb[r16 * 4 + m] = row < p.M ? p.rs[row] : 0.0f;
+            }
+    }
+    (void)NT;
+}
+
+// ------------------------------------------------------------------ planning
+
+struct Plan {
+    int route, waves, splits;
+};
+
+// Each wave keeps at least this many 128-wide k units so its loads pipeline.
+constexpr int64_t kMinUnitsPerWave = 3;
+
+// Launch shape for one (route, tokens-per-launch): the grid should fit the GPU in a single
+// round of resident workgroups (no tail of late workgroups), with as many resident waves as
+// possible (bytes in flight), and as few k splits as possible among equally good shapes.
+Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
+{
+    Plan best{route, 1, 1};
+    int64_t best_rounds = -1, best_waves = -1;
+    for (int waves = 1; waves <= 8; waves *= 2) {
+        if (NU < waves) break;
+        const int bpc = run_blocks_per_cu(fmt, route, Tl, waves);
+        if (bpc <= 0) continue;
+        const int64_t slots = (int64_t)cus * bpc;
+        int64_t splits = slots / NT;
+        const int64_t cap = NU / (waves * kMinUnitsPerWave);
+        if (splits > cap) splits = cap;
+        if (splits < 1) splits = 1;
+        const int64_t wgs = NT * splits;
+        const int64_t rounds = (wgs + slots - 1) / slots;
+        const int64_t resident = (wgs < slots ? wgs : slots) * waves;
+        const bool better = best_rounds < 0 || rounds < best_rounds ||
+                            (rounds == best_rounds && resident > best_waves) ||
+                            (rounds == best_rounds && resident == best_waves && splits < best.splits);
+        if (better) {
+            best = Plan{route, waves, (int)splits};
+            best_rounds = rounds;
+            best_waves = resident;
+        }
+    }
+    return best;
+}
+
+}  // namespace
+
+struct qmat {
+    int fmt;
+    int64_t M, K, NT, NU, Mpad;
+    const uint8_t *packed;
+    size_t bytes;
+    float *ws;
+    size_t ws_floats;
+    uint32_t *counters;
+    int device;
+    int cus;
+    Plan plan[2][kMaxT + 1];  // [route - 1][tokens per launch]
+};
+
+namespace {
+
+// tokens one launch of a route handles when the call has T tokens
+int launch_tokens(int route, int T) { return route == kRouteValu ? (T < kValuMaxT ? T : kValuMaxT) : T; }
+
+// The automatic route: the vector-ALU kernel for the smallest T, the MFMA kernel beyond.
+int auto_route(int fmt, int T)
+{
+    (void)fmt;
+    return T <= kValuMaxT ? kRouteValu : kRouteMfma;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qmat_packed_bytes(int fmt, int64_t M, int64_t K)
+{
+    if (!format_ok(fmt) || !shape_ok(M, K)) return 0;
+    return code_bytes(fmt, M, K) + scale_bytes(fmt, M, K);
+}
+
+int qmat_pack(int fmt, int64_t M, int64_t K, const void *codes, const void *scales, void *out, size_t out_bytes)
+{
+    if (!format_ok(fmt)) return fail(QMAT_EINVAL, "qmat_pack: unknown format %d", fmt);
+    if (!shape_ok(M, K)) return fail(QMAT_ESHAPE, "qmat_pack: bad shape M=%lld K=%lld (K must be a positive multiple of 64)", (long long)M, (long long)K);
+    if (!codes || !scales || !out) return fail(QMAT_EINVAL, "qmat_pack: null pointer");
+    const size_t need = qmat_packed_bytes(fmt, M, K);
+    if (out_bytes < need) return fail(QMAT_ESIZE, "qmat_pack: out_bytes %zu < %zu", out_bytes, need);
+    PackSrc p{fmt, M, K, nullptr, nullptr, nullptr, nullptr};
+    if (fmt == 8) {
+        p.bytes = static_cast<const uint8_t *>(codes);
+        p.rs = static_cast<const float *>(scales);
+        for (int64_t i = 0; i < M * K; ++i)
+            if ((p.bytes[i] & 0x7F) == 0x7F)
+                return fail(QMAT_ERANGE, "qmat_pack: NaN E4M3 byte 0x%02x at row %lld col %lld", p.bytes[i], (long long)(i / K), (long long)(i % K));
+        for (int64_t i = 0; i < M; ++i)
+            if (!std::isfinite(p.rs[i])) return fail(QMAT_ERANGE, "qmat_pack: non-finite row scale at row %lld", (long long)i);
+    } else {
+        p.codes = static_cast<const int8_t *>(codes);
+        p.hs = static_cast<const uint16_t *>(scales);
+        const int lo = -(1 << (fmt - 1)), hi = (1 << (fmt - 1)) - 1;
+        for (int64_t i = 0; i < M * K; ++i)
+            if (p.codes[i] < lo || p.codes[i] > hi)
+                return fail(QMAT_ERANGE, "qmat_pack: code %d outside [%d,%d] at row %lld col %lld", p.codes[i], lo, hi, (long long)(i / K), (long long)(i % K));
+        const int64_t G = K / kGroup;
+        for (int64_t i = 0; i < M * G; ++i)
+            if ((p.hs[i] & 0x7C00) == 0x7C00)
+                return fail(QMAT_ERANGE, "qmat_pack: non-finite FP16 scale 0x%04x at row %lld group %lld", p.hs[i], (long long)(i / G), (long long)(i % G));
+    }
+    uint8_t *o = static_cast<uint8_t *>(out);
+    const int64_t NT = num_tiles(M);
+    unsigned nth = std::thread::hardware_concurrency();
+    if (nth == 0) nth = 1;
+    if (nth > 16) nth = 16;
+    if ((int64_t)nth > NT) nth = (unsigned)NT;
+    auto work = [&](unsigned k) {
+        for (int64_t t = (int64_t)k; t < NT; t += nth) pack_tile(p, t, o);
+    };
+    if (nth == 1) {
+        work(0);
+    } else {
+        std::vector<std::thread> th;
+        try {
+            for (unsigned k = 1; k < nth; ++k) th.emplace_back(work, k);
+        } catch (...) {
+            for (auto &t : th) t.join();
+            return fail(QMAT_ENOMEM, "qmat_pack: could not start threads");
+        }
+        work(0);
+        for (auto &t : th) t.join();
+    }
+    return ok();
+}
+
+int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packed_dev, size_t bytes)
+{
+    if (!handle) return fail(QMAT_EINVAL, "qmat_create: null handle pointer");
+    *handle = nullptr;
+    if (!format_ok(fmt)) return fail(QMAT_EINVAL, "qmat_create: unknown format %d", fmt);
+    if (!shape_ok(M, K)) return fail(QMAT_ESHAPE, "qmat_create: bad shape M=%lld K=%lld", (long long)M, (long long)K);
+    if (!packed_dev) return fail(QMAT_EINVAL, "qmat_create: null packed pointer");
+    if (reinterpret_cast<uintptr_t>(packed_dev) % 16) return fail(QMAT_EINVAL, "qmat_create: packed pointer not 16-byte aligned");
+    const size_t need = qmat_packed_bytes(fmt, M, K);
+    if (bytes != need) return fail(QMAT_ESIZE, "qmat_create: bytes %zu != packed size %zu", bytes, need);
+    qmat *h = new (std::nothrow) qmat;
+    if (!h) return fail(QMAT_ENOMEM, "qmat_create: out of host memory");
+    h->fmt = fmt;
+    h->M = M;
+    h->K = K;
+    h->NT = num_tiles(M);
+    h->NU = num_units(K);
+    h->Mpad = h->NT * kTileRows;
+    h->packed = static_cast<const uint8_t *>(packed_dev);
+    h->bytes = bytes;
+    h->ws = nullptr;
+    h->counters = nullptr;
+    h->ws_floats = 0;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return fail(QMAT_EHIP, "qmat_create: hipGetDevice failed");
+    }
+    if (hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || h->cus < 1) {
+        delete h;
+        return fail(QMAT_EHIP, "qmat_create: cannot read the compute unit count");
+    }
+    // launch plans for both routes and every tokens-per-launch; the workspace covers the
+    // largest split-K partial set among them, and at least 8 splits at T = 16 for matrices of
+    // up to 65536 rows (explicit launch shapes in tests and tuning)
+    size_t need_ws = 0;
+    for (int r = kRouteValu; r <= kRouteMfma; ++r)
+        for (int T = 1; T <= kMaxT; ++T) {
+            const int Tl = launch_tokens(r, T);
+            const Plan p = make_plan(fmt, r, Tl, h->NT, h->NU, h->cus);
+            h->plan[r - 1][T] = p;
+            if (p.splits > 1) {
+                const size_t f = (size_t)p.splits * Tl * (size_t)h->Mpad;
+                if (f > need_ws) need_ws = f;
+            }
+        }
+    if (h->Mpad <= 65536 && need_ws < (size_t)8 * kMaxT * h->Mpad) need_ws = (size_t)8 * kMaxT * h->Mpad;
+    if (need_ws > 0) {
+        h->ws_floats = need_ws;
+        if (hipMalloc(&h->ws, h->ws_floats * sizeof(float)) != hipSuccess) {
+            (void)hipGetLastError();
+            delete h;
+            return fail(QMAT_ENOMEM, "qmat_create: workspace allocation failed");
+        }
+        if (hipMalloc(&h->counters, (size_t)h->NT * sizeof(uint32_t)) != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipFree(h->ws);
+            delete h;
+            return fail(QMAT_ENOMEM, "qmat_create: counter allocation failed");
+        }
+        if (hipMemset(h->counters, 0, (size_t)h->NT * sizeof(uint32_t)) != hipSuccess ||
+            hipDeviceSynchronize() != hipSuccess) {
+            (void)hipFree(h->ws);
+            (void)hipFree(h->counters);
+            delete h;
+            return fail(QMAT_EHIP, "qmat_create: counter initialisation failed");
+        }
+    }
+    *handle = h;
+    return ok();
+}
+
+int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int waves, int splits, void *stream)
+{
+    if (!h) return fail(QMAT_EINVAL, "qmat_run: null handle");
+    if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d]", T, kMaxT);
+    if (T == 0) return ok();
+    if (!x_dev || !y_dev) return fail(QMAT_EINVAL, "qmat_run: null x or y");
+    if (reinterpret_cast<uintptr_t>(x_dev) % 16) return fail(QMAT_EINVAL, "qmat_run: x not 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_run: y not 4-byte aligned");
+    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA) return fail(QMAT_EINVAL, "qmat_run: bad route %d", route);
+    if (!(waves == 0 || waves == 1 || waves == 2 || waves == 4 || waves == 8))
+        return fail(QMAT_EINVAL, "qmat_run: waves must be 0, 1, 2, 4 or 8");
+    if (splits < 0) return fail(QMAT_EINVAL, "qmat_run: splits must be >= 0");
+    const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
+    Plan p = h->plan[r - 1][T];
+    if (waves) p.waves = waves;
+    if (splits) p.splits = splits;
+    if ((int64_t)p.splits * p.waves > h->NU * 64) return fail(QMAT_ESIZE, "qmat_run: too many splits");
+    const int Tl = launch_tokens(p.route, T);
+    if (p.splits > 1 && (size_t)p.splits * Tl * (size_t)h->Mpad > h->ws_floats)
+        return fail(QMAT_ESIZE, "qmat_run: %d splits at %d tokens exceed the workspace", p.splits, Tl);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint16_t *x = static_cast<const uint16_t *>(x_dev);
+    const uint8_t *codes = h->packed;
+    const uint8_t *scales = h->packed + code_bytes(h->fmt, h->M, h->K);
+    for (int t0 = 0; t0 < T; t0 += Tl) {
+        RunArgs a;
+        a.codes = codes;
+        a.scales = scales;
+        a.x = x + (int64_t)t0 * h->K;
+        a.y = y_dev + (int64_t)t0 * h->M;
+        a.ws = h->ws;
+        a.counters = h->counters;
+        a.ldy = h->M;
+        a.M = (int)h->M;
+        a.K = (int)h->K;
+        a.T = (T - t0 < Tl) ? (T - t0) : Tl;
+        a.NT = (int)h->NT;
+        a.NU = (int)h->NU;
+        a.S = p.splits;
+        a.Mpad = (int)h->Mpad;
+        const hipError_t e = launch_run(h->fmt, p.route, a, p.waves, st);
+        if (e != hipSuccess) return fail(QMAT_EHIP, "qmat_run: launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+int qmat_get_plan(qmat_t h, int T, int route, int *route_out, int *waves, int *splits)
+{
+    if (!h || !route_out || !waves || !splits) return fail(QMAT_EINVAL, "qmat_get_plan: null argument");
+    if (T < 1 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kMaxT);
+    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA) return fail(QMAT_EINVAL, "qmat_get_plan: bad route %d", route);
+    const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
+    const Plan &p = h->plan[r - 1][T];
+    *route_out = r == kRouteValu ? QMAT_ROUTE_VALU : QMAT_ROUTE_MFMA;
+    *waves = p.waves;
+    *splits = p.splits;
+    return ok();
+}
+
+int qmat_run(qmat_t h, const void *x_dev, float *y_dev, int T, void *stream)
+{
+    return qmat_run_ex(h, x_dev, y_dev, T, QMAT_ROUTE_AUTO, 0, 0, stream);
+}
+
+int qmat_dequant(qmat_t h, float *w_dev, void *stream)
+{
+    if (!h) return fail(QMAT_EINVAL, "qmat_dequant: null handle");
+    if (!w_dev) return fail(QMAT_EINVAL, "qmat_dequant: null output");
+    if (reinterpret_cast<uintptr_t>(w_dev) % 16) return fail(QMAT_EINVAL, "qmat_dequant: output not 16-byte aligned");
+    DequantArgs a;
+    a.codes = h->packed;
+    a.scales = h->packed + code_bytes(h->fmt, h->M, h->K);
+    a.w = w_dev;
+    a.M = (int)h->M;
+    a.K = (int)h->K;
+    a.NT = (int)h->NT;
+    a.NU = (int)h->NU;
+    const hipError_t e = launch_dequant(h->fmt, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QMAT_EHIP, "qmat_dequant: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t qmat_workspace_bytes(qmat_t h)
+{
+    if (!h) return 0;
+    return h->ws_floats * sizeof(float) + (h->counters ? (size_t)h->NT * sizeof(uint32_t) : 0);
+}
+
+void qmat_destroy(qmat_t h)
+{
+    if (!h) return;
+    if (h->ws) (void)hipFree(h->ws);
+    if (h->counters) (void)hipFree(h->counters);
+    delete h;
+}
+
+const char *qmat_last_error(void) { return g_err; }
+
+}  // extern "C"

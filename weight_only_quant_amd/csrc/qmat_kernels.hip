@@ -1,0 +1,588 @@
+// gfx950 (CDNA4) kernels for the weight-only quantized small-T product y = x . W^T.
+//
+// Weight formats (NInfer model cards): groupwise Q4/Q5/Q6 — FP16 scale per 64 weights along K
+// times a two's-complement code ("Qwen3.8-27B for NInfer on the RTX 3090", "What is different
+// from the upstream artifact") — and row-scaled FP8 E4M3 ("Qwen3.8-27B NVFP4 for NInfer",
+// "Artifact").  The packed layout is described in qmat_layout.h.
+//
+// Every code is turned into an exact small float before any product is formed:
+//   Q4   v_cvt_off_f32_i4 reads a two's-complement nibble as code/16 (SDWA picks the byte);
+//   Q5/6 the code is assembled in the top bits of a byte and v_cvt_f32_i32 with SDWA sign
+//        extension reads it as 8*code or 4*code;
+//   FP8  v_cvt_scalef32_pk_bf16_fp8 widens two E4M3 bytes to bf16 exactly.
+// These values are exact in bf16, so bf16(code) * bf16(x) is an exact product; dot products
+// accumulate in fp32 (v_dot2c_f32_bf16 on the vector ALU, or the 16x16x32 bf16 MFMA), and the
+// per-group scale (times the power of two of the code encoding) is applied once per 64-group.
+// No offset-binary tricks: a row with sparse or zero codes has no cancellation error.
+//
+// Work split: a wave owns one 64-row tile and a contiguous range of 128-wide k units.  NW waves
+// of a workgroup split a tile's units and reduce through LDS; S workgroups split further and the
+// last-arriving one adds the S partials from the workspace in a fixed order (deterministic, no
+// atomics on data, no memset: the arrival counter is reset by the last block).
+#include <hip/hip_runtime.h>
+
+#include "qmat_kernels.h"
+#include "qmat_layout.h"
+
+namespace qmatk {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+template <int FMT> struct Fmt;
+// NB: 1 KB blocks per unit.  kToCode: the unpacked value times kToCode is the code (Q4 reads
+// code/16, Q5 8*code, Q6 4*code); the factor is folded into the group scale.
+template <> struct Fmt<4> { static constexpr int NB = 4; static constexpr float kToCode = 16.0f; };
+template <> struct Fmt<5> { static constexpr int NB = 5; static constexpr float kToCode = 0.125f; };
+template <> struct Fmt<6> { static constexpr int NB = 6; static constexpr float kToCode = 0.25f; };
+template <> struct Fmt<8> { static constexpr int NB = 8; static constexpr float kToCode = 1.0f; };
+
+// ------------------------------------------------------------------ exact code conversion
+
+// sign-extended nibble in bits [3:0] of byte B of v, as a float equal to nibble / 16
+template <int B> __device__ __forceinline__ float nib_lo(uint32_t v);
+template <> __device__ __forceinline__ float nib_lo<0>(uint32_t v)
+{
+    return __builtin_amdgcn_cvt_off_f32_i4(v);
+}
+template <> __device__ __forceinline__ float nib_lo<1>(uint32_t v)
+{
+    float r;
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
+        : "=v"(r) : "v"(v));
+    return r;
+}
+template <> __device__ __forceinline__ float nib_lo<2>(uint32_t v)
+{
+    float r;
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
+        : "=v"(r) : "v"(v));
+    return r;
+}
+template <> __device__ __forceinline__ float nib_lo<3>(uint32_t v)
+{
+    float r;
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
+        : "=v"(r) : "v"(v));
+    return r;
+}
+
+// byte B of v as a signed integer, converted to float (SDWA sign-extending convert)
+template <int B> __device__ __forceinline__ float sbyte(uint32_t v)
+{
+    return (float)(int8_t)(v >> (8 * B));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+__device__ __forceinline__ uint32_t shift_signed(uint32_t v, int s)
+{
+    return s >= 0 ? (v << s) : (v >> -s);
+}
+
+// The 8 codes of row m in k step KA of a unit, as exact floats equal to code / kToCode.
+// W: the lane's 4*NB dwords of the unit (layout in qmat_layout.h).
+template <int FMT, int KA, int MM>
+__device__ __forceinline__ void codes8(const uint32_t *W, float (&f)[8])
+{
+    if constexpr (FMT == 4) {
+        const uint32_t n = W[4 * KA + MM], h = n >> 4;
+        f[0] = nib_lo<0>(n); f[1] = nib_lo<0>(h);
+        f[2] = nib_lo<1>(n); f[3] = nib_lo<1>(h);
+        f[4] = nib_lo<2>(n); f[5] = nib_lo<2>(h);
+        f[6] = nib_lo<3>(n); f[7] = nib_lo<3>(h);
+    } else {
+        uint32_t o[2];
+        if constexpr (FMT == 5) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int oi = 2 * MM + hh;
+                if (oi < 4) {
+                    o[hh] = W[5 * KA + oi] & 0xF8F8F8F8u;
+                } else {
+                    const int d = oi - 4;
+                    o[hh] = ((W[5 * KA + d] << 5) & 0xE0E0E0E0u) |
+                            (shift_signed(W[5 * KA + 4], 3 - 2 * d) & 0x18181818u);
+                }
+            }
+        } else {  // FMT == 6
+            const uint32_t A = W[6 * KA + 3 * (MM >> 1)], B = W[6 * KA + 3 * (MM >> 1) + 1],
+                           C = W[6 * KA + 3 * (MM >> 1) + 2];
+            if ((MM & 1) == 0) {
+                o[0] = A & 0xFCFCFCFCu;
+                o[1] = B & 0xFCFCFCFCu;
+            } else {
+                o[0] = C & 0xFCFCFCFCu;
+                o[1] = ((A << 6) & 0xC0C0C0C0u) | ((B << 4) & 0x30303030u) | ((C << 2) & 0x0C0C0C0Cu);
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            f[4 * hh + 0] = sbyte<0>(o[hh]);
+            f[4 * hh + 1] = sbyte<1>(o[hh]);
+            f[4 * hh + 2] = sbyte<2>(o[hh]);
+            f[4 * hh + 3] = sbyte<3>(o[hh]);
+        }
+    }
+}
+
+// The 8 weights of row m in k step KA as 4 dwords of bf16 pairs (k, k+1), exact: groupwise
+// code / kToCode, FP8 the E4M3 value.
+template <int FMT, int KA, int MM>
+__device__ __forceinline__ void bf16x8_of(const uint32_t *W, uint32_t (&b)[4])
+{
+    if constexpr (FMT == 8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t w = W[8 * KA + 2 * MM + h];
+            b[2 * h + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+            b[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+        }
+    } else {
+        float f[8];
+        codes8<FMT, KA, MM>(W, f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = pack_bf16(f[2 * i], f[2 * i + 1]);
+    }
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// binary16 scale of group g (0/1 in the unit) for the lane's row m, from the lane's 16-byte
+// scale slot (index 4*g + m)
+__device__ __forceinline__ float group_scale(const u32x4_t &sc, int g, int m)
+{
+    const int idx = 4 * g + m;
+    const uint32_t w = sc[idx >> 1];
+    return half_bits_to_float((idx & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+// ------------------------------------------------------------------ split bookkeeping
+
+struct Slice {
+    int tile, sp, w, nw, u0, u1;
+};
+
+__device__ __forceinline__ Slice make_slice(const RunArgs &a)
+{
+    Slice s;
+    s.nw = blockDim.x >> 6;
+    s.w = threadIdx.x >> 6;
+    s.tile = blockIdx.x / a.S;
+    s.sp = blockIdx.x - s.tile * a.S;
+    const int nsl = a.S * s.nw, sl = s.sp * s.nw + s.w;
+    s.u0 = (int)(((int64_t)a.NU * sl) / nsl);
+    s.u1 = (int)(((int64_t)a.NU * (sl + 1)) / nsl);
+    return s;
+}
+
+// Combine the waves' and workgroups' partial tiles and write y.  Every wave passes its values
+// through put(t, row_in_tile, v) calls made identically by all waves (same (t, row) sets).
+// red: dynamic LDS of nw * T * 64 floats (unused when nw == 1 and S == 1).
+template <typename ForEach>
+__device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *red, ForEach for_each)
+{
+    const int row0 = s.tile * kTileRows;
+    if (s.nw == 1 && a.S == 1) {
+        for_each([&](int t, int r, float v) {
+            if (row0 + r < a.M) a.y[(int64_t)t * a.ldy + row0 + r] = v;
+        });
+        return;
+    }
+    const int n = a.T * kTileRows;
+    if (s.nw > 1) {
+        for_each([&](int t, int r, float v) { red[s.w * n + t * kTileRows + r] = v; });
+        __syncthreads();
+    }
+    const int nthr = blockDim.x;
+    if (a.S == 1) {
+        for (int e = threadIdx.x; e < n; e += nthr) {
+            float v = red[e];
+            for (int w = 1; w < s.nw; ++w) v += red[w * n + e];
+            const int t = e / kTileRows, r = e - t * kTileRows;
+            if (row0 + r < a.M) a.y[(int64_t)t * a.ldy + row0 + r] = v;
+        }
+        return;
+    }
+    // S > 1.  The workgroup's partial tile goes to the workspace through returning agent-scope
+    // atomic exchanges: each is performed at the device coherence point before its old value
+    // comes back, and every thread consumes its old values before the barrier, so all of the
+    // tile's partials are in place before thread 0 bumps the arrival counter.  The last of the
+    // S workgroups to arrive reads the S partials with agent-scope atomic loads and adds them
+    // in split order (deterministic).  No cache-wide fences, no memset: the last block resets
+    // the counter for the next call.
+    float *wsp = a.ws + (int64_t)s.sp * a.T * a.Mpad;
+    uint32_t sink = 0;
+    auto publish = [&](int t, int r, float v) {
+        uint32_t *p = reinterpret_cast<uint32_t *>(wsp + (int64_t)t * a.Mpad + row0 + r);
+        sink |= __hip_atomic_exchange(p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (s.nw > 1) {
+        for (int e = threadIdx.x; e < n; e += nthr) {
+            float v = red[e];
+            for (int w = 1; w < s.nw; ++w) v += red[w * n + e];
+            const int t = e / kTileRows, r = e - t * kTileRows;
+            publish(t, r, v);
+        }
+    } else {
+        for_each(publish);
+    }
+    asm volatile("" ::"v"(sink));
+    __syncthreads();
+    __shared__ int last;
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s.tile], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        last = (prev == (uint32_t)(a.S - 1));
+    }
+    __syncthreads();
+    if (!last) return;
+    for (int e = threadIdx.x; e < n; e += nthr) {
+        const int t = e / kTileRows, r = e - t * kTileRows;
+        if (row0 + r >= a.M) continue;
+        uint32_t *p = reinterpret_cast<uint32_t *>(a.ws + (int64_t)t * a.Mpad + row0 + r);
+        float v = __builtin_bit_cast(float, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        for (int sp = 1; sp < a.S; ++sp)
+            v += __builtin_bit_cast(float, __hip_atomic_load(p + (int64_t)sp * a.T * a.Mpad, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT));
+        a.y[(int64_t)t * a.ldy + row0 + r] = v;
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&a.counters[s.tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ unit loads
+
+template <int NB> struct UnitRaw {
+    u32x4_t c[NB];
+    u32x4_t sc;
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_unit(const RunArgs &a, int tile, int u, int lane, UnitRaw<Fmt<FMT>::NB> &r)
+{
+    constexpr int NB = Fmt<FMT>::NB;
+    const u32x4_t *cp = reinterpret_cast<const u32x4_t *>(a.codes) + (((int64_t)tile * a.NU + u) * NB) * 64 + lane;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) r.c[j] = cp[j * 64];
+    if constexpr (FMT != 8)
+        r.sc = reinterpret_cast<const u32x4_t *>(a.scales)[((int64_t)tile * a.NU + u) * 16 + (lane & 15)];
+}
+
+// 8 bf16 activations (one k octet) of token t at column k, clamped inside the row: the
+// clamped columns only meet zero codes of padding groups.
+__device__ __forceinline__ u32x4_t load_x8(const RunArgs &a, int t, int k)
+{
+    const int kk = k < a.K - 8 ? k : a.K - 8;
+    return *reinterpret_cast<const u32x4_t *>(a.x + (int64_t)t * a.K + kk);
+}
+
+// ------------------------------------------------------------------ vector-ALU route
+
+template <int FMT, int TT, int KA, int MM>
+__device__ __forceinline__ void valu_step(const uint32_t *W, const u32x4_t (&xv)[4][TT], float (&p)[4][TT])
+{
+    uint32_t b[4];
+    bf16x8_of<FMT, KA, MM>(W, b);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) p[MM][t] = dot2(b[d], xv[KA][t][d], p[MM][t]);
+}
+
+template <int FMT, int TT>
+__global__ __launch_bounds__(512) void valu_kernel(RunArgs a)
+{
+    constexpr int NB = Fmt<FMT>::NB;
+    extern __shared__ float red[];
+    const Slice s = make_slice(a);
+    const int lane = threadIdx.x & 63, q = lane >> 4;
+    float acc[4][TT];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[m][t] = 0.f;
+
+    UnitRaw<NB> cur, nxt;
+    if (s.u0 < s.u1) load_unit<FMT>(a, s.tile, s.u0, lane, cur);
+    for (int u = s.u0; u < s.u1; ++u) {
+        u32x4_t xv[4][TT];
+#pragma unroll
+        for (int ka = 0; ka < 4; ++ka)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) xv[ka][t] = load_x8(a, t, u * kUnitK + 32 * ka + 8 * q);
+        if (u + 1 < s.u1) load_unit<FMT>(a, s.tile, u + 1, lane, nxt);
+        const uint32_t *W = reinterpret_cast<const uint32_t *>(cur.c);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            float p[4][TT];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int t = 0; t < TT; ++t) p[m][t] = 0.f;
+            if (g == 0) {
+                valu_step<FMT, TT, 0, 0>(W, xv, p); valu_step<FMT, TT, 0, 1>(W, xv, p);
+                valu_step<FMT, TT, 0, 2>(W, xv, p); valu_step<FMT, TT, 0, 3>(W, xv, p);
+                valu_step<FMT, TT, 1, 0>(W, xv, p); valu_step<FMT, TT, 1, 1>(W, xv, p);
+                valu_step<FMT, TT, 1, 2>(W, xv, p); valu_step<FMT, TT, 1, 3>(W, xv, p);
+            } else {
+                valu_step<FMT, TT, 2, 0>(W, xv, p); valu_step<FMT, TT, 2, 1>(W, xv, p);
+                valu_step<FMT, TT, 2, 2>(W, xv, p); valu_step<FMT, TT, 2, 3>(W, xv, p);
+                valu_step<FMT, TT, 3, 0>(W, xv, p); valu_step<FMT, TT, 3, 1>(W, xv, p);
+                valu_step<FMT, TT, 3, 2>(W, xv, p); valu_step<FMT, TT, 3, 3>(W, xv, p);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if constexpr (FMT == 8) {
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) acc[m][t] += p[m][t];
+                } else {
+                    const float sf = group_scale(cur.sc, g, m) * Fmt<FMT>::kToCode;
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) acc[m][t] = fmaf(sf, p[m][t], acc[m][t]);
+                }
+            }
+        }
+        if (u + 1 < s.u1) cur = nxt;
+    }
+    if constexpr (FMT == 8) {
+        const f32x4_t rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)s.tile * 16 + (lane & 15)];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) acc[m][t] *= rs[m];
+    }
+    // the four lanes L, L^16, L^32, L^48 hold the same rows for different k octets
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            acc[m][t] += __shfl_xor(acc[m][t], 16);
+            acc[m][t] += __shfl_xor(acc[m][t], 32);
+        }
+    // lane block q keeps row 16*q + L%16
+    float v[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+        v[t] = q == 0 ? acc[0][t] : q == 1 ? acc[1][t] : q == 2 ? acc[2][t] : acc[3][t];
+    const int r = 16 * q + (lane & 15);
+    finish(a, s, red, [&](auto put) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) put(t, r, v[t]);
+    });
+}
+
+// ------------------------------------------------------------------ MFMA route
+
+template <int FMT, int KA>
+__device__ __forceinline__ void mfma_step(const uint32_t *W, const u32x4_t &xa, f32x4_t (&D)[4])
+{
+    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, xa);
+#define QMAT_MFMA_ROW(MM)                                                              \
+    {                                                                                  \
+        uint32_t b[4];                                                                 \
+        bf16x8_of<FMT, KA, MM>(W, b);                                                  \
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, (u32x4_t){b[0], b[1], b[2], b[3]}); \
+        D[MM] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, D[MM], 0, 0, 0);        \
+    }
+    QMAT_MFMA_ROW(0) QMAT_MFMA_ROW(1) QMAT_MFMA_ROW(2) QMAT_MFMA_ROW(3)
+#undef QMAT_MFMA_ROW
+}
+
+// A operand: 16 tokens x 32 k (lane l: token l % 16, k octet l / 16); B operand: 32 k x 16 rows
+// of the tile (lane l: row 16*m + l % 16, the same k octet) — exactly the packed layout.
+// D[m]: lane l holds tokens 4*(l/16) + r (r = 0..3) of row 16*m + l % 16.
+template <int FMT>
+__global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
+{
+    constexpr int NB = Fmt<FMT>::NB;
+    extern __shared__ float red[];
+    const Slice s = make_slice(a);
+    const int lane = threadIdx.x & 63, tok = lane & 15, oct = lane >> 4;
+    const bool tok_ok = tok < a.T;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    UnitRaw<NB> cur, nxt;
+    if (s.u0 < s.u1) load_unit<FMT>(a, s.tile, s.u0, lane, cur);
+    for (int u = s.u0; u < s.u1; ++u) {
+        u32x4_t xa[4];
+#pragma unroll
+        for (int ka = 0; ka < 4; ++ka)
+            xa[ka] = tok_ok ? load_x8(a, tok, u * kUnitK + 32 * ka + 8 * oct) : (u32x4_t){0u, 0u, 0u, 0u};
+        if (u + 1 < s.u1) load_unit<FMT>(a, s.tile, u + 1, lane, nxt);
+        const uint32_t *W = reinterpret_cast<const uint32_t *>(cur.c);
+        if constexpr (FMT == 8) {
+            mfma_step<FMT, 0>(W, xa[0], acc);
+            mfma_step<FMT, 1>(W, xa[1], acc);
+            mfma_step<FMT, 2>(W, xa[2], acc);
+            mfma_step<FMT, 3>(W, xa[3], acc);
+        } else {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                f32x4_t D[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) D[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                if (g == 0) {
+                    mfma_step<FMT, 0>(W, xa[0], D);
+                    mfma_step<FMT, 1>(W, xa[1], D);
+                } else {
+                    mfma_step<FMT, 2>(W, xa[2], D);
+                    mfma_step<FMT, 3>(W, xa[3], D);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float sf = group_scale(cur.sc, g, m) * Fmt<FMT>::kToCode;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[m][r] = fmaf(sf, D[m][r], acc[m][r]);
+                }
+            }
+        }
+        if (u + 1 < s.u1) cur = nxt;
+    }
+    if constexpr (FMT == 8) {
+        const f32x4_t rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)s.tile * 16 + (lane & 15)];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] *= rs[m];
+    }
+    const int t0 = 4 * oct, rr = lane & 15;
+    finish(a, s, red, [&](auto put) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (t0 + r < a.T) put(t0 + r, 16 * m + rr, acc[m][r]);
+    });
+}
+
+// ------------------------------------------------------------------ dequant (checking path)
+
+template <int FMT, int KA, int MM>
+__device__ __forceinline__ void dequant_step(const DequantArgs &a, const uint32_t *W, const u32x4_t &sc,
+                                             const f32x4_t &rs, int tile, int u, int lane)
+{
+    const int row = tile * kTileRows + 16 * MM + (lane & 15);
+    const int k = u * kUnitK + 32 * KA + 8 * (lane >> 4);
+    if (row >= a.M || k >= a.K) return;
+    float out[8];
+    if constexpr (FMT == 8) {
+        uint32_t b[4];
+        bf16x8_of<FMT, KA, MM>(W, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = rs[MM] * __builtin_bit_cast(float, b[i] << 16);
+            out[2 * i + 1] = rs[MM] * __builtin_bit_cast(float, b[i] & 0xFFFF0000u);
+        }
+    } else {
+        float f[8];
+        codes8<FMT, KA, MM>(W, f);
+        const float sc_f = group_scale(sc, KA >> 1, MM);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = sc_f * (f[i] * Fmt<FMT>::kToCode);
+    }
+    float *dst = a.w + (int64_t)row * a.K + k;
+    reinterpret_cast<f32x4_t *>(dst)[0] = (f32x4_t){out[0], out[1], out[2], out[3]};
+    reinterpret_cast<f32x4_t *>(dst)[1] = (f32x4_t){out[4], out[5], out[6], out[7]};
+}
+
+template <int FMT>
+__global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a)
+{
+    constexpr int NB = Fmt<FMT>::NB;
+    const int lane = threadIdx.x;
+    const int tile = blockIdx.x / a.NU, u = blockIdx.x - tile * a.NU;
+    u32x4_t c[NB];
+    const u32x4_t *cp = reinterpret_cast<const u32x4_t *>(a.codes) + (((int64_t)tile * a.NU + u) * NB) * 64 + lane;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) c[j] = cp[j * 64];
+    u32x4_t sc = (u32x4_t){0u, 0u, 0u, 0u};
+    f32x4_t rs = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    if constexpr (FMT == 8)
+        rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)tile * 16 + (lane & 15)];
+    else
+        sc = reinterpret_cast<const u32x4_t *>(a.scales)[((int64_t)tile * a.NU + u) * 16 + (lane & 15)];
+    const uint32_t *W = reinterpret_cast<const uint32_t *>(c);
+#define QMAT_DQ(KA)                                          \
+    dequant_step<FMT, KA, 0>(a, W, sc, rs, tile, u, lane);   \
+    dequant_step<FMT, KA, 1>(a, W, sc, rs, tile, u, lane);   \
+    dequant_step<FMT, KA, 2>(a, W, sc, rs, tile, u, lane);   \
+    dequant_step<FMT, KA, 3>(a, W, sc, rs, tile, u, lane);
+    QMAT_DQ(0) QMAT_DQ(1) QMAT_DQ(2) QMAT_DQ(3)
+#undef QMAT_DQ
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <int FMT> static const void *run_kernel(int route, int T)
+{
+    if (route == kRouteMfma) return reinterpret_cast<const void *>(&mfma_kernel<FMT>);
+    switch (T) {
+    case 1: return reinterpret_cast<const void *>(&valu_kernel<FMT, 1>);
+    case 2: return reinterpret_cast<const void *>(&valu_kernel<FMT, 2>);
+    case 3: return reinterpret_cast<const void *>(&valu_kernel<FMT, 3>);
+    case 4: return reinterpret_cast<const void *>(&valu_kernel<FMT, 4>);
+    default: return nullptr;
+    }
+}
+
+static const void *run_kernel_for(int fmt, int route, int T)
+{
+    switch (fmt) {
+    case 4: return run_kernel<4>(route, T);
+    case 5: return run_kernel<5>(route, T);
+    case 6: return run_kernel<6>(route, T);
+    case 8: return run_kernel<8>(route, T);
+    default: return nullptr;
+    }
+}
+
+static size_t run_lds_bytes(int waves, int T) { return waves > 1 ? (size_t)waves * T * kTileRows * sizeof(float) : 0; }
+
+hipError_t launch_run(int fmt, int route, const RunArgs &a, int waves, hipStream_t st)
+{
+    const void *k = run_kernel_for(fmt, route, a.T);
+    if (!k) return hipErrorInvalidValue;
+    RunArgs arg = a;
+    void *args[] = {&arg};
+    return hipLaunchKernel(k, dim3((unsigned)(a.NT * a.S)), dim3((unsigned)(64 * waves)), args,
+                           run_lds_bytes(waves, a.T), st);
+}
+
+int run_blocks_per_cu(int fmt, int route, int T, int waves)
+{
+    const void *k = run_kernel_for(fmt, route, T);
+    int n = 0;
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * waves, run_lds_bytes(waves, T)) != hipSuccess)
+        return 0;
+    return n;
+}
+
+template <int FMT> static const void *dequant_kernel_ptr() { return reinterpret_cast<const void *>(&dequant_kernel<FMT>); }
+
+hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t st)
+{
+    const void *k = fmt == 4 ? dequant_kernel_ptr<4>() : fmt == 5 ? dequant_kernel_ptr<5>()
+                  : fmt == 6 ? dequant_kernel_ptr<6>() : fmt == 8 ? dequant_kernel_ptr<8>() : nullptr;
+    if (!k) return hipErrorInvalidValue;
+    DequantArgs arg = a;
+    void *args[] = {&arg};
+    return hipLaunchKernel(k, dim3((unsigned)(a.NT * a.NU)), dim3(64), args, 0, st);
+}
+
+}  // namespace qmatk
