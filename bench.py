@@ -76,8 +76,8 @@ class Resident:
 
 
 def time_run(res, T, steps, warmup):
-    """Returns (ms_per_step over the timed region, mean per-launch kernel ms from events
-    bracketing each launch on the launch stream)."""
+    """Eager stream launches.  Returns (ms_per_step over the timed region, mean and median
+    per-launch kernel ms from HIP events bracketing each launch on the launch stream)."""
     import torch
     import weight_only_quant_amd as wq
     stream = torch.cuda.current_stream()
@@ -100,25 +100,96 @@ def time_run(res, T, steps, warmup):
     return total / steps, float(np.mean(per)), float(np.median(per))
 
 
+def time_graph(res, T, steps, warmup):
+    """The same K steps captured once into a HIP graph and replayed: the way a decode step
+    is launched in an engine.  Returns ms per step over the timed replay."""
+    import gc
+    import torch
+    import weight_only_quant_amd as wq
+    x, y = res.x[:T], res.y[:T]
+    hs = res.handles
+    gc.collect()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            wq.qmat_run(hs[i % len(hs)], x, y, T=T)
+    for _ in range(max(1, warmup // steps)):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del g
+    return ms
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch for a workload from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        from weight_only_quant_amd.rocprof_summary import kernel_source_sha256
+        rec = json.load(open(path))
+        if rec.get("kernel_source_sha256") != kernel_source_sha256():
+            return None
+        return int(round(rec["traffic_bytes"]))
+    except Exception:
+        return None
+
+
+def plan_str(res, T):
+    import weight_only_quant_amd as wq
+    r, d, w, sp = wq.qmat_get_plan(res.handles[0], T)
+    return f"{'valu' if r == wq.QMAT_ROUTE_VALU else 'mfma'} depth={d} waves={w} splits={sp}"
+
+
+EAGER_ONLY = False
+
+
+def measure(res, T, steps, warmup):
+    ms_e, k_mean, k_med = time_run(res, T, steps, warmup)
+    ms_g = ms_e if EAGER_ONLY else time_graph(res, T, steps, warmup)
+    wl = res.wl
+    ab = alg_bytes(wl.fmt, wl.M, wl.K, T)
+    return {"us_per_call": round(ms_g * 1e3, 3), "eager_us_per_call": round(ms_e * 1e3, 3),
+            "kernel_us": round(k_mean * 1e3, 3), "kernel_us_median": round(k_med * 1e3, 3),
+            "GBps": round(ab / (ms_g * 1e-3) / 1e9, 1), "kernel_GBps": round(ab / (k_mean * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * ab / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "bytes": ab, "plan": plan_str(res, T)}
+
+
 def cpu_baseline(res, T, target_s=12.0):
-    """The CPU oracle (as it stands) on a bounded sample of rows of the same workload."""
+    """The CPU oracle (as it stands) on a bounded sample of the same workload: whole passes
+    over all rows (or a row subset when one pass would exceed the budget), repeated until
+    about target_s seconds of CPU work have run."""
     import oracle
     wl = res.wl
     threads = min(os.cpu_count() or 1, 16)
     x = wl.x[:T]
-    rows = np.arange(min(wl.M, 512))
+    probe = np.arange(min(wl.M, 512))
     t0 = time.time()
-    oracle.gemv(wl.fmt, wl.codes, wl.scales, x, rows=rows, nthreads=threads)
-    dt = max(time.time() - t0, 1e-3)
-    n = int(min(wl.M, max(512, len(rows) * target_s / dt)))
-    rows = np.linspace(0, wl.M - 1, n).astype(np.int64)
-    t0 = time.time()
-    oracle.gemv(wl.fmt, wl.codes, wl.scales, x, rows=rows, nthreads=threads)
+    oracle.gemv(wl.fmt, wl.codes, wl.scales, x, rows=probe, nthreads=threads)
+    per_row_s = max(time.time() - t0, 1e-6) / len(probe)
+    n = int(min(wl.M, max(512, target_s / per_row_s)))
+    rows = None if n == wl.M else np.linspace(0, wl.M - 1, n).astype(np.int64)
+    passes, t0 = 0, time.time()
+    while True:
+        oracle.gemv(wl.fmt, wl.codes, wl.scales, x, rows=rows, nthreads=threads)
+        passes += 1
+        if time.time() - t0 >= target_s:
+            break
     dt = time.time() - t0
     per_row = alg_bytes(wl.fmt, 1, wl.K, 0)
-    gbs = (n * per_row + 2 * T * wl.K + 4 * T * n) / dt / 1e9
+    gbs = passes * (n * per_row + 2 * T * wl.K + 4 * T * n) / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {wl.M} rows of {wl.name} at T={T} ({dt:.1f} s, fp64 scalar C, {threads} threads)"}
+            "sample": f"{passes} pass(es) over {n} of {wl.M} rows of {wl.name} at T={T} in {dt:.1f} s "
+                      f"(fp64 scalar C, {threads} threads)"}
 
 
 def read_ceiling_gbs():
@@ -149,7 +220,13 @@ def main():
     ap.add_argument("--only", default=None, help="comma-separated config names for the extra shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 256 MiB device copy (known bytes) for scaling PMC byte counters")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="time eager stream launches only (no graph replay), e.g. under a counter profiler")
     args = ap.parse_args()
+    global EAGER_ONLY
+    EAGER_ONLY = args.eager_only
     if args.gpus != 1:
         log("bench.py: this build runs on one GPU only (the product shards by rows with no "
             "collective; see the design notes); --gpus must be 1")
@@ -158,6 +235,14 @@ def main():
     import torch
     import qmat_inputs as qi
     import weight_only_quant_amd as wq
+    if args.copy_calibration:
+        src = torch.ones((64 << 20,), dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {src.numel() * 4} bytes x5")
+        return
     if not os.path.exists(wq.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
@@ -167,12 +252,14 @@ def main():
     name, T = PRIMARY
     res = Resident(name)
     wl = res.wl
-    ms, k_mean, k_med = time_run(res, T, args.steps, args.warmup)
-    ab = alg_bytes(wl.fmt, wl.M, wl.K, T)
+    m = measure(res, T, args.steps, args.warmup)
+    ab = m["bytes"]
+    ms = m["us_per_call"] * 1e-3
     value = ab / (ms * 1e-3) / 1e9
-    achieved = ab / (k_mean * 1e-3) / 1e9
-    log(f"[bench] {name} T={T}: {ms * 1e3:.2f} us/step, kernel {k_mean * 1e3:.2f} us (median {k_med * 1e3:.2f}), "
-        f"{value:.0f} GB/s step, {achieved:.0f} GB/s kernel")
+    # one launch per step: the average launch duration is the graph-replay time per step
+    # (kernel plus the inter-kernel gap); per-launch event brackets add their own flushes
+    achieved = value
+    log(f"[bench] {name} T={T}: {m}")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -188,12 +275,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{name}_T{T}", "format": "Q4 groupwise (64-weight groups, FP16 scales)",
                    "M": wl.M, "K": wl.K, "T": T, "x": "bf16", "y": "fp32", "global_batch": T,
-                   "parallelism": "single-gpu", "rotation_copies": len(res.copies)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel_us_mean": round(k_mean * 1e3, 3), "kernel_us_median": round(k_med * 1e3, 3),
-                     "bytes_per_launch": ab},
-        "us_per_call": round(ms * 1e3, 3),
+                   "parallelism": "single-gpu", "rotation_copies": len(res.copies),
+                   "launch": "eager stream launches" if EAGER_ONLY else "K steps captured in one HIP graph and replayed",
+                   "plan": m["plan"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"{name}_T{T}"),
+                     "launch_us_mean": m["us_per_call"], "event_bracketed_launch_us_mean": m["kernel_us"],
+                     "event_bracketed_launch_us_median": m["kernel_us_median"], "bytes_per_launch": ab},
+        "us_per_call": m["us_per_call"],
+        "eager_us_per_call": m["eager_us_per_call"],
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
     }
     extra = {}
@@ -205,11 +295,7 @@ def main():
     for T2 in qi.CONFIGS[name][3]:
         if T2 == T:
             continue
-        ms2, km2, _ = time_run(res, T2, args.steps, args.warmup)
-        ab2 = alg_bytes(wl.fmt, wl.M, wl.K, T2)
-        extra[f"{name}_T{T2}"] = {"us_per_call": round(ms2 * 1e3, 3), "kernel_us": round(km2 * 1e3, 3),
-                                  "GBps": round(ab2 / (ms2 * 1e-3) / 1e9, 1),
-                                  "pct_hbm_peak": round(100 * ab2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        extra[f"{name}_T{T2}"] = measure(res, T2, args.steps, args.warmup)
         log(f"[bench] {name} T={T2}: {extra[f'{name}_T{T2}']}")
     res.close()
     del res
@@ -222,11 +308,7 @@ def main():
             r = Resident(n)
             for T2 in qi.CONFIGS[n][3]:
                 steps = args.steps if r.wl.M * r.wl.K < 1e9 else max(50, args.steps // 4)
-                ms2, km2, _ = time_run(r, T2, steps, args.warmup)
-                ab2 = alg_bytes(r.wl.fmt, r.wl.M, r.wl.K, T2)
-                extra[f"{n}_T{T2}"] = {"us_per_call": round(ms2 * 1e3, 3), "kernel_us": round(km2 * 1e3, 3),
-                                       "GBps": round(ab2 / (ms2 * 1e-3) / 1e9, 1),
-                                       "pct_hbm_peak": round(100 * ab2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+                extra[f"{n}_T{T2}"] = measure(r, T2, steps, args.warmup)
                 log(f"[bench] {n} T={T2}: {extra[f'{n}_T{T2}']}")
             r.close()
             del r

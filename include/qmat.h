@@ -102,18 +102,20 @@ int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream
 
 /* qmat_run with an explicit kernel route and launch shape, for tests and tuning.
  *   route:  qmat_route.
+ *   depth:  128-wide k units each wave keeps in flight (1..3; 0 = auto).
  *   waves:  waves per workgroup splitting K inside one workgroup (1, 2, 4 or 8; 0 = auto).
  *   splits: workgroups splitting K across the grid (>= 1; 0 = auto); the partial sums go
  *           through the handle's workspace and are added in a fixed order.
- * Errors: as qmat_run, plus QMAT_EINVAL (route, waves) and QMAT_ESIZE (splits * T * rows
+ * Errors: as qmat_run, plus QMAT_EINVAL (route, depth, waves) and QMAT_ESIZE (splits * T * rows
  * exceeds the workspace reserved at create time, or more splits than k units). */
-int qmat_run_ex(qmat_t handle, const void *x_dev, float *y_dev, int T, int route, int waves,
-                int splits, void *stream);
+int qmat_run_ex(qmat_t handle, const void *x_dev, float *y_dev, int T, int route, int depth,
+                int waves, int splits, void *stream);
 
 /* The launch qmat_run would make for T tokens on a route (QMAT_ROUTE_AUTO: the library's
- * choice): the route taken, waves per workgroup and k splits across workgroups.  Host only.
+ * choice): the route taken, units in flight per wave, waves per workgroup and k splits across
+ * workgroups.  Host only.
  * Errors: QMAT_EINVAL (null argument, bad route), QMAT_ESHAPE (T outside [1, 16]). */
-int qmat_get_plan(qmat_t handle, int T, int route, int *route_out, int *waves, int *splits);
+int qmat_get_plan(qmat_t handle, int T, int route, int *route_out, int *depth, int *waves, int *splits);
 
 /* Expand the packed matrix to fp32 w [M][K] (device), bit-exact: groupwise
  * fp32(scale) * code, FP8 fl32(r * e4m3).  For checking; not a fast path. */

@@ -126,7 +126,7 @@ def test_create_validation_without_gpu():
 def test_run_and_dequant_reject_null_handle():
     L = wq.lib()
     assert L.qmat_run(None, 16, 16, 1, None) == wq.QMAT_EINVAL
-    assert L.qmat_run_ex(None, 16, 16, 1, 0, 0, 0, None) == wq.QMAT_EINVAL
+    assert L.qmat_run_ex(None, 16, 16, 1, 0, 0, 0, 0, None) == wq.QMAT_EINVAL
     assert L.qmat_dequant(None, 16, None) == wq.QMAT_EINVAL
     assert L.qmat_workspace_bytes(None) == 0
     L.qmat_destroy(None)

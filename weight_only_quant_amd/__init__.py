@@ -30,9 +30,9 @@ SIGNATURES = {
     "qmat_pack": (_int, [_int, _i64, _i64, _vp, _vp, _vp, _sz]),
     "qmat_create": (_int, [ctypes.POINTER(_vp), _int, _i64, _i64, _vp, _sz]),
     "qmat_run": (_int, [_vp, _vp, _vp, _int, _vp]),
-    "qmat_run_ex": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _vp]),
+    "qmat_run_ex": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]),
     "qmat_dequant": (_int, [_vp, _vp, _vp]),
-    "qmat_get_plan": (_int, [_vp, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "qmat_get_plan": (_int, [_vp, _int, _int] + [ctypes.POINTER(_int)] * 4),
     "qmat_workspace_bytes": (_sz, [_vp]),
     "qmat_destroy": (None, [_vp]),
     "qmat_last_error": (ctypes.c_char_p, []),
@@ -119,9 +119,10 @@ def qmat_run(handle: int, x, y, T: Optional[int] = None, stream=None) -> None:
 
 
 def qmat_run_ex(handle: int, x, y, T: Optional[int] = None, route: int = QMAT_ROUTE_AUTO,
-                waves: int = 0, splits: int = 0, stream=None) -> None:
+                waves: int = 0, splits: int = 0, stream=None, depth: int = 0) -> None:
     T = x.shape[0] if T is None else T
-    _check(lib().qmat_run_ex(handle, x.data_ptr(), y.data_ptr(), T, route, waves, splits, _stream_handle(stream)))
+    _check(lib().qmat_run_ex(handle, x.data_ptr(), y.data_ptr(), T, route, depth, waves, splits,
+                             _stream_handle(stream)))
 
 
 def qmat_dequant(handle: int, w, stream=None) -> None:
@@ -130,10 +131,10 @@ def qmat_dequant(handle: int, w, stream=None) -> None:
 
 
 def qmat_get_plan(handle: int, T: int, route: int = QMAT_ROUTE_AUTO):
-    """(route, waves, splits) of the launch qmat_run makes for T tokens."""
-    r, w, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(lib().qmat_get_plan(handle, T, route, ctypes.byref(r), ctypes.byref(w), ctypes.byref(s)))
-    return r.value, w.value, s.value
+    """(route, depth, waves, splits) of the launch qmat_run makes for T tokens."""
+    r, d, w, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().qmat_get_plan(handle, T, route, ctypes.byref(r), ctypes.byref(d), ctypes.byref(w), ctypes.byref(s)))
+    return r.value, d.value, w.value, s.value
 
 
 def qmat_workspace_bytes(handle: int) -> int:
@@ -166,14 +167,15 @@ class QMat:
         self.handle = qmat_create(fmt, M, K, packed_dev)
         return self
 
-    def run(self, x, y=None, route: int = QMAT_ROUTE_AUTO, waves: int = 0, splits: int = 0, stream=None):
+    def run(self, x, y=None, route: int = QMAT_ROUTE_AUTO, waves: int = 0, splits: int = 0, stream=None,
+            depth: int = 0):
         import torch
         if y is None:
             y = torch.empty((x.shape[0], self.M), dtype=torch.float32, device=x.device)
-        if route == QMAT_ROUTE_AUTO and not waves and not splits:
+        if route == QMAT_ROUTE_AUTO and not (waves or splits or depth):
             qmat_run(self.handle, x, y, stream=stream)
         else:
-            qmat_run_ex(self.handle, x, y, route=route, waves=waves, splits=splits, stream=stream)
+            qmat_run_ex(self.handle, x, y, route=route, waves=waves, splits=splits, stream=stream, depth=depth)
         return y
 
     def dequant(self, w=None, stream=None):

@@ -146,41 +146,27 @@ void pack_tile(const PackSrc &p, int64_t tile, uint8_t *out)
 // ------------------------------------------------------------------ planning
 
 struct Plan {
-    int route, waves, splits;
+    int route, depth, waves, splits;
 };
 
-// Each wave keeps at least this many 128-wide k units so its loads pipeline.
-constexpr int64_t kMinUnitsPerWave = 3;
 
-// Launch shape for one (route, tokens-per-launch): the grid should fit the GPU in a single
-// round of resident workgroups (no tail of late workgroups), with as many resident waves as
-// possible (bytes in flight), and as few k splits as possible among equally good shapes.
+// Launch shape for one (route, tokens-per-launch).  Measured on MI355X over the benchmark
+// shapes (a sweep of depth x waves x splits): the best shapes use 8 waves per workgroup, keep at
+// least ~2.5 k units (320 columns) per wave, and reach about 4096 waves in total, which needs
+// k splits across workgroups when the matrix has few 64-row tiles.  Nothing is gained from a
+// deeper prefetch ring than one unit per wave at the occupancy these kernels reach.
 Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
 {
-    Plan best{route, 1, 1};
-    int64_t best_rounds = -1, best_waves = -1;
-    for (int waves = 1; waves <= 8; waves *= 2) {
-        if (NU < waves) break;
-        const int bpc = run_blocks_per_cu(fmt, route, Tl, waves);
-        if (bpc <= 0) continue;
-        const int64_t slots = (int64_t)cus * bpc;
-        int64_t splits = slots / NT;
-        const int64_t cap = NU / (waves * kMinUnitsPerWave);
-        if (splits > cap) splits = cap;
-        if (splits < 1) splits = 1;
-        const int64_t wgs = NT * splits;
-        const int64_t rounds = (wgs + slots - 1) / slots;
-        const int64_t resident = (wgs < slots ? wgs : slots) * waves;
-        const bool better = best_rounds < 0 || rounds < best_rounds ||
-                            (rounds == best_rounds && resident > best_waves) ||
-                            (rounds == best_rounds && resident == best_waves && splits < best.splits);
-        if (better) {
-            best = Plan{route, waves, (int)splits};
-            best_rounds = rounds;
-            best_waves = resident;
-        }
-    }
-    return best;
+    (void)fmt;
+    Plan p{route, 1, 8, 1};
+    while (p.waves > 1 && NU < 2 * p.waves) p.waves /= 2;
+    const int64_t target_waves = 16LL * cus;
+    int64_t splits = (2 * NU) / (5 * p.waves);                      // >= 2.5 units per wave
+    const int64_t want = (target_waves + NT * p.waves - 1) / (NT * p.waves);
+    if (splits > want) splits = want;
+    if (splits < 1) splits = 1;
+    p.splits = (int)splits;
+    return p;
 }
 
 }  // namespace
@@ -203,11 +189,14 @@ namespace {
 // tokens one launch of a route handles when the call has T tokens
 int launch_tokens(int route, int T) { return route == kRouteValu ? (T < kValuMaxT ? T : kValuMaxT) : T; }
 
-// The automatic route: the vector-ALU kernel for the smallest T, the MFMA kernel beyond.
+// The automatic route: the vector-ALU kernel (v_dot2c_f32_bf16) for a single token, the MFMA
+// kernel from two tokens on.  Measured on MI355X: at T = 2 the vector-ALU kernel issues twice
+// the dot products per weight and is already 5-15% slower than the MFMA kernel on every
+// benchmark shape; at T = 4 it is up to 1.5x slower (ALU-bound).
 int auto_route(int fmt, int T)
 {
     (void)fmt;
-    return T <= kValuMaxT ? kRouteValu : kRouteMfma;
+    return T <= 1 ? kRouteValu : kRouteMfma;
 }
 
 }  // namespace
@@ -344,7 +333,8 @@ int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packe
     return ok();
 }
 
-int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int waves, int splits, void *stream)
+int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int depth, int waves, int splits,
+                void *stream)
 {
     if (!h) return fail(QMAT_EINVAL, "qmat_run: null handle");
     if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d]", T, kMaxT);
@@ -356,8 +346,10 @@ int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int
     if (!(waves == 0 || waves == 1 || waves == 2 || waves == 4 || waves == 8))
         return fail(QMAT_EINVAL, "qmat_run: waves must be 0, 1, 2, 4 or 8");
     if (splits < 0) return fail(QMAT_EINVAL, "qmat_run: splits must be >= 0");
+    if (depth < 0 || depth > kMaxDepth) return fail(QMAT_EINVAL, "qmat_run: depth must be 0..%d", kMaxDepth);
     const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
     Plan p = h->plan[r - 1][T];
+    if (depth) p.depth = depth;
     if (waves) p.waves = waves;
     if (splits) p.splits = splits;
     if ((int64_t)p.splits * p.waves > h->NU * 64) return fail(QMAT_ESIZE, "qmat_run: too many splits");
@@ -384,20 +376,21 @@ int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int
         a.NU = (int)h->NU;
         a.S = p.splits;
         a.Mpad = (int)h->Mpad;
-        const hipError_t e = launch_run(h->fmt, p.route, a, p.waves, st);
+        const hipError_t e = launch_run(h->fmt, p.route, p.depth, a, p.waves, st);
         if (e != hipSuccess) return fail(QMAT_EHIP, "qmat_run: launch failed: %s", hipGetErrorString(e));
     }
     return ok();
 }
 
-int qmat_get_plan(qmat_t h, int T, int route, int *route_out, int *waves, int *splits)
+int qmat_get_plan(qmat_t h, int T, int route, int *route_out, int *depth, int *waves, int *splits)
 {
-    if (!h || !route_out || !waves || !splits) return fail(QMAT_EINVAL, "qmat_get_plan: null argument");
+    if (!h || !route_out || !depth || !waves || !splits) return fail(QMAT_EINVAL, "qmat_get_plan: null argument");
     if (T < 1 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kMaxT);
     if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA) return fail(QMAT_EINVAL, "qmat_get_plan: bad route %d", route);
     const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
     const Plan &p = h->plan[r - 1][T];
     *route_out = r == kRouteValu ? QMAT_ROUTE_VALU : QMAT_ROUTE_MFMA;
+    *depth = p.depth;
     *waves = p.waves;
     *splits = p.splits;
     return ok();
@@ -405,7 +398,7 @@ int qmat_get_plan(qmat_t h, int T, int route, int *route_out, int *waves, int *s
 
 int qmat_run(qmat_t h, const void *x_dev, float *y_dev, int T, void *stream)
 {
-    return qmat_run_ex(h, x_dev, y_dev, T, QMAT_ROUTE_AUTO, 0, 0, stream);
+    return qmat_run_ex(h, x_dev, y_dev, T, QMAT_ROUTE_AUTO, 0, 0, 0, stream);
 }
 
 int qmat_dequant(qmat_t h, float *w_dev, void *stream)

@@ -32,11 +32,19 @@ enum Route { kRouteValu = 1, kRouteMfma = 2 };
 // Tokens one vector-ALU launch handles; larger T runs as several launches.
 constexpr int kValuMaxT = 4;
 
-hipError_t launch_run(int fmt, int route, const RunArgs &a, int waves, hipStream_t stream);
+// depth: k units in flight per wave (1..kMaxDepth).
+constexpr int kMaxDepth = 3;
+hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, hipStream_t stream);
 hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t stream);
 
 // Workgroups of (64 * waves) threads of the product kernel for (fmt, route, T) that one compute
 // unit holds at once (0 on error).
-int run_blocks_per_cu(int fmt, int route, int T, int waves);
+int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int NU, int S);
+
+// Dynamic LDS bytes of one product launch (activation stage + reduction area).
+size_t run_lds_bytes_for(int route, int waves, int T, int NU, int S);
+
+// Dynamic LDS one workgroup may use.
+constexpr size_t kMaxLds = 64 * 1024;
 
 }  // namespace qmatk

@@ -35,7 +35,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 template <int FMT> struct Fmt;
 // NB: 1 KB blocks per unit.  kToCode: the unpacked value times kToCode is the code (Q4 reads
 // code/16, Q5 8*code, Q6 4*code); the factor is folded into the group scale.
-template <> struct Fmt<4> { static constexpr int NB = 4; static constexpr float kToCode = 16.0f; };
+template <> struct Fmt<4> { static constexpr int NB = 4; static constexpr float kToCode = 0.0625f; };
 template <> struct Fmt<5> { static constexpr int NB = 5; static constexpr float kToCode = 0.125f; };
 template <> struct Fmt<6> { static constexpr int NB = 6; static constexpr float kToCode = 0.25f; };
 template <> struct Fmt<8> { static constexpr int NB = 8; static constexpr float kToCode = 1.0f; };
@@ -51,21 +51,21 @@ template <> __device__ __forceinline__ float nib_lo<0>(uint32_t v)
 template <> __device__ __forceinline__ float nib_lo<1>(uint32_t v)
 {
     float r;
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
+    asm volatile("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
         : "=v"(r) : "v"(v));
     return r;
 }
 template <> __device__ __forceinline__ float nib_lo<2>(uint32_t v)
 {
     float r;
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
+    asm volatile("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
         : "=v"(r) : "v"(v));
     return r;
 }
 template <> __device__ __forceinline__ float nib_lo<3>(uint32_t v)
 {
     float r;
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
+    asm volatile("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
         : "=v"(r) : "v"(v));
     return r;
 }
@@ -92,11 +92,14 @@ template <int FMT, int KA, int MM>
 __device__ __forceinline__ void codes8(const uint32_t *W, float (&f)[8])
 {
     if constexpr (FMT == 4) {
-        const uint32_t n = W[4 * KA + MM], h = n >> 4;
-        f[0] = nib_lo<0>(n); f[1] = nib_lo<0>(h);
-        f[2] = nib_lo<1>(n); f[3] = nib_lo<1>(h);
-        f[4] = nib_lo<2>(n); f[5] = nib_lo<2>(h);
-        f[6] = nib_lo<3>(n); f[7] = nib_lo<3>(h);
+        // nibble e = 2i sits in bits [3:0] of byte i, e = 2i+1 in bits [7:4]; moved to the top
+        // of each byte they read as signed bytes worth 16 * code
+        const uint32_t n = W[4 * KA + MM];
+        const uint32_t lo = (n << 4) & 0xF0F0F0F0u, hi = n & 0xF0F0F0F0u;
+        f[0] = sbyte<0>(lo); f[1] = sbyte<0>(hi);
+        f[2] = sbyte<1>(lo); f[3] = sbyte<1>(hi);
+        f[4] = sbyte<2>(lo); f[5] = sbyte<2>(hi);
+        f[6] = sbyte<3>(lo); f[7] = sbyte<3>(hi);
     } else {
         uint32_t o[2];
         if constexpr (FMT == 5) {
@@ -182,7 +185,7 @@ __device__ __forceinline__ Slice make_slice(const RunArgs &a)
 {
     Slice s;
     s.nw = blockDim.x >> 6;
-    s.w = threadIdx.x >> 6;
+    s.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
     s.tile = blockIdx.x / a.S;
     s.sp = blockIdx.x - s.tile * a.S;
     const int nsl = a.S * s.nw, sl = s.sp * s.nw + s.w;
@@ -268,20 +271,27 @@ __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *
 
 // ------------------------------------------------------------------ unit loads
 
-template <int NB> struct UnitRaw {
+// What one lane needs for one 128-wide k unit: its NB packed code slots, its scale slot and the
+// XN vectors of 8 bf16 activations the unit multiplies.
+template <int NB, int XN> struct Unit {
     u32x4_t c[NB];
     u32x4_t sc;
+    u32x4_t x[XN];
 };
 
-template <int FMT>
-__device__ __forceinline__ void load_unit(const RunArgs &a, int tile, int u, int lane, UnitRaw<Fmt<FMT>::NB> &r)
+
+// Packed weights are read exactly once per call: nontemporal loads keep them from displacing
+// the activations (reused by every row tile) in the caches.
+__device__ __forceinline__ u32x4_t stream_load(const u32x4_t *p) { return __builtin_nontemporal_load(p); }
+
+template <int FMT, int NB, int XN>
+__device__ __forceinline__ void load_weights(const RunArgs &a, int tile, int u, int lane, Unit<NB, XN> &r)
 {
-    constexpr int NB = Fmt<FMT>::NB;
     const u32x4_t *cp = reinterpret_cast<const u32x4_t *>(a.codes) + (((int64_t)tile * a.NU + u) * NB) * 64 + lane;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) r.c[j] = cp[j * 64];
+    for (int j = 0; j < NB; ++j) r.c[j] = stream_load(cp + j * 64);
     if constexpr (FMT != 8)
-        r.sc = reinterpret_cast<const u32x4_t *>(a.scales)[((int64_t)tile * a.NU + u) * 16 + (lane & 15)];
+        r.sc = stream_load(reinterpret_cast<const u32x4_t *>(a.scales) + ((int64_t)tile * a.NU + u) * 16 + (lane & 15));
 }
 
 // 8 bf16 activations (one k octet) of token t at column k, clamped inside the row: the
@@ -292,23 +302,72 @@ __device__ __forceinline__ u32x4_t load_x8(const RunArgs &a, int t, int k)
     return *reinterpret_cast<const u32x4_t *>(a.x + (int64_t)t * a.K + kk);
 }
 
+// Software pipeline over a wave's units [u0, u1): a ring of D units in flight; a slot is
+// refilled with unit u + D right after unit u has been consumed from it.  mid() runs once
+// after the first loads are issued (their latency hides it).
+template <int D, typename U, typename Load, typename Mid, typename Use>
+__device__ __forceinline__ void pipeline(int u0, int u1, U (&buf)[D], Load load, Mid mid, Use use)
+{
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (u0 + d < u1) load(buf[d], u0 + d);
+    mid();
+    for (int u = u0; u < u1; u += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (u + d < u1) {
+                use(buf[d], u + d);
+                if (u + d + D < u1) load(buf[d], u + d + D);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ vector-ALU route
 
-template <int FMT, int TT, int KA, int MM>
-__device__ __forceinline__ void valu_step(const uint32_t *W, const u32x4_t (&xv)[4][TT], float (&p)[4][TT])
+template <int FMT, int TT, int KA, int MM, int NB, int XN>
+__device__ __forceinline__ void valu_step(const Unit<NB, XN> &U, float (&p)[4][TT])
 {
+    const uint32_t *W = reinterpret_cast<const uint32_t *>(U.c);
     uint32_t b[4];
     bf16x8_of<FMT, KA, MM>(W, b);
 #pragma unroll
     for (int t = 0; t < TT; ++t)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) p[MM][t] = dot2(b[d], xv[KA][t][d], p[MM][t]);
+        for (int d = 0; d < 4; ++d) p[MM][t] = dot2(b[d], U.x[4 * t + KA][d], p[MM][t]);
 }
 
-template <int FMT, int TT>
+template <int FMT, int TT, int G, int NB, int XN>
+__device__ __forceinline__ void valu_group(const Unit<NB, XN> &U, float (&acc)[4][TT])
+{
+    float p[4][TT];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) p[m][t] = 0.f;
+    valu_step<FMT, TT, 2 * G, 0>(U, p); valu_step<FMT, TT, 2 * G, 1>(U, p);
+    valu_step<FMT, TT, 2 * G, 2>(U, p); valu_step<FMT, TT, 2 * G, 3>(U, p);
+    valu_step<FMT, TT, 2 * G + 1, 0>(U, p); valu_step<FMT, TT, 2 * G + 1, 1>(U, p);
+    valu_step<FMT, TT, 2 * G + 1, 2>(U, p); valu_step<FMT, TT, 2 * G + 1, 3>(U, p);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        if constexpr (FMT == 8) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) acc[m][t] += p[m][t];
+        } else {
+            const float sf = group_scale(U.sc, G, m);
+#pragma unroll
+            for (int t = 0; t < TT; ++t) acc[m][t] = fmaf(sf, p[m][t], acc[m][t]);
+        }
+    }
+}
+
+// Lane L handles rows 16*m + L%16 (m = 0..3) and k octet L/16 of every 32-wide k step, for TT
+// tokens; the four lanes sharing L%16 are summed at the end.
+template <int FMT, int TT, int D>
 __global__ __launch_bounds__(512) void valu_kernel(RunArgs a)
 {
-    constexpr int NB = Fmt<FMT>::NB;
+    constexpr int NB = Fmt<FMT>::NB, XN = 4 * TT;
     extern __shared__ float red[];
     const Slice s = make_slice(a);
     const int lane = threadIdx.x & 63, q = lane >> 4;
@@ -318,55 +377,28 @@ __global__ __launch_bounds__(512) void valu_kernel(RunArgs a)
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[m][t] = 0.f;
 
-    UnitRaw<NB> cur, nxt;
-    if (s.u0 < s.u1) load_unit<FMT>(a, s.tile, s.u0, lane, cur);
-    for (int u = s.u0; u < s.u1; ++u) {
-        u32x4_t xv[4][TT];
+    Unit<NB, XN> buf[D];
+    pipeline<D>(s.u0, s.u1, buf,
+        [&](Unit<NB, XN> &r, int u) {
+            load_weights<FMT>(a, s.tile, u, lane, r);
 #pragma unroll
-        for (int ka = 0; ka < 4; ++ka)
+            for (int t = 0; t < TT; ++t)
 #pragma unroll
-            for (int t = 0; t < TT; ++t) xv[ka][t] = load_x8(a, t, u * kUnitK + 32 * ka + 8 * q);
-        if (u + 1 < s.u1) load_unit<FMT>(a, s.tile, u + 1, lane, nxt);
-        const uint32_t *W = reinterpret_cast<const uint32_t *>(cur.c);
+                for (int ka = 0; ka < 4; ++ka) r.x[4 * t + ka] = load_x8(a, t, u * kUnitK + 32 * ka + 8 * q);
+        },
+        [&]() {},
+        [&](const Unit<NB, XN> &U, int) {
+            valu_group<FMT, TT, 0>(U, acc);
+            valu_group<FMT, TT, 1>(U, acc);
+        });
+
+    // the code encoding's power of two (groupwise) or the row scale (FP8), once per row
+    f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
+    if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)s.tile * 16 + (lane & 15)];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            float p[4][TT];
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int t = 0; t < TT; ++t) p[m][t] = 0.f;
-            if (g == 0) {
-                valu_step<FMT, TT, 0, 0>(W, xv, p); valu_step<FMT, TT, 0, 1>(W, xv, p);
-                valu_step<FMT, TT, 0, 2>(W, xv, p); valu_step<FMT, TT, 0, 3>(W, xv, p);
-                valu_step<FMT, TT, 1, 0>(W, xv, p); valu_step<FMT, TT, 1, 1>(W, xv, p);
-                valu_step<FMT, TT, 1, 2>(W, xv, p); valu_step<FMT, TT, 1, 3>(W, xv, p);
-            } else {
-                valu_step<FMT, TT, 2, 0>(W, xv, p); valu_step<FMT, TT, 2, 1>(W, xv, p);
-                valu_step<FMT, TT, 2, 2>(W, xv, p); valu_step<FMT, TT, 2, 3>(W, xv, p);
-                valu_step<FMT, TT, 3, 0>(W, xv, p); valu_step<FMT, TT, 3, 1>(W, xv, p);
-                valu_step<FMT, TT, 3, 2>(W, xv, p); valu_step<FMT, TT, 3, 3>(W, xv, p);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if constexpr (FMT == 8) {
-#pragma unroll
-                    for (int t = 0; t < TT; ++t) acc[m][t] += p[m][t];
-                } else {
-                    const float sf = group_scale(cur.sc, g, m) * Fmt<FMT>::kToCode;
-#pragma unroll
-                    for (int t = 0; t < TT; ++t) acc[m][t] = fmaf(sf, p[m][t], acc[m][t]);
-                }
-            }
-        }
-        if (u + 1 < s.u1) cur = nxt;
-    }
-    if constexpr (FMT == 8) {
-        const f32x4_t rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)s.tile * 16 + (lane & 15)];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int t = 0; t < TT; ++t) acc[m][t] *= rs[m];
-    }
+        for (int t = 0; t < TT; ++t) acc[m][t] *= rs[m];
     // the four lanes L, L^16, L^32, L^48 hold the same rows for different k octets
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -389,16 +421,17 @@ __global__ __launch_bounds__(512) void valu_kernel(RunArgs a)
 
 // ------------------------------------------------------------------ MFMA route
 
-template <int FMT, int KA>
-__device__ __forceinline__ void mfma_step(const uint32_t *W, const u32x4_t &xa, f32x4_t (&D)[4])
+template <int FMT, int KA, int NB, int XN>
+__device__ __forceinline__ void mfma_step(const Unit<NB, XN> &U, f32x4_t (&D)[4])
 {
-    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, xa);
-#define QMAT_MFMA_ROW(MM)                                                              \
-    {                                                                                  \
-        uint32_t b[4];                                                                 \
-        bf16x8_of<FMT, KA, MM>(W, b);                                                  \
-        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, (u32x4_t){b[0], b[1], b[2], b[3]}); \
-        D[MM] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, D[MM], 0, 0, 0);        \
+    const uint32_t *W = reinterpret_cast<const uint32_t *>(U.c);
+    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, U.x[KA]);
+#define QMAT_MFMA_ROW(MM)                                                                       \
+    {                                                                                           \
+        uint32_t b[4];                                                                          \
+        bf16x8_of<FMT, KA, MM>(W, b);                                                           \
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, (u32x4_t){b[0], b[1], b[2], b[3]});     \
+        D[MM] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, D[MM], 0, 0, 0);                 \
     }
     QMAT_MFMA_ROW(0) QMAT_MFMA_ROW(1) QMAT_MFMA_ROW(2) QMAT_MFMA_ROW(3)
 #undef QMAT_MFMA_ROW
@@ -407,10 +440,10 @@ __device__ __forceinline__ void mfma_step(const uint32_t *W, const u32x4_t &xa, 
 // A operand: 16 tokens x 32 k (lane l: token l % 16, k octet l / 16); B operand: 32 k x 16 rows
 // of the tile (lane l: row 16*m + l % 16, the same k octet) — exactly the packed layout.
 // D[m]: lane l holds tokens 4*(l/16) + r (r = 0..3) of row 16*m + l % 16.
-template <int FMT>
+template <int FMT, int D_>
 __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
 {
-    constexpr int NB = Fmt<FMT>::NB;
+    constexpr int NB = Fmt<FMT>::NB, XN = 4;
     extern __shared__ float red[];
     const Slice s = make_slice(a);
     const int lane = threadIdx.x & 63, tok = lane & 15, oct = lane >> 4;
@@ -419,48 +452,48 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    UnitRaw<NB> cur, nxt;
-    if (s.u0 < s.u1) load_unit<FMT>(a, s.tile, s.u0, lane, cur);
-    for (int u = s.u0; u < s.u1; ++u) {
-        u32x4_t xa[4];
+    Unit<NB, XN> buf[D_];
+    pipeline<D_>(s.u0, s.u1, buf,
+        [&](Unit<NB, XN> &r, int u) {
+            load_weights<FMT>(a, s.tile, u, lane, r);
 #pragma unroll
-        for (int ka = 0; ka < 4; ++ka)
-            xa[ka] = tok_ok ? load_x8(a, tok, u * kUnitK + 32 * ka + 8 * oct) : (u32x4_t){0u, 0u, 0u, 0u};
-        if (u + 1 < s.u1) load_unit<FMT>(a, s.tile, u + 1, lane, nxt);
-        const uint32_t *W = reinterpret_cast<const uint32_t *>(cur.c);
-        if constexpr (FMT == 8) {
-            mfma_step<FMT, 0>(W, xa[0], acc);
-            mfma_step<FMT, 1>(W, xa[1], acc);
-            mfma_step<FMT, 2>(W, xa[2], acc);
-            mfma_step<FMT, 3>(W, xa[3], acc);
-        } else {
+            for (int ka = 0; ka < 4; ++ka)
+                r.x[ka] = tok_ok ? load_x8(a, tok, u * kUnitK + 32 * ka + 8 * oct) : (u32x4_t){0u, 0u, 0u, 0u};
+        },
+        [&]() {},
+        [&](const Unit<NB, XN> &U, int) {
+            if constexpr (FMT == 8) {
+                mfma_step<FMT, 0>(U, acc);
+                mfma_step<FMT, 1>(U, acc);
+                mfma_step<FMT, 2>(U, acc);
+                mfma_step<FMT, 3>(U, acc);
+            } else {
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                f32x4_t D[4];
+                for (int g = 0; g < 2; ++g) {
+                    f32x4_t P[4];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) D[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-                if (g == 0) {
-                    mfma_step<FMT, 0>(W, xa[0], D);
-                    mfma_step<FMT, 1>(W, xa[1], D);
-                } else {
-                    mfma_step<FMT, 2>(W, xa[2], D);
-                    mfma_step<FMT, 3>(W, xa[3], D);
-                }
+                    for (int m = 0; m < 4; ++m) P[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                    if (g == 0) {
+                        mfma_step<FMT, 0>(U, P);
+                        mfma_step<FMT, 1>(U, P);
+                    } else {
+                        mfma_step<FMT, 2>(U, P);
+                        mfma_step<FMT, 3>(U, P);
+                    }
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float sf = group_scale(cur.sc, g, m) * Fmt<FMT>::kToCode;
+                    for (int m = 0; m < 4; ++m) {
+                        const float sf = group_scale(U.sc, g, m);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[m][r] = fmaf(sf, D[m][r], acc[m][r]);
+                        for (int r = 0; r < 4; ++r) acc[m][r] = fmaf(sf, P[m][r], acc[m][r]);
+                    }
                 }
             }
-        }
-        if (u + 1 < s.u1) cur = nxt;
-    }
-    if constexpr (FMT == 8) {
-        const f32x4_t rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)s.tile * 16 + (lane & 15)];
+        });
+
+    f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
+    if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)s.tile * 16 + (lane & 15)];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m] *= rs[m];
-    }
+    for (int m = 0; m < 4; ++m) acc[m] *= rs[m];
     const int t0 = 4 * oct, rr = lane & 15;
     finish(a, s, red, [&](auto put) {
 #pragma unroll
@@ -529,46 +562,65 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a)
 
 // ------------------------------------------------------------------ launchers
 
-template <int FMT> static const void *run_kernel(int route, int T)
+template <int FMT, int D> static const void *run_kernel_d(int route, int T)
 {
-    if (route == kRouteMfma) return reinterpret_cast<const void *>(&mfma_kernel<FMT>);
+    if (route == kRouteMfma) return reinterpret_cast<const void *>(&mfma_kernel<FMT, D>);
     switch (T) {
-    case 1: return reinterpret_cast<const void *>(&valu_kernel<FMT, 1>);
-    case 2: return reinterpret_cast<const void *>(&valu_kernel<FMT, 2>);
-    case 3: return reinterpret_cast<const void *>(&valu_kernel<FMT, 3>);
-    case 4: return reinterpret_cast<const void *>(&valu_kernel<FMT, 4>);
+    case 1: return reinterpret_cast<const void *>(&valu_kernel<FMT, 1, D>);
+    case 2: return reinterpret_cast<const void *>(&valu_kernel<FMT, 2, D>);
+    case 3: return reinterpret_cast<const void *>(&valu_kernel<FMT, 3, D>);
+    case 4: return reinterpret_cast<const void *>(&valu_kernel<FMT, 4, D>);
     default: return nullptr;
     }
 }
 
-static const void *run_kernel_for(int fmt, int route, int T)
+template <int FMT> static const void *run_kernel(int route, int T, int depth)
+{
+    switch (depth) {
+    case 1: return run_kernel_d<FMT, 1>(route, T);
+    case 2: return run_kernel_d<FMT, 2>(route, T);
+    case 3: return run_kernel_d<FMT, 3>(route, T);
+    default: return nullptr;
+    }
+}
+
+static const void *run_kernel_for(int fmt, int route, int T, int depth)
 {
     switch (fmt) {
-    case 4: return run_kernel<4>(route, T);
-    case 5: return run_kernel<5>(route, T);
-    case 6: return run_kernel<6>(route, T);
-    case 8: return run_kernel<8>(route, T);
+    case 4: return run_kernel<4>(route, T, depth);
+    case 5: return run_kernel<5>(route, T, depth);
+    case 6: return run_kernel<6>(route, T, depth);
+    case 8: return run_kernel<8>(route, T, depth);
     default: return nullptr;
     }
 }
 
-static size_t run_lds_bytes(int waves, int T) { return waves > 1 ? (size_t)waves * T * kTileRows * sizeof(float) : 0; }
-
-hipError_t launch_run(int fmt, int route, const RunArgs &a, int waves, hipStream_t st)
+static size_t run_lds_bytes(int route, int waves, int T, int NU, int S)
 {
-    const void *k = run_kernel_for(fmt, route, a.T);
+    (void)route;
+    (void)NU;
+    (void)S;
+    return waves > 1 ? (size_t)waves * T * kTileRows * sizeof(float) : 0;
+}
+
+size_t run_lds_bytes_for(int route, int waves, int T, int NU, int S) { return run_lds_bytes(route, waves, T, NU, S); }
+
+hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, hipStream_t st)
+{
+    const void *k = run_kernel_for(fmt, route, a.T, depth);
     if (!k) return hipErrorInvalidValue;
     RunArgs arg = a;
     void *args[] = {&arg};
     return hipLaunchKernel(k, dim3((unsigned)(a.NT * a.S)), dim3((unsigned)(64 * waves)), args,
-                           run_lds_bytes(waves, a.T), st);
+                           run_lds_bytes(route, waves, a.T, a.NU, a.S), st);
 }
 
-int run_blocks_per_cu(int fmt, int route, int T, int waves)
+int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int NU, int S)
 {
-    const void *k = run_kernel_for(fmt, route, T);
+    const void *k = run_kernel_for(fmt, route, T, depth);
     int n = 0;
-    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * waves, run_lds_bytes(waves, T)) != hipSuccess)
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * waves, run_lds_bytes(route, waves, T, NU, S)) !=
+                  hipSuccess)
         return 0;
     return n;
 }

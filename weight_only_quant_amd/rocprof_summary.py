@@ -1,0 +1,111 @@
+"""Summarise rocprofv3 CSV output for the qmat kernels.
+
+    python -m weight_only_quant_amd.rocprof_summary trace <kernel_trace.csv> [--out summary.md]
+    python -m weight_only_quant_amd.rocprof_summary traffic --fetch <fetch.csv> --write <write.csv>
+        --copy-fetch <copy_fetch.csv> --copy-write <copy_write.csv> --copy-bytes N
+        --kernel <substring> --grid <grid size> --workload <name> --alg-bytes N --out traffic.json
+
+trace:   per (kernel, grid size) dispatch count and mean/median/min duration.
+traffic: HBM bytes per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE (KiB per
+         dispatch), each scaled by what the same counter reports for a device copy of known
+         size (the counters need not cover every memory channel).  The JSON also records the
+         SHA-256 of the kernel source so that a later change to the kernels invalidates it.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "qmat_kernels.hip")
+
+
+def kernel_source_sha256() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _short(name: str) -> str:
+    return name.replace("void qmatk::", "").replace("(qmatk::RunArgs)", "").replace("(qmatk::DequantArgs)", "")
+
+
+def trace_summary(path: str):
+    rows = list(csv.DictReader(open(path)))
+    d = collections.defaultdict(list)
+    for r in rows:
+        grid = r.get("Grid_Size_X") or r.get("Grid_Size")
+        d[(_short(r["Kernel_Name"]), grid, r.get("Workgroup_Size_X") or r.get("Workgroup_Size"))].append(
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = []
+    for (k, g, wg), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        out.append({"kernel": k, "grid": int(g), "workgroup": int(wg), "calls": len(v),
+                    "mean_us": sum(v) / len(v) / 1e3, "median_us": statistics.median(v) / 1e3, "min_us": min(v) / 1e3})
+    return out
+
+
+def counter_mean(path: str, counter: str, kernel: str, grid: str = None) -> float:
+    vals = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter or kernel not in r["Kernel_Name"]:
+            continue
+        if grid is not None and r["Grid_Size"] != str(grid):
+            continue
+        vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernel {kernel!r} grid {grid} in {path}")
+    return sum(vals) / len(vals)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("csv")
+    t.add_argument("--out")
+    t.add_argument("--command", default="")
+    f = sub.add_parser("traffic")
+    for a in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "grid", "workload", "out"):
+        f.add_argument("--" + a.replace("_", "-"), required=True)
+    f.add_argument("--copy-bytes", type=int, required=True)
+    f.add_argument("--alg-bytes", type=int, required=True)
+    f.add_argument("--command", default="")
+    args = ap.parse_args(argv)
+    if args.cmd == "trace":
+        rows = trace_summary(args.csv)
+        lines = ["| kernel | grid | workgroup | calls | mean us | median us | min us |", "|---|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| {r['kernel']} | {r['grid']} | {r['workgroup']} | {r['calls']} | {r['mean_us']:.2f} | "
+                         f"{r['median_us']:.2f} | {r['min_us']:.2f} |")
+        text = "\n".join(lines) + "\n"
+        if args.command:
+            text = f"Command: `{args.command}`\n\n" + text
+        if args.out:
+            with open(args.out, "w") as fh:
+                fh.write(text)
+        print(text)
+        return
+    fetch_kib = counter_mean(args.fetch, "FETCH_SIZE", args.kernel, args.grid)
+    write_kib = counter_mean(args.write, "WRITE_SIZE", args.kernel, args.grid)
+    copy_fetch_kib = counter_mean(args.copy_fetch, "FETCH_SIZE", "copyBuffer")
+    copy_write_kib = counter_mean(args.copy_write, "WRITE_SIZE", "copyBuffer")
+    fs = args.copy_bytes / (copy_fetch_kib * 1024)
+    ws = args.copy_bytes / (copy_write_kib * 1024)
+    traffic = fetch_kib * 1024 * fs + write_kib * 1024 * ws
+    rec = {"workload": args.workload, "kernel": args.kernel, "grid": int(args.grid),
+           "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
+           "copy_bytes": args.copy_bytes, "copy_fetch_kib": copy_fetch_kib, "copy_write_kib": copy_write_kib,
+           "fetch_scale": fs, "write_scale": ws, "traffic_bytes": traffic, "algorithmic_bytes": args.alg_bytes,
+           "traffic_over_algorithmic": traffic / args.alg_bytes, "kernel_source_sha256": kernel_source_sha256(),
+           "command": args.command}
+    with open(args.out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
