@@ -150,20 +150,24 @@ struct Plan {
 };
 
 
-// Launch shape for one (route, tokens-per-launch).  Measured on MI355X over the benchmark
-// shapes (a sweep of depth x waves x splits): the best shapes use 8 waves per workgroup, keep at
-// least ~2.5 k units (320 columns) per wave, and reach about 4096 waves in total, which needs
-// k splits across workgroups when the matrix has few 64-row tiles.  Nothing is gained from a
-// deeper prefetch ring than one unit per wave at the occupancy these kernels reach.
+// Launch shape for one (route, tokens-per-launch), from a sweep of depth x waves x splits over
+// the benchmark shapes on MI355X.  Vector-ALU kernel: two 128-k units in flight per wave;
+// MFMA kernel: one.  Workgroups of 4 (vector ALU) or 8 (MFMA) waves split each tile's k units;
+// matrices with at least 2048 row tiles use single-wave workgroups (one wave streams a whole
+// tile).  Tiles are split along K across workgroups only until about 4 (vector ALU) or 8 (MFMA)
+// waves per compute unit exist (narrow matrices such as the K = 17408 down projection): more
+// splits cost more in partial-sum traffic and the last-arrival reduction than they gain.
 Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
 {
     (void)fmt;
-    Plan p{route, 1, 8, 1};
+    (void)Tl;
+    const bool valu = route == kRouteValu;
+    Plan p{route, valu ? 2 : 1, NT >= 2048 ? 1 : (valu ? 4 : 8), 1};
     while (p.waves > 1 && NU < 2 * p.waves) p.waves /= 2;
-    const int64_t target_waves = 16LL * cus;
-    int64_t splits = (2 * NU) / (5 * p.waves);                      // >= 2.5 units per wave
-    const int64_t want = (target_waves + NT * p.waves - 1) / (NT * p.waves);
-    if (splits > want) splits = want;
+    const int64_t target_waves = (valu ? 4LL : 8LL) * cus;
+    int64_t splits = (target_waves + (NT * p.waves) / 2) / (NT * p.waves);  // rounded
+    const int64_t cap = (2 * NU) / (5 * p.waves);                          // >= 2.5 units per wave
+    if (splits > cap) splits = cap;
     if (splits < 1) splits = 1;
     p.splits = (int)splits;
     return p;

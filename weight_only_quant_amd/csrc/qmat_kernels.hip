@@ -304,20 +304,54 @@ __device__ __forceinline__ u32x4_t load_x8(const RunArgs &a, int t, int k)
 
 // Software pipeline over a wave's units [u0, u1): a ring of D units in flight; a slot is
 // refilled with unit u + D right after unit u has been consumed from it.  mid() runs once
-// after the first loads are issued (their latency hides it).
+// after the first loads are issued (their latency hides it).  The steady-state loop has no
+// branches inside, so the compiler's wait counting sees that only the slot being consumed
+// has to have arrived; the guarded tail handles the last units.
 template <int D, typename U, typename Load, typename Mid, typename Use>
 __device__ __forceinline__ void pipeline(int u0, int u1, U (&buf)[D], Load load, Mid mid, Use use)
 {
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-        if (u0 + d < u1) load(buf[d], u0 + d);
-    mid();
-    for (int u = u0; u < u1; u += D) {
+    if (u1 - u0 >= 2 * D) {
+        // every slot is filled and refilled at least once: no guards until the tail.  The
+        // slots are issued in order (as the loop refills them) so that the wait counts at the
+        // loop head are the same on entry and on the back edge.
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (u + d < u1) {
+            load(buf[d], u0 + d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mid();
+        int u = u0;
+        do {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
                 use(buf[d], u + d);
-                if (u + d + D < u1) load(buf[d], u + d + D);
+                load(buf[d], u + d + D);
+                // keep the refill ahead of the next slot's arithmetic
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            u += D;
+        } while (u + 2 * D <= u1);
+        // D <= u1 - u < 2D units left; the slots hold units u .. u + D - 1
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            use(buf[d], u + d);
+            if (u + d + D < u1) load(buf[d], u + d + D);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (u + D + d < u1) use(buf[d], u + D + d);
+    } else {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (u0 + d < u1) load(buf[d], u0 + d);
+        mid();
+        for (int u = u0; u < u1; u += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (u + d < u1) {
+                    use(buf[d], u + d);
+                    if (u + d + D < u1) load(buf[d], u + d + D);
+                }
             }
         }
     }
@@ -447,7 +481,8 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
     extern __shared__ float red[];
     const Slice s = make_slice(a);
     const int lane = threadIdx.x & 63, tok = lane & 15, oct = lane >> 4;
-    const bool tok_ok = tok < a.T;
+    // A rows of tokens >= T only feed D rows that are never stored: load a valid token instead
+    const int tok_c = tok < a.T ? tok : a.T - 1;
     f32x4_t acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -458,7 +493,7 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
             load_weights<FMT>(a, s.tile, u, lane, r);
 #pragma unroll
             for (int ka = 0; ka < 4; ++ka)
-                r.x[ka] = tok_ok ? load_x8(a, tok, u * kUnitK + 32 * ka + 8 * oct) : (u32x4_t){0u, 0u, 0u, 0u};
+                r.x[ka] = load_x8(a, tok_c, u * kUnitK + 32 * ka + 8 * oct);
         },
         [&]() {},
         [&](const Unit<NB, XN> &U, int) {
