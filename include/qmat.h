@@ -102,7 +102,7 @@ int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream
 
 /* qmat_run with an explicit kernel route and launch shape, for tests and tuning.
  *   route:  qmat_route.
- *   depth:  128-wide k units each wave keeps in flight (1..3; 0 = auto).
+ *   depth:  128-wide k units each wave keeps in flight (1 or 2; 0 = auto).
  *   waves:  waves per workgroup splitting K inside one workgroup (1, 2, 4 or 8; 0 = auto).
  *   splits: workgroups splitting K across the grid (>= 1; 0 = auto); the partial sums go
  *           through the handle's workspace and are added in a fixed order.

@@ -127,23 +127,25 @@ def test_run_parity_small(route, fmt, M, K):
 
 
 @pytest.mark.parametrize("fmt", [4, 5, 6, 8])
-@pytest.mark.parametrize("route", ["valu", "mfma"])
-def test_run_split_shapes_agree(fmt, route):
-    # every (waves, splits) launch shape gives an in-tolerance result; each is deterministic
-    M, K, T = 200, 2176, 4 if route == "valu" else 9
-    wl = _workload(fmt, M, K, T, 7 + fmt)
+@pytest.mark.parametrize("route,T", [("valu", 1), ("valu", 4), ("mfma", 1), ("mfma", 9)])
+def test_run_split_shapes_agree(fmt, route, T):
+    # every (depth, waves, splits) launch shape gives an in-tolerance result; each is
+    # deterministic.  T = 1 on the MFMA route is its single-token specialization.
+    M, K = 200, 2176
+    wl = _workload(fmt, M, K, T, 7 + fmt + T)
     qm = wq.QMat(fmt, wl.codes, wl.scales)
     xd = _x_dev(wl.x)
-    for waves in (1, 2, 4, 8):
-        for splits in (1, 2, 3, 5):
-            say(f"split {route} fmt={fmt} waves={waves} splits={splits}")
-            y1 = torch.empty((T, M), device="cuda")
-            y2 = torch.empty((T, M), device="cuda")
-            wq.qmat_run_ex(qm.handle, xd, y1, T, route=ROUTES[route], waves=waves, splits=splits)
-            wq.qmat_run_ex(qm.handle, xd, y2, T, route=ROUTES[route], waves=waves, splits=splits)
-            torch.cuda.synchronize()
-            assert torch.equal(y1, y2)
-            _check_y(y1, wl, f"{route} waves={waves} splits={splits}")
+    for depth in (1, 2):
+        for waves in (1, 2, 4, 8):
+            for splits in (1, 2, 3, 5):
+                say(f"split {route} fmt={fmt} T={T} depth={depth} waves={waves} splits={splits}")
+                y1 = torch.empty((T, M), device="cuda")
+                y2 = torch.empty((T, M), device="cuda")
+                wq.qmat_run_ex(qm.handle, xd, y1, T, route=ROUTES[route], waves=waves, splits=splits, depth=depth)
+                wq.qmat_run_ex(qm.handle, xd, y2, T, route=ROUTES[route], waves=waves, splits=splits, depth=depth)
+                torch.cuda.synchronize()
+                assert torch.equal(y1, y2)
+                _check_y(y1, wl, f"{route} T={T} depth={depth} waves={waves} splits={splits}")
 
 
 def _exact_workload(fmt, M, K, T, seed):

@@ -150,21 +150,43 @@ struct Plan {
 };
 
 
-// Launch shape for one (route, tokens-per-launch), from a sweep of depth x waves x splits over
-// the benchmark shapes on MI355X.  Vector-ALU kernel: two 128-k units in flight per wave;
-// MFMA kernel: one.  Workgroups of 4 (vector ALU) or 8 (MFMA) waves split each tile's k units;
-// matrices with at least 2048 row tiles use single-wave workgroups (one wave streams a whole
-// tile).  Tiles are split along K across workgroups only until about 4 (vector ALU) or 8 (MFMA)
-// waves per compute unit exist (narrow matrices such as the K = 17408 down projection): more
-// splits cost more in partial-sum traffic and the last-arrival reduction than they gain.
+// Launch shape for one (route, tokens-per-launch), from graph-timed sweeps of depth x waves x
+// splits over the benchmark shapes on MI355X (within 3% of the best measured shape on each).
+//
+// MFMA kernel.  Matrices of at least 2048 row tiles: one tile per workgroup, never split; 4
+// waves share a tile's k units at T = 1 (a single token leaves registers for two units in
+// flight), 1 wave otherwise.  Narrower matrices: 4 waves per workgroup up to T = 4, 8 beyond,
+// and tiles split along K across workgroups until about 8 waves per compute unit exist, at
+// most 3 ways (every split adds a round of partial-sum traffic and a last-arrival reduction at
+// the end of the kernel; 4 and more splits measured slower on every shape).  Two units in
+// flight per wave, except with 8-wave workgroups at T > 1, whose register footprint would
+// leave room for only one workgroup per compute unit.
+//
+// Vector-ALU kernel (explicit requests only): two units in flight, 4 waves per workgroup,
+// single-wave workgroups for wide matrices, splits up to about 4 waves per compute unit.
 Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
 {
     (void)fmt;
-    (void)Tl;
-    const bool valu = route == kRouteValu;
-    Plan p{route, valu ? 2 : 1, NT >= 2048 ? 1 : (valu ? 4 : 8), 1};
+    if (route == kRouteMfma) {
+        Plan p{route, 2, 1, 1};
+        if (NT >= 2048) {
+            p.waves = Tl == 1 ? 4 : 1;
+        } else {
+            p.waves = Tl <= 4 ? 4 : 8;
+            const int64_t target_waves = 8LL * cus;
+            int64_t splits = (target_waves + NT * p.waves - 1) / (NT * p.waves);
+            if (splits > 3) splits = 3;
+            if (splits > NU / p.waves) splits = NU / p.waves;
+            if (splits < 1) splits = 1;
+            p.splits = (int)splits;
+        }
+        while (p.waves > 1 && NU < (int64_t)p.waves * p.splits) p.waves /= 2;
+        if (Tl > 1 && p.waves == 8) p.depth = 1;
+        return p;
+    }
+    Plan p{route, 2, NT >= 2048 ? 1 : 4, 1};
     while (p.waves > 1 && NU < 2 * p.waves) p.waves /= 2;
-    const int64_t target_waves = (valu ? 4LL : 8LL) * cus;
+    const int64_t target_waves = 4LL * cus;
     int64_t splits = (target_waves + (NT * p.waves) / 2) / (NT * p.waves);  // rounded
     const int64_t cap = (2 * NU) / (5 * p.waves);                          // >= 2.5 units per wave
     if (splits > cap) splits = cap;
@@ -193,14 +215,16 @@ namespace {
 // tokens one launch of a route handles when the call has T tokens
 int launch_tokens(int route, int T) { return route == kRouteValu ? (T < kValuMaxT ? T : kValuMaxT) : T; }
 
-// The automatic route: the vector-ALU kernel (v_dot2c_f32_bf16) for a single token, the MFMA
-// kernel from two tokens on.  Measured on MI355X: at T = 2 the vector-ALU kernel issues twice
-// the dot products per weight and is already 5-15% slower than the MFMA kernel on every
-// benchmark shape; at T = 4 it is up to 1.5x slower (ALU-bound).
+// The automatic route is the MFMA kernel for every T.  Both routes unpack each code to bf16
+// with the vector ALU; the MFMA kernel then spends one matrix-core instruction per 8 weights
+// per lane where the vector-ALU kernel spends four v_dot2c_f32_bf16, and the vector ALU is what
+// keeps these kernels from the HBM roofline (measured on MI355X: the MFMA kernel is 2-13%
+// faster at T = 1 on the benchmark shapes, and far faster from T = 2).
 int auto_route(int fmt, int T)
 {
     (void)fmt;
-    return T <= 1 ? kRouteValu : kRouteMfma;
+    (void)T;
+    return kRouteMfma;
 }
 
 }  // namespace

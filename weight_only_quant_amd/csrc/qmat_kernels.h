@@ -33,7 +33,7 @@ enum Route { kRouteValu = 1, kRouteMfma = 2 };
 constexpr int kValuMaxT = 4;
 
 // depth: k units in flight per wave (1..kMaxDepth).
-constexpr int kMaxDepth = 3;
+constexpr int kMaxDepth = 2;
 hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, hipStream_t stream);
 hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t stream);
 

@@ -34,8 +34,8 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 template <int FMT> struct Fmt;
 // NB: 1 KB blocks per unit.  kToCode: the unpacked value times kToCode is the code (Q4 reads
-// code/16, Q5 8*code, Q6 4*code); the factor is folded into the group scale.
-template <> struct Fmt<4> { static constexpr int NB = 4; static constexpr float kToCode = 0.0625f; };
+// code/16, Q5 8*code, Q6 4*code); the factor is applied once per row at the end.
+template <> struct Fmt<4> { static constexpr int NB = 4; static constexpr float kToCode = 16.0f; };
 template <> struct Fmt<5> { static constexpr int NB = 5; static constexpr float kToCode = 0.125f; };
 template <> struct Fmt<6> { static constexpr int NB = 6; static constexpr float kToCode = 0.25f; };
 template <> struct Fmt<8> { static constexpr int NB = 8; static constexpr float kToCode = 1.0f; };
@@ -43,31 +43,15 @@ template <> struct Fmt<8> { static constexpr int NB = 8; static constexpr float 
 // ------------------------------------------------------------------ exact code conversion
 
 // sign-extended nibble in bits [3:0] of byte B of v, as a float equal to nibble / 16
-template <int B> __device__ __forceinline__ float nib_lo(uint32_t v);
-template <> __device__ __forceinline__ float nib_lo<0>(uint32_t v)
+// (v_cvt_off_f32_i4; the byte selection folds into its SDWA operand select).  Plain builtins,
+// no inline assembly: the compiler must see these instructions to keep the wait states the
+// matrix-core instructions around them need.
+template <int B> __device__ __forceinline__ float nib_lo(uint32_t v)
 {
-    return __builtin_amdgcn_cvt_off_f32_i4(v);
-}
-template <> __device__ __forceinline__ float nib_lo<1>(uint32_t v)
-{
-    float r;
-    asm volatile("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
-        : "=v"(r) : "v"(v));
-    return r;
-}
-template <> __device__ __forceinline__ float nib_lo<2>(uint32_t v)
-{
-    float r;
-    asm volatile("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
-        : "=v"(r) : "v"(v));
-    return r;
-}
-template <> __device__ __forceinline__ float nib_lo<3>(uint32_t v)
-{
-    float r;
-    asm volatile("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
-        : "=v"(r) : "v"(v));
-    return r;
+    if constexpr (B == 0) return __builtin_amdgcn_cvt_off_f32_i4(v);
+    else if constexpr (B == 1) return __builtin_amdgcn_cvt_off_f32_i4((v >> 8) & 0xFFu);
+    else if constexpr (B == 2) return __builtin_amdgcn_cvt_off_f32_i4(v >> 16);
+    else return __builtin_amdgcn_cvt_off_f32_i4(v >> 24);
 }
 
 // byte B of v as a signed integer, converted to float (SDWA sign-extending convert)
@@ -92,14 +76,15 @@ template <int FMT, int KA, int MM>
 __device__ __forceinline__ void codes8(const uint32_t *W, float (&f)[8])
 {
     if constexpr (FMT == 4) {
-        // nibble e = 2i sits in bits [3:0] of byte i, e = 2i+1 in bits [7:4]; moved to the top
-        // of each byte they read as signed bytes worth 16 * code
-        const uint32_t n = W[4 * KA + MM];
-        const uint32_t lo = (n << 4) & 0xF0F0F0F0u, hi = n & 0xF0F0F0F0u;
-        f[0] = sbyte<0>(lo); f[1] = sbyte<0>(hi);
-        f[2] = sbyte<1>(lo); f[3] = sbyte<1>(hi);
-        f[4] = sbyte<2>(lo); f[5] = sbyte<2>(hi);
-        f[6] = sbyte<3>(lo); f[7] = sbyte<3>(hi);
+        // nibble e = 2i sits in bits [3:0] of byte i, e = 2i+1 in bits [7:4]; v_cvt_off_f32_i4
+        // reads the low four bits of the byte SDWA selects as code/16, so the odd nibbles take
+        // one rotate (a rotate rather than a shift keeps h opaque to the compiler, so its bytes
+        // are SDWA-selected too instead of being re-extracted from n)
+        const uint32_t n = W[4 * KA + MM], h = __builtin_amdgcn_alignbit(n, n, 4);
+        f[0] = nib_lo<0>(n); f[1] = nib_lo<0>(h);
+        f[2] = nib_lo<1>(n); f[3] = nib_lo<1>(h);
+        f[4] = nib_lo<2>(n); f[5] = nib_lo<2>(h);
+        f[6] = nib_lo<3>(n); f[7] = nib_lo<3>(h);
     } else {
         uint32_t o[2];
         if constexpr (FMT == 5) {
@@ -284,22 +269,31 @@ template <int NB, int XN> struct Unit {
 // the activations (reused by every row tile) in the caches.
 __device__ __forceinline__ u32x4_t stream_load(const u32x4_t *p) { return __builtin_nontemporal_load(p); }
 
+// Every address below is a wave-uniform base (tile, unit, k step: scalar registers) plus a
+// per-lane byte offset that is fixed for the whole kernel, so the loads need no vector address
+// arithmetic in the loop.
 template <int FMT, int NB, int XN>
-__device__ __forceinline__ void load_weights(const RunArgs &a, int tile, int u, int lane, Unit<NB, XN> &r)
+__device__ __forceinline__ void load_weights(const RunArgs &a, int tile, int u, uint32_t lane, Unit<NB, XN> &r)
 {
-    const u32x4_t *cp = reinterpret_cast<const u32x4_t *>(a.codes) + (((int64_t)tile * a.NU + u) * NB) * 64 + lane;
+    const int64_t tu = (int64_t)tile * a.NU + u;
+    const char *cb = reinterpret_cast<const char *>(a.codes) + tu * (NB * kBlockBytes);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) r.c[j] = stream_load(cp + j * 64);
-    if constexpr (FMT != 8)
-        r.sc = stream_load(reinterpret_cast<const u32x4_t *>(a.scales) + ((int64_t)tile * a.NU + u) * 16 + (lane & 15));
+    for (int j = 0; j < NB; ++j)
+        r.c[j] = stream_load(reinterpret_cast<const u32x4_t *>(cb + j * kBlockBytes + 16u * lane));
+    if constexpr (FMT != 8) {
+        const char *sb = reinterpret_cast<const char *>(a.scales) + tu * kScaleBlockBytes;
+        r.sc = stream_load(reinterpret_cast<const u32x4_t *>(sb + 16u * (lane & 15)));
+    }
 }
 
-// 8 bf16 activations (one k octet) of token t at column k, clamped inside the row: the
-// clamped columns only meet zero codes of padding groups.
-__device__ __forceinline__ u32x4_t load_x8(const RunArgs &a, int t, int k)
+// 8 bf16 activations for the 32-wide k step starting at column kb (wave-uniform); lane_off is
+// the lane's byte offset (token row and k octet).  The step is clamped inside the row: only
+// the half unit of a K = 64 (mod 128) matrix is clamped, and its clamped steps meet the zero
+// codes of a padding group.
+__device__ __forceinline__ u32x4_t load_x8(const RunArgs &a, int kb, uint32_t lane_off)
 {
-    const int kk = k < a.K - 8 ? k : a.K - 8;
-    return *reinterpret_cast<const u32x4_t *>(a.x + (int64_t)t * a.K + kk);
+    const int kc = kb < a.K - 32 ? kb : a.K - 32;
+    return *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const char *>(a.x) + 2 * (int64_t)kc + lane_off);
 }
 
 // Software pipeline over a wave's units [u0, u1): a ring of D units in flight; a slot is
@@ -404,13 +398,16 @@ __global__ __launch_bounds__(512) void valu_kernel(RunArgs a)
     constexpr int NB = Fmt<FMT>::NB, XN = 4 * TT;
     extern __shared__ float red[];
     const Slice s = make_slice(a);
-    const int lane = threadIdx.x & 63, q = lane >> 4;
+    const uint32_t lane = threadIdx.x & 63, q = lane >> 4;
     float acc[4][TT];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[m][t] = 0.f;
 
+    uint32_t xoff[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) xoff[t] = 2u * (uint32_t)(t * a.K) + 16u * q;
     Unit<NB, XN> buf[D];
     pipeline<D>(s.u0, s.u1, buf,
         [&](Unit<NB, XN> &r, int u) {
@@ -418,7 +415,7 @@ __global__ __launch_bounds__(512) void valu_kernel(RunArgs a)
 #pragma unroll
             for (int t = 0; t < TT; ++t)
 #pragma unroll
-                for (int ka = 0; ka < 4; ++ka) r.x[4 * t + ka] = load_x8(a, t, u * kUnitK + 32 * ka + 8 * q);
+                for (int ka = 0; ka < 4; ++ka) r.x[4 * t + ka] = load_x8(a, u * kUnitK + 32 * ka, xoff[t]);
         },
         [&]() {},
         [&](const Unit<NB, XN> &U, int) {
@@ -473,16 +470,19 @@ __device__ __forceinline__ void mfma_step(const Unit<NB, XN> &U, f32x4_t (&D)[4]
 
 // A operand: 16 tokens x 32 k (lane l: token l % 16, k octet l / 16); B operand: 32 k x 16 rows
 // of the tile (lane l: row 16*m + l % 16, the same k octet) — exactly the packed layout.
-// D[m]: lane l holds tokens 4*(l/16) + r (r = 0..3) of row 16*m + l % 16.
-template <int FMT, int D_>
+// D[m]: lane l holds tokens 4*(l/16) + r (r = 0..3) of row 16*m + l % 16.  TR: how many of the
+// four r components can hold a real token (1 when T == 1: only token 0, in lanes 0..15).
+template <int FMT, int D_, int TR>
 __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
 {
     constexpr int NB = Fmt<FMT>::NB, XN = 4;
     extern __shared__ float red[];
     const Slice s = make_slice(a);
-    const int lane = threadIdx.x & 63, tok = lane & 15, oct = lane >> 4;
+    const uint32_t lane = threadIdx.x & 63;
+    const int tok = lane & 15, oct = lane >> 4;
     // A rows of tokens >= T only feed D rows that are never stored: load a valid token instead
     const int tok_c = tok < a.T ? tok : a.T - 1;
+    const uint32_t xoff = 2u * (uint32_t)(tok_c * a.K) + 16u * oct;
     f32x4_t acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
             load_weights<FMT>(a, s.tile, u, lane, r);
 #pragma unroll
             for (int ka = 0; ka < 4; ++ka)
-                r.x[ka] = load_x8(a, tok_c, u * kUnitK + 32 * ka + 8 * oct);
+                r.x[ka] = load_x8(a, u * kUnitK + 32 * ka, xoff);
         },
         [&]() {},
         [&](const Unit<NB, XN> &U, int) {
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
                     for (int m = 0; m < 4; ++m) {
                         const float sf = group_scale(U.sc, g, m);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[m][r] = fmaf(sf, P[m][r], acc[m][r]);
+                        for (int r = 0; r < TR; ++r) acc[m][r] = fmaf(sf, P[m][r], acc[m][r]);
                     }
                 }
             }
@@ -528,13 +528,15 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
     f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
     if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)s.tile * 16 + (lane & 15)];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc[m] *= rs[m];
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < TR; ++r) acc[m][r] *= rs[m];
     const int t0 = 4 * oct, rr = lane & 15;
     finish(a, s, red, [&](auto put) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < TR; ++r)
                 if (t0 + r < a.T) put(t0 + r, 16 * m + rr, acc[m][r]);
     });
 }
@@ -558,11 +560,15 @@ __device__ __forceinline__ void dequant_step(const DequantArgs &a, const uint32_
             out[2 * i + 1] = rs[MM] * __builtin_bit_cast(float, b[i] & 0xFFFF0000u);
         }
     } else {
-        float f[8];
-        codes8<FMT, KA, MM>(W, f);
+        // the exact bf16 operands both routes feed to their products, decoded back to the code
+        uint32_t b[4];
+        bf16x8_of<FMT, KA, MM>(W, b);
         const float sc_f = group_scale(sc, KA >> 1, MM);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = sc_f * (f[i] * Fmt<FMT>::kToCode);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t hb = (i & 1) ? (b[i >> 1] & 0xFFFF0000u) : (b[i >> 1] << 16);
+            out[i] = sc_f * (__builtin_bit_cast(float, hb) * Fmt<FMT>::kToCode);
+        }
     }
     float *dst = a.w + (int64_t)row * a.K + k;
     reinterpret_cast<f32x4_t *>(dst)[0] = (f32x4_t){out[0], out[1], out[2], out[3]};
@@ -599,7 +605,9 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a)
 
 template <int FMT, int D> static const void *run_kernel_d(int route, int T)
 {
-    if (route == kRouteMfma) return reinterpret_cast<const void *>(&mfma_kernel<FMT, D>);
+    if (route == kRouteMfma)
+        return T == 1 ? reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 1>)
+                      : reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 4>);
     switch (T) {
     case 1: return reinterpret_cast<const void *>(&valu_kernel<FMT, 1, D>);
     case 2: return reinterpret_cast<const void *>(&valu_kernel<FMT, 2, D>);
@@ -614,7 +622,6 @@ template <int FMT> static const void *run_kernel(int route, int T, int depth)
     switch (depth) {
     case 1: return run_kernel_d<FMT, 1>(route, T);
     case 2: return run_kernel_d<FMT, 2>(route, T);
-    case 3: return run_kernel_d<FMT, 3>(route, T);
     default: return nullptr;
     }
 }
