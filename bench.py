@@ -145,8 +145,10 @@ def measured_traffic(workload):
 
 def plan_str(res, T):
     import weight_only_quant_amd as wq
-    r, d, w, sp = wq.qmat_get_plan(res.handles[0], T)
-    return f"{'valu' if r == wq.QMAT_ROUTE_VALU else 'mfma'} depth={d} waves={w} splits={sp}"
+    p = wq.qmat_get_plan(res.handles[0], T)
+    tail = f" tail_tiles={p.tail_tiles} tail_splits={p.tail_splits}" if p.tail_tiles else ""
+    return (f"{'valu' if p.route == wq.QMAT_ROUTE_VALU else 'mfma'} depth={p.depth} waves={p.waves} "
+            f"splits={p.splits}{tail}")
 
 
 EAGER_ONLY = False

@@ -100,22 +100,45 @@ int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packe
  * QMAT_EHIP (launch failure). */
 int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream);
 
-/* qmat_run with an explicit kernel route and launch shape, for tests and tuning.
+/* A launch shape of the product kernel.  The matrix is cut into NT = ceil(M/64) row tiles;
+ * a workgroup of `waves` waves works on one tile and splits the tile's 128-wide k units among
+ * its waves.  The leading NT - tail_tiles tiles are each shared by `splits` workgroups along K,
+ * the trailing tail_tiles tiles by `tail_splits` workgroups (a way to spread a few leftover
+ * tiles over the whole GPU when NT is not a multiple of the compute-unit count).  Tiles shared
+ * by several workgroups are summed through the handle's workspace in a fixed order, so every
+ * plan gives the same y for the same inputs run after run (different plans may differ in the
+ * last bits: the summation order differs). */
+typedef struct {
+    int route;       /* QMAT_ROUTE_VALU or QMAT_ROUTE_MFMA */
+    int depth;       /* 128-wide k units each wave keeps in flight: 1 or 2 */
+    int waves;       /* waves per workgroup: 1, 2, 4 or 8 */
+    int splits;      /* workgroups per leading tile: >= 1 */
+    int tail_tiles;  /* trailing tiles using tail_splits: 0 .. ceil(M/64) */
+    int tail_splits; /* workgroups per trailing tile: >= 1 (not read when tail_tiles == 0) */
+} qmat_plan;
+
+/* qmat_run with the automatic plan for (route, T) changed by the nonzero arguments, for tests
+ * and tuning.
  *   route:  qmat_route.
- *   depth:  128-wide k units each wave keeps in flight (1 or 2; 0 = auto).
- *   waves:  waves per workgroup splitting K inside one workgroup (1, 2, 4 or 8; 0 = auto).
- *   splits: workgroups splitting K across the grid (>= 1; 0 = auto); the partial sums go
- *           through the handle's workspace and are added in a fixed order.
- * Errors: as qmat_run, plus QMAT_EINVAL (route, depth, waves) and QMAT_ESIZE (splits * T * rows
- * exceeds the workspace reserved at create time, or more splits than k units). */
+ *   depth:  replaces plan.depth (0 = keep).
+ *   waves:  replaces plan.waves (0 = keep).
+ *   splits: replaces plan.splits and removes the trailing-tile split, so every tile is shared
+ *           by `splits` workgroups (0 = keep the automatic plan's splits and tail).
+ * Errors: as qmat_run, plus QMAT_EINVAL (route, depth, waves) and QMAT_ESIZE (the splits at
+ * this T need more workspace than was reserved at create time). */
 int qmat_run_ex(qmat_t handle, const void *x_dev, float *y_dev, int T, int route, int depth,
                 int waves, int splits, void *stream);
 
-/* The launch qmat_run would make for T tokens on a route (QMAT_ROUTE_AUTO: the library's
- * choice): the route taken, units in flight per wave, waves per workgroup and k splits across
- * workgroups.  Host only.
+/* qmat_run with an explicit launch shape (all fields read as documented on qmat_plan).
+ * Errors: as qmat_run, plus QMAT_EINVAL (null plan, a field outside its range) and QMAT_ESIZE
+ * (more splits than the handle's workspace holds at this T, or a grid beyond 2^31-1). */
+int qmat_run_plan(qmat_t handle, const void *x_dev, float *y_dev, int T, const qmat_plan *plan,
+                  void *stream);
+
+/* The plan qmat_run (route QMAT_ROUTE_AUTO) or qmat_run_ex with only a route would use for T
+ * tokens; plan->route is the route taken.  Host only.
  * Errors: QMAT_EINVAL (null argument, bad route), QMAT_ESHAPE (T outside [1, 16]). */
-int qmat_get_plan(qmat_t handle, int T, int route, int *route_out, int *depth, int *waves, int *splits);
+int qmat_get_plan(qmat_t handle, int T, int route, qmat_plan *plan);
 
 /* Expand the packed matrix to fp32 w [M][K] (device), bit-exact: groupwise
  * fp32(scale) * code, FP8 fl32(r * e4m3).  For checking; not a fast path. */

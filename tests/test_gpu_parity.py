@@ -148,6 +148,49 @@ def test_run_split_shapes_agree(fmt, route, T):
                 _check_y(y1, wl, f"{route} T={T} depth={depth} waves={waves} splits={splits}")
 
 
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("route,T", [("valu", 1), ("valu", 3), ("mfma", 1), ("mfma", 6), ("mfma", 16)])
+def test_run_tail_plans(fmt, route, T):
+    # plans whose trailing tiles are shared by a different number of workgroups than the
+    # leading ones (tail_tiles from 1 to all tiles, tail splits 1..8, leading splits 1..3):
+    # in tolerance, and deterministic (two calls, same bits)
+    M, K = 455, 1472   # 8 tiles, the last one ragged; 12 k units, the last a half unit
+    wl = _workload(fmt, M, K, T, 31 + fmt + T)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    for depth, waves, splits, tail_tiles, tail_splits in [
+            (1, 8, 1, 1, 8), (2, 4, 1, 3, 2), (2, 4, 2, 2, 5), (1, 2, 3, 8, 4), (2, 1, 1, 7, 3),
+            (1, 4, 1, 5, 1), (2, 8, 2, 1, 1), (1, 1, 1, 8, 8)]:
+        plan = wq.qmat_plan(ROUTES[route], depth, waves, splits, tail_tiles, tail_splits)
+        label = f"tail {route} fmt={fmt} T={T} plan={plan.as_tuple()}"
+        say(label)
+        y1 = torch.full((T, M), float("nan"), device="cuda")
+        y2 = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run_plan(qm.handle, xd, y1, plan, T=T)
+        wq.qmat_run_plan(qm.handle, xd, y2, plan, T=T)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), label
+        _check_y(y1, wl, label)
+
+
+def test_run_plan_rejects_bad_fields():
+    say("run_plan errors")
+    wl = _workload(4, 130, 256, 1, 5)
+    qm = wq.QMat(4, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    y = torch.empty((1, 130), device="cuda")
+    NT = 3
+    bad = [(0, 1, 4, 1, 0, 1), (2, 3, 4, 1, 0, 1), (2, 1, 3, 1, 0, 1), (2, 1, 4, 0, 0, 1),
+           (2, 1, 4, 1, NT + 1, 1), (2, 1, 4, 1, -1, 1), (2, 1, 4, 1, 1, 0)]
+    for fields in bad:
+        with pytest.raises(wq.QmatError) as e:
+            wq.qmat_run_plan(qm.handle, xd, y, wq.qmat_plan(*fields), T=1)
+        assert e.value.status == wq.QMAT_EINVAL, fields
+    with pytest.raises(wq.QmatError) as e:  # more splits than the workspace holds
+        wq.qmat_run_plan(qm.handle, xd, y, wq.qmat_plan(2, 1, 1, 1, 2, 64 * 2), T=16)
+    assert e.value.status == wq.QMAT_ESIZE
+
+
 def _exact_workload(fmt, M, K, T, seed):
     """Inputs whose products and partial sums are all exact in fp32: small integer bf16
     activations and power-of-two scales (FP8: integer-valued E4M3 bytes)."""

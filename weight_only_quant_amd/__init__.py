@@ -32,7 +32,8 @@ SIGNATURES = {
     "qmat_run": (_int, [_vp, _vp, _vp, _int, _vp]),
     "qmat_run_ex": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]),
     "qmat_dequant": (_int, [_vp, _vp, _vp]),
-    "qmat_get_plan": (_int, [_vp, _int, _int] + [ctypes.POINTER(_int)] * 4),
+    "qmat_run_plan": (_int, [_vp, _vp, _vp, _int, _vp, _vp]),
+    "qmat_get_plan": (_int, [_vp, _int, _int, _vp]),
     "qmat_workspace_bytes": (_sz, [_vp]),
     "qmat_destroy": (None, [_vp]),
     "qmat_last_error": (ctypes.c_char_p, []),
@@ -130,11 +131,26 @@ def qmat_dequant(handle: int, w, stream=None) -> None:
     _check(lib().qmat_dequant(handle, w.data_ptr(), _stream_handle(stream)))
 
 
-def qmat_get_plan(handle: int, T: int, route: int = QMAT_ROUTE_AUTO):
-    """(route, depth, waves, splits) of the launch qmat_run makes for T tokens."""
-    r, d, w, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(lib().qmat_get_plan(handle, T, route, ctypes.byref(r), ctypes.byref(d), ctypes.byref(w), ctypes.byref(s)))
-    return r.value, d.value, w.value, s.value
+class qmat_plan(ctypes.Structure):
+    """The C struct qmat_plan (launch shape of the product kernel)."""
+    _fields_ = [("route", _int), ("depth", _int), ("waves", _int), ("splits", _int),
+                ("tail_tiles", _int), ("tail_splits", _int)]
+
+    def as_tuple(self):
+        return (self.route, self.depth, self.waves, self.splits, self.tail_tiles, self.tail_splits)
+
+
+def qmat_get_plan(handle: int, T: int, route: int = QMAT_ROUTE_AUTO) -> qmat_plan:
+    """The qmat_plan qmat_run would use for T tokens on a route."""
+    p = qmat_plan()
+    _check(lib().qmat_get_plan(handle, T, route, ctypes.byref(p)))
+    return p
+
+
+def qmat_run_plan(handle: int, x, y, plan: qmat_plan, T: Optional[int] = None, stream=None) -> None:
+    """qmat_run with an explicit qmat_plan."""
+    T = x.shape[0] if T is None else T
+    _check(lib().qmat_run_plan(handle, x.data_ptr(), y.data_ptr(), T, ctypes.byref(plan), _stream_handle(stream)))
 
 
 def qmat_workspace_bytes(handle: int) -> int:

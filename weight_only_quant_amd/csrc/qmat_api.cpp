@@ -146,31 +146,55 @@ void pack_tile(const PackSrc &p, int64_t tile, uint8_t *out)
 // ------------------------------------------------------------------ planning
 
 struct Plan {
-    int route, depth, waves, splits;
+    int route, depth, waves, splits, tail_tiles, tail_splits;
 };
 
 
 // Launch shape for one (route, tokens-per-launch), from graph-timed sweeps of depth x waves x
-// splits over the benchmark shapes on MI355X (within 3% of the best measured shape on each).
+// splits x trailing-tile splits over the benchmark shapes on MI355X.
 //
-// MFMA kernel.  Matrices of at least 2048 row tiles: one tile per workgroup, never split; 4
-// waves share a tile's k units at T = 1 (a single token leaves registers for two units in
-// flight), 1 wave otherwise.  Narrower matrices: 4 waves per workgroup up to T = 4, 8 beyond,
-// and tiles split along K across workgroups until about 8 waves per compute unit exist, at
-// most 3 ways (every split adds a round of partial-sum traffic and a last-arrival reduction at
-// the end of the kernel; 4 and more splits measured slower on every shape).  Two units in
-// flight per wave, except with 8-wave workgroups at T > 1, whose register footprint would
-// leave room for only one workgroup per compute unit.
+// MFMA kernel.
+//  - Matrices of at least 2048 row tiles: one tile per workgroup, never split; 4 waves share a
+//    tile's k units at T = 1 (a single token leaves registers for two units in flight), 1 wave
+//    otherwise.
+//  - At least one tile per compute unit: 4 waves per workgroup, two units in flight at T = 1 and
+//    one above (the multi-token accumulators would otherwise halve the resident waves).  When
+//    the tile count is not a multiple of the compute-unit count, the leftover tiles would form a
+//    second, nearly empty round of workgroups on a few compute units (measured: 34816 rows take
+//    4 us longer than 32768).  Those trailing tiles are instead split along K over up to 8
+//    workgroups each, enough to give every compute unit a share, and dispatched first; the whole
+//    grid stays within one round of resident workgroups.
+//  - Fewer tiles than compute units: 4 waves per workgroup up to T = 4, 8 beyond, and every tile
+//    split along K across workgroups until about 8 waves per compute unit exist, at most 3 ways
+//    (every split adds a round of partial-sum traffic and a last-arrival reduction at the end of
+//    the kernel; 4 and more splits measured slower on every shape).  Two units in flight per
+//    wave, except with 8-wave workgroups at T > 1, whose register footprint would leave room
+//    for only one workgroup per compute unit.
 //
 // Vector-ALU kernel (explicit requests only): two units in flight, 4 waves per workgroup,
 // single-wave workgroups for wide matrices, splits up to about 4 waves per compute unit.
 Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
 {
-    (void)fmt;
     if (route == kRouteMfma) {
-        Plan p{route, 2, 1, 1};
+        Plan p{route, 2, 1, 1, 0, 1};
         if (NT >= 2048) {
             p.waves = Tl == 1 ? 4 : 1;
+        } else if (NT >= cus) {
+            p.waves = 4;
+            p.depth = Tl == 1 ? 2 : 1;
+            while (p.waves > 1 && NU < (int64_t)p.waves) p.waves /= 2;
+            const int64_t rem = NT % cus;
+            if (rem > 0) {
+                const int64_t resident = (int64_t)run_blocks_per_cu(fmt, kRouteMfma, p.depth, Tl, p.waves, (int)NU, 1) * cus;
+                int64_t st = cus / rem;
+                if (st > 8) st = 8;
+                if (st > NU) st = NU;
+                while (st > 1 && (NT - rem) + rem * st > resident) --st;
+                if (st > 1) {
+                    p.tail_tiles = (int)rem;
+                    p.tail_splits = (int)st;
+                }
+            }
         } else {
             p.waves = Tl <= 4 ? 4 : 8;
             const int64_t target_waves = 8LL * cus;
@@ -179,12 +203,12 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
             if (splits > NU / p.waves) splits = NU / p.waves;
             if (splits < 1) splits = 1;
             p.splits = (int)splits;
+            while (p.waves > 1 && NU < (int64_t)p.waves * p.splits) p.waves /= 2;
+            if (Tl > 1 && p.waves == 8) p.depth = 1;
         }
-        while (p.waves > 1 && NU < (int64_t)p.waves * p.splits) p.waves /= 2;
-        if (Tl > 1 && p.waves == 8) p.depth = 1;
         return p;
     }
-    Plan p{route, 2, NT >= 2048 ? 1 : 4, 1};
+    Plan p{route, 2, NT >= 2048 ? 1 : 4, 1, 0, 1};
     while (p.waves > 1 && NU < 2 * p.waves) p.waves /= 2;
     const int64_t target_waves = 4LL * cus;
     int64_t splits = (target_waves + (NT * p.waves) / 2) / (NT * p.waves);  // rounded
@@ -330,12 +354,10 @@ int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packe
             const int Tl = launch_tokens(r, T);
             const Plan p = make_plan(fmt, r, Tl, h->NT, h->NU, h->cus);
             h->plan[r - 1][T] = p;
-            if (p.splits > 1) {
-                const size_t f = (size_t)p.splits * Tl * (size_t)h->Mpad;
-                if (f > need_ws) need_ws = f;
-            }
+            const size_t f = run_workspace_floats(Tl, (int)h->NT, p.splits, p.tail_tiles, p.tail_splits);
+            if (f > need_ws) need_ws = f;
         }
-    if (h->Mpad <= 65536 && need_ws < (size_t)8 * kMaxT * h->Mpad) need_ws = (size_t)8 * kMaxT * h->Mpad;
+    if (h->Mpad <= 4096 && need_ws < (size_t)8 * kMaxT * h->Mpad) need_ws = (size_t)8 * kMaxT * h->Mpad;
     if (need_ws > 0) {
         h->ws_floats = need_ws;
         if (hipMalloc(&h->ws, h->ws_floats * sizeof(float)) != hipSuccess) {
@@ -361,29 +383,32 @@ int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packe
     return ok();
 }
 
-int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int depth, int waves, int splits,
-                void *stream)
+namespace {
+
+int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, void *stream)
 {
-    if (!h) return fail(QMAT_EINVAL, "qmat_run: null handle");
     if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d]", T, kMaxT);
     if (T == 0) return ok();
     if (!x_dev || !y_dev) return fail(QMAT_EINVAL, "qmat_run: null x or y");
     if (reinterpret_cast<uintptr_t>(x_dev) % 16) return fail(QMAT_EINVAL, "qmat_run: x not 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_run: y not 4-byte aligned");
-    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA) return fail(QMAT_EINVAL, "qmat_run: bad route %d", route);
-    if (!(waves == 0 || waves == 1 || waves == 2 || waves == 4 || waves == 8))
-        return fail(QMAT_EINVAL, "qmat_run: waves must be 0, 1, 2, 4 or 8");
-    if (splits < 0) return fail(QMAT_EINVAL, "qmat_run: splits must be >= 0");
-    if (depth < 0 || depth > kMaxDepth) return fail(QMAT_EINVAL, "qmat_run: depth must be 0..%d", kMaxDepth);
-    const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
-    Plan p = h->plan[r - 1][T];
-    if (depth) p.depth = depth;
-    if (waves) p.waves = waves;
-    if (splits) p.splits = splits;
-    if ((int64_t)p.splits * p.waves > h->NU * 64) return fail(QMAT_ESIZE, "qmat_run: too many splits");
+    if (p.route != kRouteValu && p.route != kRouteMfma) return fail(QMAT_EINVAL, "qmat_run: bad route");
+    if (!(p.waves == 1 || p.waves == 2 || p.waves == 4 || p.waves == 8))
+        return fail(QMAT_EINVAL, "qmat_run: waves must be 1, 2, 4 or 8");
+    if (p.depth < 1 || p.depth > kMaxDepth) return fail(QMAT_EINVAL, "qmat_run: depth must be 1..%d", kMaxDepth);
+    if (p.splits < 1) return fail(QMAT_EINVAL, "qmat_run: splits must be >= 1");
+    if (p.tail_tiles < 0 || p.tail_tiles > h->NT)
+        return fail(QMAT_EINVAL, "qmat_run: tail_tiles %d outside [0,%lld]", p.tail_tiles, (long long)h->NT);
+    const int tail_splits = p.tail_tiles > 0 ? p.tail_splits : 1;
+    if (tail_splits < 1) return fail(QMAT_EINVAL, "qmat_run: tail_splits must be >= 1");
+    if ((int64_t)p.splits * p.waves > h->NU * 64 || (int64_t)tail_splits * p.waves > h->NU * 64)
+        return fail(QMAT_ESIZE, "qmat_run: too many splits");
+    const int64_t grid = (int64_t)p.tail_tiles * tail_splits + (h->NT - p.tail_tiles) * (int64_t)p.splits;
+    if (grid > 0x7FFFFFFFLL) return fail(QMAT_ESIZE, "qmat_run: grid of %lld workgroups too large", (long long)grid);
     const int Tl = launch_tokens(p.route, T);
-    if (p.splits > 1 && (size_t)p.splits * Tl * (size_t)h->Mpad > h->ws_floats)
-        return fail(QMAT_ESIZE, "qmat_run: %d splits at %d tokens exceed the workspace", p.splits, Tl);
+    if (run_workspace_floats(Tl, (int)h->NT, p.splits, p.tail_tiles, tail_splits) > h->ws_floats)
+        return fail(QMAT_ESIZE, "qmat_run: splits %d / tail %d x %d at %d tokens exceed the workspace", p.splits,
+                    p.tail_tiles, tail_splits, Tl);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const uint16_t *x = static_cast<const uint16_t *>(x_dev);
     const uint8_t *codes = h->packed;
@@ -403,24 +428,63 @@ int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int
         a.NT = (int)h->NT;
         a.NU = (int)h->NU;
         a.S = p.splits;
-        a.Mpad = (int)h->Mpad;
+        a.NTt = p.tail_tiles;
+        a.St = tail_splits;
         const hipError_t e = launch_run(h->fmt, p.route, p.depth, a, p.waves, st);
         if (e != hipSuccess) return fail(QMAT_EHIP, "qmat_run: launch failed: %s", hipGetErrorString(e));
     }
     return ok();
 }
 
-int qmat_get_plan(qmat_t h, int T, int route, int *route_out, int *depth, int *waves, int *splits)
+}  // namespace
+
+int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int depth, int waves, int splits,
+                void *stream)
 {
-    if (!h || !route_out || !depth || !waves || !splits) return fail(QMAT_EINVAL, "qmat_get_plan: null argument");
+    if (!h) return fail(QMAT_EINVAL, "qmat_run: null handle");
+    if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d]", T, kMaxT);
+    if (T == 0) return ok();
+    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA) return fail(QMAT_EINVAL, "qmat_run: bad route %d", route);
+    if (!(waves == 0 || waves == 1 || waves == 2 || waves == 4 || waves == 8))
+        return fail(QMAT_EINVAL, "qmat_run: waves must be 0, 1, 2, 4 or 8");
+    if (splits < 0) return fail(QMAT_EINVAL, "qmat_run: splits must be >= 0");
+    if (depth < 0 || depth > kMaxDepth) return fail(QMAT_EINVAL, "qmat_run: depth must be 0..%d", kMaxDepth);
+    const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
+    Plan p = h->plan[r - 1][T];
+    if (depth) p.depth = depth;
+    if (waves) p.waves = waves;
+    if (splits) {
+        p.splits = splits;
+        p.tail_tiles = 0;
+        p.tail_splits = 1;
+    }
+    return run_plan(h, x_dev, y_dev, T, p, stream);
+}
+
+int qmat_run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const qmat_plan *plan, void *stream)
+{
+    if (!h) return fail(QMAT_EINVAL, "qmat_run_plan: null handle");
+    if (!plan) return fail(QMAT_EINVAL, "qmat_run_plan: null plan");
+    if (plan->route != QMAT_ROUTE_VALU && plan->route != QMAT_ROUTE_MFMA)
+        return fail(QMAT_EINVAL, "qmat_run_plan: route must be QMAT_ROUTE_VALU or QMAT_ROUTE_MFMA");
+    const Plan p{plan->route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma, plan->depth, plan->waves, plan->splits,
+                 plan->tail_tiles, plan->tail_splits};
+    return run_plan(h, x_dev, y_dev, T, p, stream);
+}
+
+int qmat_get_plan(qmat_t h, int T, int route, qmat_plan *plan)
+{
+    if (!h || !plan) return fail(QMAT_EINVAL, "qmat_get_plan: null argument");
     if (T < 1 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kMaxT);
     if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA) return fail(QMAT_EINVAL, "qmat_get_plan: bad route %d", route);
     const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
     const Plan &p = h->plan[r - 1][T];
-    *route_out = r == kRouteValu ? QMAT_ROUTE_VALU : QMAT_ROUTE_MFMA;
-    *depth = p.depth;
-    *waves = p.waves;
-    *splits = p.splits;
+    plan->route = r == kRouteValu ? QMAT_ROUTE_VALU : QMAT_ROUTE_MFMA;
+    plan->depth = p.depth;
+    plan->waves = p.waves;
+    plan->splits = p.splits;
+    plan->tail_tiles = p.tail_tiles;
+    plan->tail_splits = p.tail_tiles > 0 ? p.tail_splits : 1;
     return ok();
 }
 

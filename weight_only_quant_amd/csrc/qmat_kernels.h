@@ -7,17 +7,30 @@
 
 namespace qmatk {
 
+// Workspace floats one launch needs (0 when no tile is shared by several workgroups).
+inline size_t run_workspace_floats(int T, int NT, int S, int NTt, int St)
+{
+    size_t f = 0;
+    if (S > 1) f += (size_t)S * T * (size_t)(NT - NTt) * 64;
+    if (NTt > 0 && St > 1) f += (size_t)St * T * (size_t)NTt * 64;
+    return f;
+}
+
 // One launch of the product kernel: tokens [0, T) of x/y as passed (the caller offsets x and y
-// for multi-pass launches), all rows, the k units split over S workgroups x NW waves per tile.
+// for multi-pass launches), all rows.  The leading NT - NTt row tiles have their k units split
+// over S workgroups x NW waves each; the trailing NTt tiles over St workgroups x NW waves.  The
+// grid is NTt * St + (NT - NTt) * S workgroups, the trailing tiles' workgroups first.
 struct RunArgs {
     const uint8_t *codes;   // packed code blocks
     const uint8_t *scales;  // packed scale blocks
     const uint16_t *x;      // bf16 [T][K]
     float *y;               // fp32 [T][ldy]
-    float *ws;              // split-K partials [S][T][Mpad] (S > 1 only)
+    float *ws;              // split-K partials: leading tiles [S][T][(NT-NTt)*64] when S > 1,
+                            // then trailing tiles [St][T][NTt*64] when St > 1
     uint32_t *counters;     // one arrival counter per tile (S > 1 only), zero between launches
     int64_t ldy;            // row stride of y in elements (M)
-    int M, K, T, NT, NU, S, Mpad;
+    int M, K, T, NT, NU, S;
+    int NTt, St;            // trailing tiles and their k splits (NTt == 0: every tile uses S)
 };
 
 struct DequantArgs {

@@ -163,17 +163,38 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 // ------------------------------------------------------------------ split bookkeeping
 
 struct Slice {
-    int tile, sp, w, nw, u0, u1;
+    int tile, sp, S, w, nw, u0, u1;
+    int wsrow, wsld;  // the tile's first row and the row count of its workspace region
+    int64_t wsoff;    // start of that region in the workspace (floats)
 };
 
+// Workgroup -> (tile, split, splits of that tile).  The trailing NTt tiles come first in the grid
+// so that their shared-tile reductions finish while the other tiles are still streaming.
 __device__ __forceinline__ Slice make_slice(const RunArgs &a)
 {
     Slice s;
     s.nw = blockDim.x >> 6;
     s.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
-    s.tile = blockIdx.x / a.S;
-    s.sp = blockIdx.x - s.tile * a.S;
-    const int nsl = a.S * s.nw, sl = s.sp * s.nw + s.w;
+    const int b = blockIdx.x, ntail = a.NTt * a.St;
+    const int nlead = a.NT - a.NTt;
+    if (b < ntail) {
+        const int tt = b / a.St;
+        s.tile = nlead + tt;
+        s.sp = b - tt * a.St;
+        s.S = a.St;
+        s.wsrow = tt * kTileRows;
+        s.wsld = a.NTt * kTileRows;
+        s.wsoff = a.S > 1 ? (int64_t)a.S * a.T * nlead * kTileRows : 0;
+    } else {
+        const int c = b - ntail;
+        s.tile = c / a.S;
+        s.sp = c - s.tile * a.S;
+        s.S = a.S;
+        s.wsrow = s.tile * kTileRows;
+        s.wsld = nlead * kTileRows;
+        s.wsoff = 0;
+    }
+    const int nsl = s.S * s.nw, sl = s.sp * s.nw + s.w;
     s.u0 = (int)(((int64_t)a.NU * sl) / nsl);
     s.u1 = (int)(((int64_t)a.NU * (sl + 1)) / nsl);
     return s;
@@ -186,7 +207,7 @@ template <typename ForEach>
 __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *red, ForEach for_each)
 {
     const int row0 = s.tile * kTileRows;
-    if (s.nw == 1 && a.S == 1) {
+    if (s.nw == 1 && s.S == 1) {
         for_each([&](int t, int r, float v) {
             if (row0 + r < a.M) a.y[(int64_t)t * a.ldy + row0 + r] = v;
         });
@@ -198,7 +219,7 @@ __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *
         __syncthreads();
     }
     const int nthr = blockDim.x;
-    if (a.S == 1) {
+    if (s.S == 1) {
         for (int e = threadIdx.x; e < n; e += nthr) {
             float v = red[e];
             for (int w = 1; w < s.nw; ++w) v += red[w * n + e];
@@ -214,10 +235,11 @@ __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *
     // S workgroups to arrive reads the S partials with agent-scope atomic loads and adds them
     // in split order (deterministic).  No cache-wide fences, no memset: the last block resets
     // the counter for the next call.
-    float *wsp = a.ws + (int64_t)s.sp * a.T * a.Mpad;
+    float *wsr = a.ws + s.wsoff + s.wsrow;
+    float *wsp = wsr + (int64_t)s.sp * a.T * s.wsld;
     uint32_t sink = 0;
     auto publish = [&](int t, int r, float v) {
-        uint32_t *p = reinterpret_cast<uint32_t *>(wsp + (int64_t)t * a.Mpad + row0 + r);
+        uint32_t *p = reinterpret_cast<uint32_t *>(wsp + (int64_t)t * s.wsld + r);
         sink |= __hip_atomic_exchange(p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     if (s.nw > 1) {
@@ -236,17 +258,17 @@ __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *
     if (threadIdx.x == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s.tile], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        last = (prev == (uint32_t)(a.S - 1));
+        last = (prev == (uint32_t)(s.S - 1));
     }
     __syncthreads();
     if (!last) return;
     for (int e = threadIdx.x; e < n; e += nthr) {
         const int t = e / kTileRows, r = e - t * kTileRows;
         if (row0 + r >= a.M) continue;
-        uint32_t *p = reinterpret_cast<uint32_t *>(a.ws + (int64_t)t * a.Mpad + row0 + r);
+        uint32_t *p = reinterpret_cast<uint32_t *>(wsr + (int64_t)t * s.wsld + r);
         float v = __builtin_bit_cast(float, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        for (int sp = 1; sp < a.S; ++sp)
-            v += __builtin_bit_cast(float, __hip_atomic_load(p + (int64_t)sp * a.T * a.Mpad, __ATOMIC_RELAXED,
+        for (int sp = 1; sp < s.S; ++sp)
+            v += __builtin_bit_cast(float, __hip_atomic_load(p + (int64_t)sp * a.T * s.wsld, __ATOMIC_RELAXED,
                                                              __HIP_MEMORY_SCOPE_AGENT));
         a.y[(int64_t)t * a.ldy + row0 + r] = v;
     }
@@ -653,7 +675,8 @@ hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves
     if (!k) return hipErrorInvalidValue;
     RunArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(k, dim3((unsigned)(a.NT * a.S)), dim3((unsigned)(64 * waves)), args,
+    const int64_t grid = (int64_t)a.NTt * a.St + (int64_t)(a.NT - a.NTt) * a.S;
+    return hipLaunchKernel(k, dim3((unsigned)grid), dim3((unsigned)(64 * waves)), args,
                            run_lds_bytes(route, waves, a.T, a.NU, a.S), st);
 }
 
