@@ -13,7 +13,8 @@ Functions and the definitions they follow (NInfer model cards):
   double_to_half                                      binary16 round-to-nearest-even
   dequant_groupwise   "Qwen3.8-27B for NInfer on the RTX 3090" / "What is different
                       from the upstream artifact": weight = FP16 group scale x code,
-                      64-weight groups, negative scales allowed
+                      64-weight groups, negative scales allowed (4, 5, 6 or 8 bits;
+                      8-bit groupwise is the cards' Q8 head / projection format)
   dequant_fp8         "Qwen3.8-27B NVFP4 for NInfer" / "Artifact": row-scaled FP8
   gemv                y = x W^T in double, plus A = sum |w x|
   rtn_encode          the upstream round-to-nearest encoder (scale = absmax / qmax)
@@ -129,7 +130,8 @@ def dequant_fp8(bytes_: np.ndarray, row_scales: np.ndarray) -> np.ndarray:
 def gemv(fmt: int, codes: np.ndarray, scales: np.ndarray, x: np.ndarray,
          rows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
     """Returns (y, A), both float64 [T, nrows]: y = x W^T over the requested rows (all
-    rows if None), A = sum_j |w_ij x_tj|."""
+    rows if None), A = sum_j |w_ij x_tj|.  fmt: 4, 5, 6 groupwise with that many bits,
+    9 groupwise 8-bit, 8 row-scaled FP8."""
     if fmt == 8:
         codes = np.ascontiguousarray(codes, dtype=np.uint8)
         scales = np.ascontiguousarray(scales, dtype=np.float32)

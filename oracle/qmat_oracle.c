@@ -16,7 +16,10 @@
  *    along a row has one FP16 scale; a weight is scale times a two's-complement
  *    code; scales may be negative so that a group can use the most negative code
  *    (-8 for 4 bits, -16 for 5 bits).  The upstream encoder there picks
- *    scale = absmax / qmax and the nearest code.
+ *    scale = absmax / qmax and the nearest code.  The same cards store the token
+ *    embedding, the upstream output head and several projections as groupwise Q8
+ *    (the "Token embedding / output head" and "Attention ... projections" rows of
+ *    their format tables); here that is the same definition with 8-bit codes.
  *  - Row-scaled FP8 weights ("Qwen3.8-27B NVFP4 for NInfer", introduction and
  *    "Artifact"): one scale per matrix row times an FP8 value.  The FP8 variant
  *    is OCP E4M3 (finite-only, bias 7) and the row scale is an IEEE fp32 value.
@@ -120,7 +123,14 @@ static int code_in_range(int bits, int c)
     return c >= -(1 << (bits - 1)) && c <= (1 << (bits - 1)) - 1;
 }
 
-static int bits_ok(int bits) { return bits == 4 || bits == 5 || bits == 6; }
+static int bits_ok(int bits) { return bits == 4 || bits == 5 || bits == 6 || bits == 8; }
+
+/* Format ids of qo_gemv: 4, 5, 6 groupwise with that many bits; 9 groupwise 8-bit;
+ * 8 row-scaled FP8.  Returns the code width of a groupwise format, 0 otherwise. */
+static int group_bits(int fmt)
+{
+    return (fmt == 4 || fmt == 5 || fmt == 6) ? fmt : fmt == 9 ? 8 : 0;
+}
 
 /* ---------------------------------------------------------------- dequant */
 
@@ -163,7 +173,7 @@ int qo_dequant_fp8(int64_t M, int64_t K, const uint8_t *bytes, const float *r, f
 /* ---------------------------------------------------------------- product */
 
 typedef struct {
-    int fmt; /* 4, 5, 6 groupwise; 8 FP8 rows */
+    int fmt; /* 4, 5, 6, 9 groupwise; 8 FP8 rows */
     int64_t M, K, T;
     const void *codes;
     const void *scales;
@@ -210,8 +220,9 @@ static void *gemv_worker(void *arg)
         } else {
             const int8_t *c = (const int8_t *)jb->codes + i * K;
             const uint16_t *s = (const uint16_t *)jb->scales + i * G;
+            const int bits = group_bits(jb->fmt);
             for (int64_t j = 0; j < K; ++j) {
-                if (!code_in_range(jb->fmt, c[j])) {
+                if (!code_in_range(bits, c[j])) {
                     jb->status = QO_ERANGE;
                     goto done;
                 }
@@ -238,14 +249,15 @@ done:
 }
 
 /* y[t][n] = sum_j w[rows[n]][j] * x[t][j] and A[t][n] = sum_j |w x|, in double,
- * sequential over j.  fmt 4/5/6: codes int8 [M][K], scales binary16 [M][K/64];
- * fmt 8: codes E4M3 bytes [M][K], scales float [M].  x: bf16 bits [T][K].
- * rows == NULL means every row (nrows must equal M).  A may be NULL. */
+ * sequential over j.  fmt 4/5/6/9 (groupwise 4, 5, 6, 8 bits): codes int8 [M][K],
+ * scales binary16 [M][K/64]; fmt 8: codes E4M3 bytes [M][K], scales float [M].
+ * x: bf16 bits [T][K].  rows == NULL means every row (nrows must equal M).  A may be
+ * NULL. */
 int qo_gemv(int fmt, int64_t M, int64_t K, int64_t T, const void *codes, const void *scales,
             const uint16_t *x, const int64_t *rows, int64_t nrows, double *y, double *A,
             int nthreads)
 {
-    if (!(bits_ok(fmt) || fmt == 8) || M < 0 || K <= 0 || K % 64 || T < 0 || nrows < 0)
+    if (!(group_bits(fmt) || fmt == 8) || M < 0 || K <= 0 || K % 64 || T < 0 || nrows < 0)
         return QO_EINVAL;
     if (!rows && nrows != M)
         return QO_EINVAL;

@@ -24,14 +24,20 @@ import numpy as np
 import torch
 
 Q4, Q5, Q6, FP8 = 4, 5, 6, 8
+Q8 = 9          # groupwise 8-bit codes (the format id is not the bit width: 8 is FP8)
 GROUP = 64
+
+
+def code_bits(fmt: int) -> int:
+    """Bits per code of a groupwise format id (4, 5, 6 or Q8 -> 8); 0 for FP8."""
+    return {Q4: 4, Q5: 5, Q6: 6, Q8: 8}.get(fmt, 0)
 
 
 @dataclasses.dataclass
 class Workload:
     """One synthetic matrix plus activations.
 
-    fmt      4/5/6 for groupwise codes, 8 for row-scaled FP8 E4M3.
+    fmt      4/5/6 (and Q8 = 9) for groupwise codes, 8 for row-scaled FP8 E4M3.
     codes    int8 [M, K] two's complement codes (groupwise) or uint8 [M, K] E4M3 bytes (FP8).
     scales   uint16 [M, K/64] binary16 bit patterns (groupwise) or float32 [M] (FP8).
     x        uint16 [T, K] bfloat16 bit patterns.
@@ -50,7 +56,7 @@ class Workload:
         """Bytes of stored weight information per the format definition (codes + scales)."""
         if self.fmt == FP8:
             return self.M * self.K + 4 * self.M
-        return self.M * self.K * self.fmt // 8 + 2 * self.M * (self.K // GROUP)
+        return self.M * self.K * code_bits(self.fmt) // 8 + 2 * self.M * (self.K // GROUP)
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -86,14 +92,18 @@ def draw_activations(gen: torch.Generator, T: int, K: int) -> np.ndarray:
     return x.view(torch.int16).numpy().view(np.uint16)
 
 
-def groupwise(name: str, bits: int, M: int, K: int, T: int, scale_mult: float, seed: int = 0) -> Workload:
+def groupwise(name: str, fmt: int, M: int, K: int, T: int, scale_mult: float, seed: int = 0) -> Workload:
+    """fmt: Q4, Q5, Q6 or Q8."""
     if K % GROUP:
         raise ValueError("K must be a multiple of 64")
+    bits = code_bits(fmt)
+    if not bits:
+        raise ValueError(f"not a groupwise format: {fmt}")
     g = _gen(seed)
     codes = draw_group_codes(g, bits, M, K)
     scales = draw_group_scales(g, M, K // GROUP, scale_mult)
     x = draw_activations(g, T, K)
-    return Workload(name, bits, M, K, T, codes, scales, x)
+    return Workload(name, fmt, M, K, T, codes, scales, x)
 
 
 def fp8_rows(name: str, M: int, K: int, T: int, scale_mult: float = 0.01, seed: int = 0) -> Workload:
@@ -113,6 +123,8 @@ CONFIGS: Dict[str, tuple] = {
     "q6_head_248320x5120": (Q6, 248320, 5120, [1, 8], 0.005),
     "fp8_head_248320x5120": (FP8, 248320, 5120, [1, 8, 16], 0.01),
     "fp8_proj_5120x5120": (FP8, 5120, 5120, [1, 8, 16], 0.01),
+    # the upstream artifact's 8-bit output head (the pages time its 8-token verify)
+    "q8_head_248320x5120": (Q8, 248320, 5120, [1, 8], 0.0005),
 }
 
 

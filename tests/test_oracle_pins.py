@@ -114,7 +114,7 @@ SCALE_SET = [0.0, -0.0, 2.0 ** -24, -(2.0 ** -24), 2.0 ** -14 - 2.0 ** -24, -(2.
              2.0 ** -14, -(2.0 ** -14), 1.0, -1.0, 65504.0, -65504.0, 0.3333, -7.125, 1e-3]
 
 
-@pytest.mark.parametrize("bits", [4, 5, 6])
+@pytest.mark.parametrize("bits", [4, 5, 6, 8])
 def test_dequant_every_code_times_every_scale_is_exact(bits):
     # brute force: each code value at each position of a group, times scales that
     # include signed zeros, subnormals, the largest normal; the result must be the
@@ -143,6 +143,20 @@ def test_dequant_every_code_times_every_scale_is_exact(bits):
             if exact == 0:
                 want_neg = (math.copysign(1, s) < 0) != (codes[r, j] < 0)
                 assert (math.copysign(1, got) < 0) == want_neg, (r, j, s, codes[r, j])
+
+
+def test_gemv_q8_is_the_groupwise_definition_with_8_bit_codes():
+    # format id 9 (8-bit groupwise) gives exactly what the groupwise dequant with 8-bit
+    # codes gives; an 8-bit code matrix whose codes fit in 6 bits gives the Q6 result
+    wl = qi.groupwise("t", qi.Q8, 19, 192, 2, 0.01, 4)
+    y8, A8 = oracle.gemv(qi.Q8, wl.codes, wl.scales, wl.x)
+    W = oracle.dequant_groupwise(8, wl.codes, wl.scales).astype(np.float64)
+    X = _x64(wl.x)
+    assert np.all(np.abs(y8 - X @ W.T) <= 1e-12 * A8)
+    small = np.clip(wl.codes, -32, 31).astype(np.int8)
+    y8s, _ = oracle.gemv(qi.Q8, small, wl.scales, wl.x)
+    y6, _ = oracle.gemv(6, small, wl.scales, wl.x)
+    assert np.array_equal(y8s, y6)
 
 
 def test_dequant_rejects_out_of_range_codes():
@@ -209,7 +223,7 @@ def _x64(x_bits):
     return torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
 
 
-@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
 def test_gemv_matches_float64_matmul(fmt):
     # library cross-check: numpy float64 matmul on an independently dequantized
     # matrix (catches a transposed operand, a wrong group index, a scale applied
@@ -225,7 +239,7 @@ def test_gemv_matches_float64_matmul(fmt):
     assert np.allclose(A, A_ref, rtol=1e-12, atol=0)
 
 
-@pytest.mark.parametrize("fmt", [4, 6, 8])
+@pytest.mark.parametrize("fmt", [4, 6, 8, qi.Q8])
 def test_gemv_brute_force_exact_fractions(fmt):
     # exact rational sum on a tiny case; the oracle may differ only by its double
     # summation error (<= K * 2^-53 * A)
@@ -300,7 +314,7 @@ def test_rtn_golden_cases():
         assert codes[0].tolist() == [_eval_expr(case["codes"], j) for j in range(64)], case["name"]
 
 
-@pytest.mark.parametrize("bits", [4, 5, 6])
+@pytest.mark.parametrize("bits", [4, 5, 6, 8])
 def test_rtn_invariants(bits):
     rng = np.random.default_rng(bits)
     n = 400
@@ -329,7 +343,7 @@ def test_rtn_invariants(bits):
 def test_rtn_power_of_two_scale_round_trip():
     # a group built as s*c with s a power of two and a code hitting +-qmax returns (s, c)
     rng = np.random.default_rng(0)
-    for bits in (4, 5, 6):
+    for bits in (4, 5, 6, 8):
         qmax = (1 << (bits - 1)) - 1
         for e in range(-20, 10):
             c = rng.integers(-qmax, qmax + 1, 64)
