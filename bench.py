@@ -38,10 +38,11 @@ def log(*a):
 
 def alg_bytes(fmt, M, K, T):
     """Packed weight information (codes + scales, each read once) + x read + y written."""
+    import qmat_inputs as qi
     if fmt == 8:
         w = M * K + 4 * M
     else:
-        w = M * K * fmt // 8 + 2 * M * (K // 64)
+        w = M * K * qi.code_bits(fmt) // 8 + 2 * M * (K // 64)
     return w + 2 * T * K + 4 * T * M
 
 
@@ -217,7 +218,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=800)
     ap.add_argument("--primary-only", action="store_true", help="skip the other benchmark shapes")
     ap.add_argument("--only", default=None, help="comma-separated config names for the extra shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -11,6 +11,8 @@
  *    complement code c in [-2^(b-1), 2^(b-1)-1].  Scales may be negative (that is how a
  *    group reaches the most negative code).
  *        w[i][j] = fp32(scale[i][j/64]) * code[i][j]            (exact in fp32)
+ *    Groupwise Q8 is the same definition with 8-bit codes in [-128, 127]: the cards' format
+ *    tables store the token embedding, the upstream output head and several projections so.
  *  - Row-scaled FP8 ("Qwen3.8-27B NVFP4 for NInfer", introduction and "Artifact"): one
  *    scale per row times an FP8 value.  The FP8 encoding is OCP E4M3 ("FN": bias 7, no
  *    infinities, S.1111.111 is NaN, largest finite 448) and the row scale is fp32.
@@ -51,10 +53,11 @@ typedef enum {
 } qmat_status;
 
 typedef enum {
-    QMAT_Q4 = 4,          /* groupwise 4-bit codes, FP16 scale per 64 weights */
-    QMAT_Q5 = 5,          /* groupwise 5-bit */
-    QMAT_Q6 = 6,          /* groupwise 6-bit */
-    QMAT_FP8_E4M3_ROW = 8 /* OCP E4M3 bytes, fp32 scale per row */
+    QMAT_Q4 = 4,           /* groupwise 4-bit codes, FP16 scale per 64 weights */
+    QMAT_Q5 = 5,           /* groupwise 5-bit */
+    QMAT_Q6 = 6,           /* groupwise 6-bit */
+    QMAT_FP8_E4M3_ROW = 8, /* OCP E4M3 bytes, fp32 scale per row */
+    QMAT_Q8 = 9            /* groupwise 8-bit (the value is not the bit width: 8 is FP8) */
 } qmat_format;
 
 typedef enum {
@@ -68,7 +71,7 @@ typedef struct qmat *qmat_t;
 /* Size in bytes of the packed blob for an M x K matrix, or 0 if (fmt, M, K) is invalid.
  * Layout (all offsets from the start of the blob; 64-row tiles, NT = ceil(M/64);
  * 128-wide k units, NU = ceil(K/128)):
- *   codes:  NT * NU * NB blocks of 1024 bytes, NB = 4 (Q4), 5 (Q5), 6 (Q6), 8 (FP8);
+ *   codes:  NT * NU * NB blocks of 1024 bytes, NB = 4 (Q4), 5 (Q5), 6 (Q6), 8 (Q8, FP8);
  *   scales: groupwise NT * NU * 256 bytes (fp16 [tile][unit][row%16][group in unit][row/16]);
  *           FP8 NT * 256 bytes (fp32 [tile][row%16][row/16]).
  * The byte order inside a block is documented in the repository's design notes.
@@ -76,7 +79,7 @@ typedef struct qmat *qmat_t;
 size_t qmat_packed_bytes(int fmt, int64_t M, int64_t K);
 
 /* Pack a matrix into the layout above.  Host only; pure; thread-safe.
- *   codes:  groupwise: int8 [M][K], each in [-2^(b-1), 2^(b-1)-1];
+ *   codes:  groupwise: int8 [M][K], each in [-2^(b-1), 2^(b-1)-1] (b = 4, 5, 6, or 8 for Q8);
  *           FP8: uint8 [M][K] E4M3 bytes (0x7F / 0xFF, the NaNs, are rejected).
  *   scales: groupwise: uint16 [M][K/64] binary16 bit patterns, finite, any sign;
  *           FP8: float [M], finite.

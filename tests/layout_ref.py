@@ -3,7 +3,7 @@ comment at the top of weight_only_quant_amd/csrc/qmat_layout.h), in numpy.  Used
 tests to check qmat_pack by round trip; it shares no code with the packer."""
 import numpy as np
 
-NB = {4: 4, 5: 5, 6: 6, 8: 8}
+NB = {4: 4, 5: 5, 6: 6, 8: 8, 9: 8}  # format id -> 1 KB blocks per unit (9 = Q8)
 
 
 def dims(fmt, M, K):
@@ -65,9 +65,11 @@ def unpack(fmt, M, K, blob):
                             ((A << np.uint32(6)) & np.uint32(0xC0C0C0C0)) | ((B << np.uint32(4)) & np.uint32(0x30303030)) |
                             ((C << np.uint32(2)) & np.uint32(0x0C0C0C0C)))
                     v = _sbyte(O, i) >> 2
-                else:
+                else:  # FP8 bytes, or Q8 two's complement bytes
                     w = W[..., 8 * ka + 2 * m + e // 4]
                     v = ((w >> np.uint32(8 * (e % 4))) & np.uint32(0xFF)).astype(np.int32)
+                    if fmt == 9:
+                        v = np.where(v >= 128, v - 256, v)
                 cols = (128 * u_idx + 32 * ka + 8 * q[None, None, :] + e)  # [1,NU,64]
                 out[np.broadcast_to(rows, v.shape), np.broadcast_to(cols, v.shape)] = v
     if fmt == 8:

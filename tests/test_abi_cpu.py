@@ -78,9 +78,9 @@ def test_pack_rejects_out_of_range_codes(fmt, bad):
 
 
 def test_pack_accepts_extreme_codes():
-    for fmt in (4, 5, 6):
+    for fmt, bits in ((4, 4), (5, 5), (6, 6), (wq.QMAT_Q8, 8)):
         c, s = _codes(fmt)
-        c[0, 0], c[0, 1] = -(1 << (fmt - 1)), (1 << (fmt - 1)) - 1
+        c[0, 0], c[0, 1] = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
         wq.qmat_pack(fmt, c, s)
 
 
@@ -115,7 +115,7 @@ def test_create_validation_without_gpu():
     L = wq.lib()
     h = ctypes.c_void_p()
     assert L.qmat_create(None, 4, 64, 128, 16, 100) == wq.QMAT_EINVAL
-    assert L.qmat_create(ctypes.byref(h), 9, 64, 128, 16, 100) == wq.QMAT_EINVAL
+    assert L.qmat_create(ctypes.byref(h), 7, 64, 128, 16, 100) == wq.QMAT_EINVAL
     assert L.qmat_create(ctypes.byref(h), 4, 64, 100, 16, 100) == wq.QMAT_ESHAPE
     assert L.qmat_create(ctypes.byref(h), 4, 64, 128, None, 100) == wq.QMAT_EINVAL
     assert L.qmat_create(ctypes.byref(h), 4, 64, 128, 8, wq.qmat_packed_bytes(4, 64, 128)) == wq.QMAT_EINVAL  # misaligned

@@ -59,7 +59,7 @@ def _check_y(y, wl, label, rows=None):
 DQ_SHAPES = [(64, 128), (200, 320), (1, 64), (130, 192)]
 
 
-@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
 @pytest.mark.parametrize("M,K", DQ_SHAPES)
 def test_dequant_bit_exact(fmt, M, K):
     say(f"dequant fmt={fmt} M={M} K={K}")
@@ -68,15 +68,16 @@ def test_dequant_bit_exact(fmt, M, K):
     w = qm.dequant()
     torch.cuda.synchronize()
     got = w.cpu().numpy()
-    ref = oracle.dequant_fp8(wl.codes, wl.scales) if fmt == 8 else oracle.dequant_groupwise(fmt, wl.codes, wl.scales)
+    ref = oracle.dequant_fp8(wl.codes, wl.scales) if fmt == 8 else oracle.dequant_groupwise(qi.code_bits(fmt), wl.codes, wl.scales)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt", [4, 5, 6])
+@pytest.mark.parametrize("fmt", [4, 5, 6, qi.Q8])
 def test_dequant_every_code_edge_scales(fmt):
     # every code at every position, times +-0, subnormal, largest-normal and ordinary scales
     say(f"dequant edge fmt={fmt}")
-    lo, hi = -(1 << (fmt - 1)), (1 << (fmt - 1)) - 1
+    bits = qi.code_bits(fmt)
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
     n = hi - lo + 1
     svals = np.array([0.0, -0.0, 2 ** -24, -(2 ** -24), 2 ** -14 - 2 ** -24, 2 ** -14, -1.0, 65504.0,
                       -65504.0, 0.3333, 1e-3, -7.125], dtype=np.float16).view(np.uint16)
@@ -89,7 +90,7 @@ def test_dequant_every_code_edge_scales(fmt):
     scales = np.roll(scales, 1, axis=1) if fmt == 5 else scales
     qm = wq.QMat(fmt, codes, scales)
     got = qm.dequant().cpu().numpy()
-    ref = oracle.dequant_groupwise(fmt, codes, scales)
+    ref = oracle.dequant_groupwise(bits, codes, scales)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
@@ -111,7 +112,7 @@ RUN_SHAPES = [(200, 320), (64, 1024), (1, 64), (130, 192), (257, 2176)]
 
 
 @pytest.mark.parametrize("route", ["valu", "mfma"])
-@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
 @pytest.mark.parametrize("M,K", RUN_SHAPES)
 def test_run_parity_small(route, fmt, M, K):
     wl = _workload(fmt, M, K, 16, 100 + M + K + fmt)
@@ -126,7 +127,7 @@ def test_run_parity_small(route, fmt, M, K):
         _check_y(y, sub, f"{route} fmt={fmt} {M}x{K} T={T}")
 
 
-@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
 @pytest.mark.parametrize("route,T", [("valu", 1), ("valu", 4), ("mfma", 1), ("mfma", 9)])
 def test_run_split_shapes_agree(fmt, route, T):
     # every (depth, waves, splits) launch shape gives an in-tolerance result; each is
@@ -148,7 +149,7 @@ def test_run_split_shapes_agree(fmt, route, T):
                 _check_y(y1, wl, f"{route} T={T} depth={depth} waves={waves} splits={splits}")
 
 
-@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
 @pytest.mark.parametrize("route,T", [("valu", 1), ("valu", 3), ("mfma", 1), ("mfma", 6), ("mfma", 16)])
 def test_run_tail_plans(fmt, route, T):
     # plans whose trailing tiles are shared by a different number of workgroups than the
@@ -202,7 +203,8 @@ def _exact_workload(fmt, M, K, T, seed):
         codes = torch.from_numpy(ints).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         scales = (2.0 ** rng.integers(-6, 3, M)).astype(np.float32)
     else:
-        lo, hi = -(1 << (fmt - 1)), (1 << (fmt - 1)) - 1
+        bits = qi.code_bits(fmt)
+        lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
         codes = rng.integers(lo, hi + 1, (M, K)).astype(np.int8)
         sg = np.where(rng.random((M, K // 64)) < 0.5, -1.0, 1.0)
         scales = (sg * 2.0 ** rng.integers(-2, 2, (M, K // 64))).astype(np.float16).view(np.uint16)
@@ -210,7 +212,7 @@ def _exact_workload(fmt, M, K, T, seed):
 
 
 @pytest.mark.parametrize("route", ["valu", "mfma"])
-@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
 def test_run_bit_exact_on_exact_inputs(route, fmt):
     M, K = 130, 1024
     for T in (1, 4, 8, 16):
@@ -226,7 +228,7 @@ def test_run_bit_exact_on_exact_inputs(route, fmt):
 
 # ------------------------------------------------------------------ degenerate inputs
 
-@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
 def test_zero_and_sparse_codes(fmt):
     # all-zero codes give exactly zero; one nonzero code per row gives that single product
     M, K, T = 70, 640, 8
@@ -235,7 +237,8 @@ def test_zero_and_sparse_codes(fmt):
     rng = np.random.default_rng(5)
     cols = rng.integers(0, K, M)
     for i in range(1, M):
-        codes[i, cols[i]] = (0x38 if fmt == 8 else (-(1 << (fmt - 1)) if i % 2 else (1 << (fmt - 1)) - 1))
+        b = qi.code_bits(fmt)
+        codes[i, cols[i]] = (0x38 if fmt == 8 else (-(1 << (b - 1)) if i % 2 else (1 << (b - 1)) - 1))
     for route in ("valu", "mfma"):
         say(f"sparse {route} fmt={fmt}")
         qm = wq.QMat(fmt, codes, wl.scales)
@@ -349,6 +352,6 @@ def test_full_size_sampled_rows(name):
     if wl.fmt == 8:
         ref = oracle.dequant_fp8(wl.codes[drows], wl.scales[drows])
     else:
-        ref = oracle.dequant_groupwise(wl.fmt, wl.codes[drows], wl.scales[drows])
+        ref = oracle.dequant_groupwise(qi.code_bits(wl.fmt), wl.codes[drows], wl.scales[drows])
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     qm.close()

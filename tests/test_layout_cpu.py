@@ -16,7 +16,7 @@ def _workload(fmt, M, K, seed):
     return qi.groupwise("t", fmt, M, K, 1, 0.01, seed)
 
 
-@pytest.mark.parametrize("fmt", [4, 5, 6, 8])
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
 @pytest.mark.parametrize("M,K", SHAPES)
 def test_pack_round_trip(fmt, M, K):
     wl = _workload(fmt, M, K, M + K + fmt)
@@ -41,10 +41,11 @@ def test_pack_round_trip(fmt, M, K):
     assert not sp.any()
 
 
-@pytest.mark.parametrize("fmt", [4, 5, 6])
+@pytest.mark.parametrize("fmt", [4, 5, 6, qi.Q8])
 def test_pack_every_code_at_every_position(fmt):
     # each code value visits every position of every k octet and every row slot of a tile
-    lo, hi = -(1 << (fmt - 1)), (1 << (fmt - 1)) - 1
+    bits = qi.code_bits(fmt)
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
     n = hi - lo + 1
     M, K = 64 + 5, 256
     r = np.arange(M)[:, None]
@@ -73,3 +74,4 @@ def test_packed_bytes_per_weight():
     assert wq.qmat_packed_bytes(5, 5120, 17408) == 5120 * 17408 * 5 // 8 + 5120 * 272 * 2
     assert wq.qmat_packed_bytes(6, 248320, 5120) == 248320 * 5120 * 3 // 4 + 248320 * 80 * 2
     assert wq.qmat_packed_bytes(8, 248320, 5120) == 248320 * 5120 + 248320 * 4
+    assert wq.qmat_packed_bytes(wq.QMAT_Q8, 248320, 5120) == 248320 * 5120 + 248320 * 80 * 2

@@ -56,8 +56,8 @@ struct PackSrc {
 inline uint32_t code_at(const PackSrc &p, int64_t row, int64_t k)
 {
     if (row >= p.M || k >= p.K) return 0;
-    if (p.fmt == 8) return p.bytes[row * p.K + k];
-    return (uint32_t)(uint8_t)p.codes[row * p.K + k] & ((1u << p.fmt) - 1u);
+    if (p.fmt == kFmtFp8) return p.bytes[row * p.K + k];
+    return (uint32_t)(uint8_t)p.codes[row * p.K + k] & ((1u << group_code_bits(p.fmt)) - 1u);
 }
 
 void pack_tile(const PackSrc &p, int64_t tile, uint8_t *out)
@@ -109,7 +109,7 @@ void pack_tile(const PackSrc &p, int64_t tile, uint8_t *out)
                         W[6 * ka + 3 * pp + 1] = B;
                         W[6 * ka + 3 * pp + 2] = C;
                     }
-                } else {  // FP8
+                } else {  // FP8 bytes, or Q8 codes as bytes
                     for (int m = 0; m < 4; ++m)
                         for (int h = 0; h < 2; ++h) {
                             uint32_t w = 0;
@@ -121,7 +121,7 @@ void pack_tile(const PackSrc &p, int64_t tile, uint8_t *out)
             for (int j = 0; j < NB; ++j)
                 memcpy(codes + ((tile * NU + u) * NB + j) * kBlockBytes + 16 * L, &W[4 * j], 16);
         }
-        if (fmt != 8) {
+        if (fmt != kFmtFp8) {
             const int64_t G = p.K / kGroup;
             uint16_t *sb = reinterpret_cast<uint16_t *>(scales + (tile * NU + u) * kScaleBlockBytes);
             for (int r16 = 0; r16 < 16; ++r16)
@@ -132,7 +132,7 @@ void pack_tile(const PackSrc &p, int64_t tile, uint8_t *out)
                     }
         }
     }
-    if (fmt == 8) {
+    if (fmt == kFmtFp8) {
         float *sb = reinterpret_cast<float *>(scales + tile * kScaleBlockBytes);
         for (int r16 = 0; r16 < 16; ++r16)
             for (int m = 0; m < 4; ++m) {
@@ -269,7 +269,7 @@ int qmat_pack(int fmt, int64_t M, int64_t K, const void *codes, const void *scal
     const size_t need = qmat_packed_bytes(fmt, M, K);
     if (out_bytes < need) return fail(QMAT_ESIZE, "qmat_pack: out_bytes %zu < %zu", out_bytes, need);
     PackSrc p{fmt, M, K, nullptr, nullptr, nullptr, nullptr};
-    if (fmt == 8) {
+    if (fmt == kFmtFp8) {
         p.bytes = static_cast<const uint8_t *>(codes);
         p.rs = static_cast<const float *>(scales);
         for (int64_t i = 0; i < M * K; ++i)
@@ -280,7 +280,8 @@ int qmat_pack(int fmt, int64_t M, int64_t K, const void *codes, const void *scal
     } else {
         p.codes = static_cast<const int8_t *>(codes);
         p.hs = static_cast<const uint16_t *>(scales);
-        const int lo = -(1 << (fmt - 1)), hi = (1 << (fmt - 1)) - 1;
+        const int bits = group_code_bits(fmt);
+        const int lo = -(1 << (bits - 1)), hi = (1 << (bits - 1)) - 1;
         for (int64_t i = 0; i < M * K; ++i)
             if (p.codes[i] < lo || p.codes[i] > hi)
                 return fail(QMAT_ERANGE, "qmat_pack: code %d outside [%d,%d] at row %lld col %lld", p.codes[i], lo, hi, (long long)(i / K), (long long)(i % K));

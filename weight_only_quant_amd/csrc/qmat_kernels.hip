@@ -2,13 +2,16 @@
 //
 // Weight formats (NInfer model cards): groupwise Q4/Q5/Q6 — FP16 scale per 64 weights along K
 // times a two's-complement code ("Qwen3.8-27B for NInfer on the RTX 3090", "What is different
-// from the upstream artifact") — and row-scaled FP8 E4M3 ("Qwen3.8-27B NVFP4 for NInfer",
-// "Artifact").  The packed layout is described in qmat_layout.h.
+// from the upstream artifact") — groupwise Q8, the same definition with 8-bit codes (the cards'
+// format tables: token embedding / output head, attention and other projections) — and
+// row-scaled FP8 E4M3 ("Qwen3.8-27B NVFP4 for NInfer", "Artifact").  The packed layout is
+// described in qmat_layout.h.  Template parameter FMT is the format id (9 = Q8).
 //
 // Every code is turned into an exact small float before any product is formed:
 //   Q4   v_cvt_off_f32_i4 reads a two's-complement nibble as code/16 (SDWA picks the byte);
 //   Q5/6 the code is assembled in the top bits of a byte and v_cvt_f32_i32 with SDWA sign
 //        extension reads it as 8*code or 4*code;
+//   Q8   the same SDWA convert reads each stored byte as the code;
 //   FP8  v_cvt_scalef32_pk_bf16_fp8 widens two E4M3 bytes to bf16 exactly.
 // These values are exact in bf16, so bf16(code) * bf16(x) is an exact product; dot products
 // accumulate in fp32 (v_dot2c_f32_bf16 on the vector ALU, or the 16x16x32 bf16 MFMA), and the
@@ -39,6 +42,7 @@ template <> struct Fmt<4> { static constexpr int NB = 4; static constexpr float 
 template <> struct Fmt<5> { static constexpr int NB = 5; static constexpr float kToCode = 0.125f; };
 template <> struct Fmt<6> { static constexpr int NB = 6; static constexpr float kToCode = 0.25f; };
 template <> struct Fmt<8> { static constexpr int NB = 8; static constexpr float kToCode = 1.0f; };
+template <> struct Fmt<9> { static constexpr int NB = 8; static constexpr float kToCode = 1.0f; };
 
 // ------------------------------------------------------------------ exact code conversion
 
@@ -99,6 +103,10 @@ __device__ __forceinline__ void codes8(const uint32_t *W, float (&f)[8])
                             (shift_signed(W[5 * KA + 4], 3 - 2 * d) & 0x18181818u);
                 }
             }
+        } else if constexpr (FMT == 9) {
+            // Q8: the row's 8 codes are the bytes of two dwords, already signed bytes
+            o[0] = W[8 * KA + 2 * MM];
+            o[1] = W[8 * KA + 2 * MM + 1];
         } else {  // FMT == 6
             const uint32_t A = W[6 * KA + 3 * (MM >> 1)], B = W[6 * KA + 3 * (MM >> 1) + 1],
                            C = W[6 * KA + 3 * (MM >> 1) + 2];
@@ -655,6 +663,7 @@ static const void *run_kernel_for(int fmt, int route, int T, int depth)
     case 5: return run_kernel<5>(route, T, depth);
     case 6: return run_kernel<6>(route, T, depth);
     case 8: return run_kernel<8>(route, T, depth);
+    case 9: return run_kernel<9>(route, T, depth);
     default: return nullptr;
     }
 }
@@ -695,7 +704,8 @@ template <int FMT> static const void *dequant_kernel_ptr() { return reinterpret_
 hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t st)
 {
     const void *k = fmt == 4 ? dequant_kernel_ptr<4>() : fmt == 5 ? dequant_kernel_ptr<5>()
-                  : fmt == 6 ? dequant_kernel_ptr<6>() : fmt == 8 ? dequant_kernel_ptr<8>() : nullptr;
+                  : fmt == 6 ? dequant_kernel_ptr<6>() : fmt == 8 ? dequant_kernel_ptr<8>()
+                  : fmt == 9 ? dequant_kernel_ptr<9>() : nullptr;
     if (!k) return hipErrorInvalidValue;
     DequantArgs arg = a;
     void *args[] = {&arg};

@@ -22,7 +22,9 @@
 //               bits [7:2] of byte i the codes (m0, e=i), (m0, e=4+i), (m1, e=i) (signed byte =
 //               4*code); their bits [1:0] hold bits [5:4], [3:2], [1:0] of code (m1, e=4+i).
 //   FP8 (NB 8): W[8*kappa + 2*m + h] holds the E4M3 bytes of row m, e = 4h + i in byte i.
+//   Q8  (NB 8): the same byte order, each byte an 8-bit two's complement code.
 //
+// Format ids: 4, 5, 6 groupwise with that many bits; 9 groupwise 8-bit (Q8); 8 row-scaled FP8.
 // Scales: groupwise, one 256-byte block per (tile, unit) at scales + (t*NU + u)*256; lane L reads
 // 16 bytes at + 16*(L % 16): binary16 of (row rho(L, m), group 2u + g) at index 4*g + m.
 // FP8: one 256-byte block per tile at scales + t*256; fp32 of row rho(L, m) at index 4*(L%16) + m.
@@ -41,9 +43,18 @@ constexpr int kBlockBytes = 1024;
 constexpr int kScaleBlockBytes = 256;
 constexpr int kMaxT = 16;
 
+constexpr int kFmtFp8 = 8;  // row-scaled FP8 E4M3
+constexpr int kFmtQ8 = 9;   // groupwise 8-bit codes
+
 constexpr int blocks_per_unit(int fmt)
 {
-    return fmt == 4 ? 4 : fmt == 5 ? 5 : fmt == 6 ? 6 : fmt == 8 ? 8 : 0;
+    return fmt == 4 ? 4 : fmt == 5 ? 5 : fmt == 6 ? 6 : (fmt == kFmtFp8 || fmt == kFmtQ8) ? 8 : 0;
+}
+
+// bits per code of a groupwise format, 0 for FP8
+constexpr int group_code_bits(int fmt)
+{
+    return (fmt == 4 || fmt == 5 || fmt == 6) ? fmt : fmt == kFmtQ8 ? 8 : 0;
 }
 
 inline bool format_ok(int fmt) { return blocks_per_unit(fmt) != 0; }
@@ -58,7 +69,7 @@ inline size_t code_bytes(int fmt, int64_t M, int64_t K)
 
 inline size_t scale_bytes(int fmt, int64_t M, int64_t K)
 {
-    return fmt == 8 ? (size_t)num_tiles(M) * kScaleBlockBytes
+    return fmt == kFmtFp8 ? (size_t)num_tiles(M) * kScaleBlockBytes
                     : (size_t)num_tiles(M) * (size_t)num_units(K) * kScaleBlockBytes;
 }
 
