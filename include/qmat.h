@@ -97,6 +97,17 @@ int qmat_pack(int fmt, int64_t M, int64_t K, const void *codes, const void *scal
  * Errors: QMAT_EINVAL, QMAT_ESHAPE, QMAT_ESIZE (bytes mismatch), QMAT_ENOMEM, QMAT_EHIP. */
 int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packed_dev, size_t bytes);
 
+/* A handle over rows [row0, row0 + rows) of an existing handle's matrix, sharing its packed
+ * device memory (no copy): for example the gate and the up halves of a gate+up matrix packed
+ * as one (the giveen/ninfer-ext README, "Flash-Next speed", "How it got here": projection splits
+ * taken as views of one weight instead of device copies).
+ *   row0: a multiple of 64 (a tile boundary); rows >= 1; row0 + rows <= the parent's M.
+ * The view behaves as an M = rows matrix in every call (y is [T][rows]).  It borrows the packed
+ * memory the parent borrows (which must outlive both) but not the parent handle itself, which
+ * may be destroyed first; it owns its own split-K workspace, allocated here.
+ * Errors: QMAT_EINVAL (null pointers), QMAT_ESHAPE (row range), QMAT_ENOMEM, QMAT_EHIP. */
+int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows);
+
 /* y = x . W^T.  x: device bf16 [T][K] (16-byte aligned); y: device fp32 [T][M], fully
  * overwritten.  T == 0 is a no-op.  Asynchronous on stream; no allocation, no sync.
  * Errors: QMAT_EINVAL (null handle/pointers, misaligned x), QMAT_ESHAPE (T > 16 or T < 0),

@@ -123,6 +123,14 @@ def test_create_validation_without_gpu():
     assert h.value is None
 
 
+def test_create_view_rejects_null_arguments():
+    L = wq.lib()
+    h = ctypes.c_void_p()
+    assert L.qmat_create_view(None, 16, 0, 64) == wq.QMAT_EINVAL
+    assert L.qmat_create_view(ctypes.byref(h), None, 0, 64) == wq.QMAT_EINVAL
+    assert h.value is None
+
+
 def test_run_and_dequant_reject_null_handle():
     L = wq.lib()
     assert L.qmat_run(None, 16, 16, 1, None) == wq.QMAT_EINVAL

@@ -192,6 +192,46 @@ def test_run_plan_rejects_bad_fields():
     assert e.value.status == wq.QMAT_ESIZE
 
 
+@pytest.mark.parametrize("fmt", [4, 6, 8, qi.Q8])
+def test_row_views(fmt):
+    # views over tile-aligned row ranges of one packed matrix (gate / up halves, a ragged last
+    # range, a single partial tile) give the sub-matrix's product and dequantization; the view
+    # outlives its parent handle
+    M, K, T = 455, 704, 5
+    wl = _workload(fmt, M, K, T, 41 + fmt)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    for row0, rows in [(0, 192), (192, 263), (128, 64), (448, 7), (64, 1), (0, M)]:
+        say(f"view fmt={fmt} rows [{row0}, {row0 + rows})")
+        v = wq.qmat_create_view(qm.handle, row0, rows)
+        sub = qi.Workload("v", fmt, rows, K, T, wl.codes[row0:row0 + rows], wl.scales[row0:row0 + rows], wl.x)
+        for Tr in (1, T):
+            y = torch.full((Tr, rows), float("nan"), device="cuda")
+            wq.qmat_run(v, xd[:Tr], y, T=Tr)
+            torch.cuda.synchronize()
+            _check_y(y, qi.Workload("v", fmt, rows, K, Tr, sub.codes, sub.scales, wl.x[:Tr]), f"view {row0}+{rows} T={Tr}")
+        w = torch.empty((rows, K), device="cuda")
+        wq.qmat_dequant(v, w)
+        torch.cuda.synchronize()
+        ref = oracle.dequant_fp8(sub.codes, sub.scales) if fmt == 8 else \
+            oracle.dequant_groupwise(qi.code_bits(fmt), sub.codes, sub.scales)
+        assert np.array_equal(w.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+        wq.qmat_destroy(v)
+    v = wq.qmat_create_view(qm.handle, 256, 199)
+    qm.close()  # the parent handle goes first; the packed blob (qm.packed) stays alive
+    y = torch.empty((T, 199), device="cuda")
+    wq.qmat_run(v, xd, y, T=T)
+    torch.cuda.synchronize()
+    _check_y(y, qi.Workload("v", fmt, 199, K, T, wl.codes[256:], wl.scales[256:], wl.x), "view after parent")
+    wq.qmat_destroy(v)
+    parent = wq.qmat_create(fmt, M, K, qm.packed)
+    for row0, rows in [(1, 64), (-64, 64), (0, 0), (448, 8), (512, 1)]:
+        with pytest.raises(wq.QmatError) as e:
+            wq.qmat_create_view(parent, row0, rows)
+        assert e.value.status == wq.QMAT_ESHAPE, (row0, rows)
+    wq.qmat_destroy(parent)
+
+
 def _exact_workload(fmt, M, K, T, seed):
     """Inputs whose products and partial sums are all exact in fp32: small integer bf16
     activations and power-of-two scales (FP8: integer-valued E4M3 bytes)."""

@@ -29,6 +29,7 @@ SIGNATURES = {
     "qmat_packed_bytes": (_sz, [_int, _i64, _i64]),
     "qmat_pack": (_int, [_int, _i64, _i64, _vp, _vp, _vp, _sz]),
     "qmat_create": (_int, [ctypes.POINTER(_vp), _int, _i64, _i64, _vp, _sz]),
+    "qmat_create_view": (_int, [ctypes.POINTER(_vp), _vp, _i64, _i64]),
     "qmat_run": (_int, [_vp, _vp, _vp, _int, _vp]),
     "qmat_run_ex": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]),
     "qmat_dequant": (_int, [_vp, _vp, _vp]),
@@ -110,6 +111,13 @@ def qmat_create(fmt: int, M: int, K: int, packed_dev) -> int:
     """packed_dev: a torch uint8 device tensor holding qmat_pack's output (borrowed)."""
     h = ctypes.c_void_p()
     _check(lib().qmat_create(ctypes.byref(h), fmt, M, K, packed_dev.data_ptr(), packed_dev.numel()))
+    return h.value
+
+
+def qmat_create_view(parent: int, row0: int, rows: int) -> int:
+    """A handle over rows [row0, row0 + rows) of parent's matrix (row0 a multiple of 64)."""
+    h = ctypes.c_void_p()
+    _check(lib().qmat_create_view(ctypes.byref(h), parent, row0, rows))
     return h.value
 
 

@@ -224,8 +224,8 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
 struct qmat {
     int fmt;
     int64_t M, K, NT, NU, Mpad;
-    const uint8_t *packed;
-    size_t bytes;
+    const uint8_t *codes;   // first code block of the handle's first tile (borrowed)
+    const uint8_t *scales;  // its first scale block (borrowed)
     float *ws;
     size_t ws_floats;
     uint32_t *counters;
@@ -315,40 +315,37 @@ int qmat_pack(int fmt, int64_t M, int64_t K, const void *codes, const void *scal
     return ok();
 }
 
-int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packed_dev, size_t bytes)
+namespace {
+
+// A handle over M x K rows whose packed tiles start at (codes, scales): plans for every route
+// and T, and the split-K workspace they need.
+int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
+                const char *who)
 {
-    if (!handle) return fail(QMAT_EINVAL, "qmat_create: null handle pointer");
-    *handle = nullptr;
-    if (!format_ok(fmt)) return fail(QMAT_EINVAL, "qmat_create: unknown format %d", fmt);
-    if (!shape_ok(M, K)) return fail(QMAT_ESHAPE, "qmat_create: bad shape M=%lld K=%lld", (long long)M, (long long)K);
-    if (!packed_dev) return fail(QMAT_EINVAL, "qmat_create: null packed pointer");
-    if (reinterpret_cast<uintptr_t>(packed_dev) % 16) return fail(QMAT_EINVAL, "qmat_create: packed pointer not 16-byte aligned");
-    const size_t need = qmat_packed_bytes(fmt, M, K);
-    if (bytes != need) return fail(QMAT_ESIZE, "qmat_create: bytes %zu != packed size %zu", bytes, need);
     qmat *h = new (std::nothrow) qmat;
-    if (!h) return fail(QMAT_ENOMEM, "qmat_create: out of host memory");
+    if (!h) return fail(QMAT_ENOMEM, "%s: out of host memory", who);
     h->fmt = fmt;
     h->M = M;
     h->K = K;
     h->NT = num_tiles(M);
     h->NU = num_units(K);
     h->Mpad = h->NT * kTileRows;
-    h->packed = static_cast<const uint8_t *>(packed_dev);
-    h->bytes = bytes;
+    h->codes = codes;
+    h->scales = scales;
     h->ws = nullptr;
     h->counters = nullptr;
     h->ws_floats = 0;
     if (hipGetDevice(&h->device) != hipSuccess) {
         delete h;
-        return fail(QMAT_EHIP, "qmat_create: hipGetDevice failed");
+        return fail(QMAT_EHIP, "%s: hipGetDevice failed", who);
     }
     if (hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || h->cus < 1) {
         delete h;
-        return fail(QMAT_EHIP, "qmat_create: cannot read the compute unit count");
+        return fail(QMAT_EHIP, "%s: cannot read the compute unit count", who);
     }
     // launch plans for both routes and every tokens-per-launch; the workspace covers the
     // largest split-K partial set among them, and at least 8 splits at T = 16 for matrices of
-    // up to 65536 rows (explicit launch shapes in tests and tuning)
+    // up to 4096 rows (explicit launch shapes in tests and tuning)
     size_t need_ws = 0;
     for (int r = kRouteValu; r <= kRouteMfma; ++r)
         for (int T = 1; T <= kMaxT; ++T) {
@@ -364,24 +361,55 @@ int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packe
         if (hipMalloc(&h->ws, h->ws_floats * sizeof(float)) != hipSuccess) {
             (void)hipGetLastError();
             delete h;
-            return fail(QMAT_ENOMEM, "qmat_create: workspace allocation failed");
+            return fail(QMAT_ENOMEM, "%s: workspace allocation failed", who);
         }
         if (hipMalloc(&h->counters, (size_t)h->NT * sizeof(uint32_t)) != hipSuccess) {
             (void)hipGetLastError();
             (void)hipFree(h->ws);
             delete h;
-            return fail(QMAT_ENOMEM, "qmat_create: counter allocation failed");
+            return fail(QMAT_ENOMEM, "%s: counter allocation failed", who);
         }
         if (hipMemset(h->counters, 0, (size_t)h->NT * sizeof(uint32_t)) != hipSuccess ||
             hipDeviceSynchronize() != hipSuccess) {
             (void)hipFree(h->ws);
             (void)hipFree(h->counters);
             delete h;
-            return fail(QMAT_EHIP, "qmat_create: counter initialisation failed");
+            return fail(QMAT_EHIP, "%s: counter initialisation failed", who);
         }
     }
     *handle = h;
     return ok();
+}
+
+}  // namespace
+
+int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packed_dev, size_t bytes)
+{
+    if (!handle) return fail(QMAT_EINVAL, "qmat_create: null handle pointer");
+    *handle = nullptr;
+    if (!format_ok(fmt)) return fail(QMAT_EINVAL, "qmat_create: unknown format %d", fmt);
+    if (!shape_ok(M, K)) return fail(QMAT_ESHAPE, "qmat_create: bad shape M=%lld K=%lld", (long long)M, (long long)K);
+    if (!packed_dev) return fail(QMAT_EINVAL, "qmat_create: null packed pointer");
+    if (reinterpret_cast<uintptr_t>(packed_dev) % 16) return fail(QMAT_EINVAL, "qmat_create: packed pointer not 16-byte aligned");
+    const size_t need = qmat_packed_bytes(fmt, M, K);
+    if (bytes != need) return fail(QMAT_ESIZE, "qmat_create: bytes %zu != packed size %zu", bytes, need);
+    const uint8_t *codes = static_cast<const uint8_t *>(packed_dev);
+    return make_handle(handle, fmt, M, K, codes, codes + code_bytes(fmt, M, K), "qmat_create");
+}
+
+int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows)
+{
+    if (!view) return fail(QMAT_EINVAL, "qmat_create_view: null view pointer");
+    *view = nullptr;
+    if (!parent) return fail(QMAT_EINVAL, "qmat_create_view: null parent");
+    if (row0 < 0 || rows < 1 || row0 % kTileRows || row0 + rows > parent->M)
+        return fail(QMAT_ESHAPE, "qmat_create_view: rows [%lld, %lld) not a 64-aligned range of the parent's %lld rows",
+                    (long long)row0, (long long)(row0 + rows), (long long)parent->M);
+    const int64_t t0 = row0 / kTileRows;
+    const size_t cstep = (size_t)parent->NU * blocks_per_unit(parent->fmt) * kBlockBytes;
+    const size_t sstep = parent->fmt == kFmtFp8 ? (size_t)kScaleBlockBytes : (size_t)parent->NU * kScaleBlockBytes;
+    return make_handle(view, parent->fmt, rows, parent->K, parent->codes + t0 * cstep, parent->scales + t0 * sstep,
+                       "qmat_create_view");
 }
 
 namespace {
@@ -412,8 +440,8 @@ int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, vo
                     p.tail_tiles, tail_splits, Tl);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const uint16_t *x = static_cast<const uint16_t *>(x_dev);
-    const uint8_t *codes = h->packed;
-    const uint8_t *scales = h->packed + code_bytes(h->fmt, h->M, h->K);
+    const uint8_t *codes = h->codes;
+    const uint8_t *scales = h->scales;
     for (int t0 = 0; t0 < T; t0 += Tl) {
         RunArgs a;
         a.codes = codes;
@@ -500,8 +528,8 @@ int qmat_dequant(qmat_t h, float *w_dev, void *stream)
     if (!w_dev) return fail(QMAT_EINVAL, "qmat_dequant: null output");
     if (reinterpret_cast<uintptr_t>(w_dev) % 16) return fail(QMAT_EINVAL, "qmat_dequant: output not 16-byte aligned");
     DequantArgs a;
-    a.codes = h->packed;
-    a.scales = h->packed + code_bytes(h->fmt, h->M, h->K);
+    a.codes = h->codes;
+    a.scales = h->scales;
     a.w = w_dev;
     a.M = (int)h->M;
     a.K = (int)h->K;
