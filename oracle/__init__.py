@@ -19,6 +19,13 @@ Functions and the definitions they follow (NInfer model cards):
   gemv                y = x W^T in double, plus A = sum |w x|
   rtn_encode          the upstream round-to-nearest encoder (scale = absmax / qmax)
   check               the acceptance test |y - y_ref| <= 1e-4 * A + 1e-6
+  logsumexp           log sum_i exp(y_i) per token over the output-head logits (the fork's
+                      "single-pass logsumexp": giveen/ninfer-ext README, upstream pull
+                      requests merged ahead of upstream), in float64 (numpy)
+  topk                the k largest logits per token, ties to the lower row, rows mapped
+                      through an optional index (the candidate top-k that reads the full head or
+                      the indexed 131,072-row proposal head: "Qwen3.8-27B for NInfer on the RTX
+                      3090", run notes), numpy
 """
 from __future__ import annotations
 
@@ -179,3 +186,30 @@ def check(y: np.ndarray, y_ref: np.ndarray, A: np.ndarray, rel: float = REL_TOL,
     worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape) if ratio.size else ()
     wr = float(ratio[worst]) if ratio.size else 0.0
     return bool(wr <= 1.0), wr, worst
+
+
+def logsumexp(y: np.ndarray) -> np.ndarray:
+    """y: float [T, M] -> float64 [T]: log(sum_i exp(y[t, i])), evaluated as
+    m + log(sum_i exp(y - m)) with m the row maximum (every term in (0, 1], no overflow)."""
+    y = np.asarray(y, dtype=np.float64)
+    if y.ndim != 2 or y.shape[1] == 0:
+        raise ValueError("y must be [T, M] with M >= 1")
+    m = y.max(axis=1)
+    return m + np.log(np.exp(y - m[:, None]).sum(axis=1))
+
+
+def topk(y: np.ndarray, k: int, index: Optional[np.ndarray] = None):
+    """y: float [T, M] -> (values float64 [T, k], ids int64 [T, k]): per token the k largest
+    values in descending order, equal values ordered by ascending row; ids are the rows, or
+    index[row] when an index is given.  Slots past M hold -inf and id -1."""
+    y = np.asarray(y, dtype=np.float64)
+    T, M = y.shape
+    vals = np.full((T, k), -np.inf)
+    ids = np.full((T, k), -1, dtype=np.int64)
+    rows = np.arange(M)
+    for t in range(T):
+        order = np.lexsort((rows, -y[t]))[:k]   # primary key -value, then row
+        n = order.size
+        vals[t, :n] = y[t, order]
+        ids[t, :n] = order if index is None else np.asarray(index, dtype=np.int64)[order]
+    return vals, ids

@@ -140,3 +140,26 @@ def config(name: str, T: Optional[int] = None, seed: int = 0) -> Workload:
 
 def config_names() -> List[str]:
     return list(CONFIGS)
+
+
+def logits(T: int, M: int, seed: int = 0, ties: bool = True) -> np.ndarray:
+    """Synthetic output-head logits, float32 [T, M]: N(0, 1) * 3 with a few large values
+    (draws: the values, then the positions and sizes of the large values); with ties, every
+    token also gets groups of exactly equal values among its largest (copies of its own
+    maximum and of other drawn values at random rows)."""
+    g = _gen(seed)
+    y = torch.randn((T, M), generator=g, dtype=torch.float32) * 3.0
+    nbig = max(1, M // 4096)
+    pos = torch.randint(0, M, (T, nbig), generator=g)
+    big = torch.rand((T, nbig), generator=g) * 12.0 + 8.0
+    y.scatter_(1, pos, big)
+    if ties:
+        npick = min(M, 8)
+        src = torch.randint(0, M, (T, npick), generator=g)
+        dst = torch.randint(0, M, (T, npick), generator=g)
+        vals = torch.gather(y, 1, src)
+        y.scatter_(1, dst, vals)
+        top = y.max(dim=1, keepdim=True).values
+        dst2 = torch.randint(0, M, (T, 2), generator=g)
+        y.scatter_(1, dst2, top.expand(T, 2))
+    return y.numpy()

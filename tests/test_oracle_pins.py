@@ -369,3 +369,57 @@ def test_check_flags_errors_beyond_tolerance():
     assert not ok and idx == (0, 2)
     ok, _, _ = oracle.check(np.array([[np.nan, -2.0, 0.0]]), y_ref, A)
     assert not ok
+
+
+# ------------------------------------------------------------------ head epilogue: log-sum-exp and top-k
+
+def test_logsumexp_closed_forms():
+    # a constant row: c + log M exactly; one dominant value: that value (the rest underflow
+    # relative to it); duplicating every value adds log 2
+    for M in (1, 7, 64, 1000):
+        for c in (0.0, -3.5, 41.0, 1e-3):
+            got = oracle.logsumexp(np.full((1, M), c))
+            assert abs(got[0] - (c + math.log(M))) <= 1e-15 * max(1.0, abs(c) + math.log(M))
+    y = np.array([[1000.0, 0.0, -5.0, 3.0]])
+    assert oracle.logsumexp(y)[0] == 1000.0
+    rng = np.random.default_rng(2)
+    z = rng.standard_normal((3, 77)) * 4
+    assert np.allclose(oracle.logsumexp(np.concatenate([z, z], axis=1)), oracle.logsumexp(z) + math.log(2),
+                       rtol=0, atol=1e-13)
+
+
+def test_logsumexp_matches_scipy_and_is_shift_equivariant():
+    # library cross-check (scipy.special.logsumexp), bounds max <= lse <= max + log M, and
+    # lse(y + c) = lse(y) + c
+    from scipy.special import logsumexp as sp_lse
+    y = qi.logits(5, 3000, 7).astype(np.float64)
+    got = oracle.logsumexp(y)
+    assert np.allclose(got, sp_lse(y, axis=1), rtol=0, atol=1e-12)
+    mx = y.max(axis=1)
+    assert np.all(got >= mx) and np.all(got <= mx + math.log(y.shape[1]))
+    assert np.allclose(oracle.logsumexp(y + 17.25), got + 17.25, rtol=0, atol=1e-12)
+
+
+def test_topk_brute_force_with_ties_and_index():
+    # brute force: Python's sort by (value descending, row ascending) on tiny rows full of
+    # ties, with and without an index map; k beyond M pads with (-inf, -1)
+    rng = np.random.default_rng(3)
+    for trial in range(40):
+        M = int(rng.integers(1, 40))
+        T = int(rng.integers(1, 4))
+        y = rng.integers(-3, 4, (T, M)).astype(np.float32) * 0.5
+        index = rng.permutation(10 * M)[:M] if trial % 2 else None
+        for k in (1, 3, 8, 45):
+            vals, ids = oracle.topk(y, k, index)
+            for t in range(T):
+                want = sorted(range(M), key=lambda r: (-float(y[t, r]), r))[:k]
+                n = len(want)
+                assert vals[t, :n].tolist() == [float(y[t, r]) for r in want]
+                assert ids[t, :n].tolist() == [int(index[r]) if index is not None else r for r in want]
+                assert np.all(vals[t, n:] == -np.inf) and np.all(ids[t, n:] == -1)
+
+
+def test_logits_generator_plants_ties():
+    y = qi.logits(4, 5000, 9)
+    for t in range(4):
+        assert np.sum(y[t] == y[t].max()) >= 2
