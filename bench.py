@@ -167,6 +167,39 @@ def measure(res, T, steps, warmup):
             "bytes": ab, "plan": plan_str(res, T)}
 
 
+def measure_epilogue(res, T, k, steps, warmup):
+    """The output-head epilogue (per-token log-sum-exp and top-k) on the logits the head product
+    left in res.y, graph-replayed; bytes are the logits read (T * M * 4)."""
+    import torch
+    import weight_only_quant_amd as wq
+    M = res.wl.M
+    e = wq.qmat_logits_create(M, T, k)
+    y = res.y[:T]
+    lse = torch.empty(T, device="cuda")
+    v = torch.empty((T, k), device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    del g
+    wq.qmat_logits_destroy(e)
+    nb = T * M * 4
+    return {"us_per_call": round(us, 3), "GBps": round(nb / us / 1e3, 1), "bytes": nb, "k": k}
+
+
 def cpu_baseline(res, T, target_s=12.0):
     """The CPU oracle (as it stands) on a bounded sample of the same workload: whole passes
     over all rows (or a row subset when one pass would exceed the budget), repeated until
@@ -313,6 +346,10 @@ def main():
                 steps = args.steps if r.wl.M * r.wl.K < 1e9 else max(50, args.steps // 4)
                 extra[f"{n}_T{T2}"] = measure(r, T2, steps, args.warmup)
                 log(f"[bench] {n} T={T2}: {extra[f'{n}_T{T2}']}")
+                if n == "q6_head_248320x5120":
+                    key = f"head_epilogue_lse_top20_248320_T{T2}"
+                    extra[key] = measure_epilogue(r, T2, 20, args.steps, 20)
+                    log(f"[bench] {key}: {extra[key]}")
             r.close()
             del r
             torch.cuda.empty_cache()

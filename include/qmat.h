@@ -164,6 +164,42 @@ size_t qmat_workspace_bytes(qmat_t handle);
 /* Release the handle and its workspace (not the packed matrix).  NULL is ignored. */
 void qmat_destroy(qmat_t handle);
 
+/* ---------------------------------------------------------------- output-head epilogue
+ *
+ * Per token, over fp32 logits y [T][M] (for example what qmat_run wrote for an output head):
+ *   lse[t]        = log sum_i exp(y[t][i])                        (the fork's "single-pass
+ *                   logsumexp": giveen/ninfer-ext README, upstream pull requests merged ahead)
+ *   top_vals[t][] = the k largest y[t][i], largest first; equal values by ascending row i
+ *   top_ids[t][]  = their rows i, or index[i] when an index map is given (the indexed 131,072-row
+ *                   proposal head whose rows stand for vocabulary ids; the candidate top-k reads
+ *                   either it or the full head: "Qwen3.8-27B for NInfer on the RTX 3090", run
+ *                   notes).  Slots beyond M hold (-inf, -1).
+ * One pass over y; the result is deterministic.  y must be finite. */
+typedef struct qmat_logits *qmat_logits_t;
+
+/* An epilogue handle for M rows, up to max_T tokens (1..16) and top-k up to max_k (0..64).  It
+ * owns a small device workspace (per token and block: two floats and max_k (value, row) pairs),
+ * allocated and zeroed here; calls sharing a handle must be ordered.
+ * Errors: QMAT_EINVAL (null pointer), QMAT_ESHAPE (M outside [1, 2^30], max_T, max_k),
+ * QMAT_ENOMEM, QMAT_EHIP. */
+int qmat_logits_create(qmat_logits_t *handle, int64_t M, int max_T, int max_k);
+
+/* Run the epilogue on the stream (asynchronous, no allocation, graph-capturable).
+ *   y_dev:        device fp32, row t at y_dev + t * ldy (ldy >= M), 4-byte aligned.
+ *   k:            0..max_k; 0 computes only lse.
+ *   index_dev:    device int32 [M] row -> id map, or NULL (ids are rows).
+ *   lse_dev:      device fp32 [T], or NULL (not computed).
+ *   top_vals_dev: device fp32 [T][k]; top_ids_dev: device int32 [T][k] (both required if k > 0).
+ * T == 0, or k == 0 with no lse output, is a no-op.
+ * Errors: QMAT_EINVAL (null handle / y / outputs, misaligned y), QMAT_ESHAPE (T, k, ldy),
+ * QMAT_EHIP (launch). */
+int qmat_logits_run(qmat_logits_t handle, const float *y_dev, int64_t ldy, int T, int k,
+                    const int32_t *index_dev, float *lse_dev, float *top_vals_dev,
+                    int32_t *top_ids_dev, void *stream);
+
+/* Release the handle and its workspace.  NULL is ignored. */
+void qmat_logits_destroy(qmat_logits_t handle);
+
 /* Message describing the calling thread's most recent error ("" if none). */
 const char *qmat_last_error(void);
 

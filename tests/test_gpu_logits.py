@@ -1,0 +1,180 @@
+"""GPU parity of the output-head epilogue (qmat_logits_*): per-token log-sum-exp and top-k
+over fp32 logits, against the oracle's float64 log-sum-exp and its sort by (value descending,
+row ascending).  The logits are oracle-side synthetic inputs (qmat_inputs.logits, with planted
+ties), so the top-k must match bit for bit; the log-sum-exp within the fp32 evaluation bound
+derived below.  An end-to-end case runs the Q6 product first and checks the epilogue against
+the oracle's float64 logits within the product tolerance.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qmat_inputs as qi
+import weight_only_quant_amd as wq
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    wq.lib()
+
+
+# fp32 evaluation bound of the log-sum-exp: each lane sums at most a few dozen terms, the
+# partial sums meet in <= 12 pairwise combinations, each term and each rescaling carries one
+# expf error (a few ulp), and the final log is taken in double: relative error of the sum
+# <= 64 * 2^-24 (about 4e-6), i.e. the same absolute error on lse, plus the final rounding
+# of lse to fp32 (2^-24 |lse|).
+def _lse_tol(ref):
+    return 64 * 2.0 ** -24 + 2.0 ** -23 * np.abs(ref)
+
+
+def _run(e, y, k, index=None, ldy_pad=0):
+    T, M = y.shape
+    yd = torch.zeros((T, M + ldy_pad), dtype=torch.float32, device="cuda")
+    yd[:, :M] = torch.from_numpy(y).cuda()
+    if ldy_pad:
+        yd[:, M:] = 1e30  # past the row: must never be read
+    lse = torch.full((T,), float("nan"), device="cuda")
+    vals = torch.full((T, max(k, 1)), float("nan"), device="cuda")
+    ids = torch.full((T, max(k, 1)), -7, dtype=torch.int32, device="cuda")
+    idx = None if index is None else torch.from_numpy(index.astype(np.int32)).cuda()
+    wq.qmat_logits_run(e, yd, k, lse=lse, top_vals=vals, top_ids=ids, index=idx)
+    torch.cuda.synchronize()
+    return lse.cpu().numpy(), vals.cpu().numpy()[:, :k], ids.cpu().numpy()[:, :k]
+
+
+@pytest.mark.parametrize("M", [1, 5, 63, 64, 1000, 4097, 70001, 248320])
+def test_lse_topk_exact_on_synthetic_logits(M):
+    e = wq.qmat_logits_create(M, 16, 64)
+    for T, k, seed, pad in [(1, 1, 1, 0), (3, 7, 2, 5), (8, 20, 3, 0), (16, 64, 4, 3), (2, 0, 5, 0)]:
+        say(f"logits M={M} T={T} k={k} pad={pad}")
+        y = qi.logits(T, M, seed=seed + M)
+        lse, vals, ids = _run(e, y, k, ldy_pad=pad)
+        ref = oracle.logsumexp(y)
+        assert np.all(np.abs(lse.astype(np.float64) - ref) <= _lse_tol(ref)), (lse, ref)
+        if k:
+            rv, ri = oracle.topk(y, k)
+            assert np.array_equal(vals.astype(np.float64), rv), (vals, rv)
+            assert np.array_equal(ids.astype(np.int64), ri), (ids, ri)
+    wq.qmat_logits_destroy(e)
+
+
+def test_topk_index_map_and_all_equal_values():
+    # the proposal-head shape with a row -> vocabulary id map; and a row of equal values,
+    # where the order is decided by the row alone
+    M = 131072
+    e = wq.qmat_logits_create(M, 8, 32)
+    rng = np.random.default_rng(0)
+    index = rng.permutation(248320)[:M].astype(np.int64)
+    y = qi.logits(4, M, seed=11)
+    say("logits proposal head with index")
+    lse, vals, ids = _run(e, y, 32, index=index)
+    rv, ri = oracle.topk(y, 32, index)
+    assert np.array_equal(vals.astype(np.float64), rv) and np.array_equal(ids.astype(np.int64), ri)
+    y = np.full((2, M), 0.25, np.float32)
+    lse, vals, ids = _run(e, y, 32, index=index)
+    assert np.array_equal(ids[0], index[:32].astype(np.int32))
+    assert abs(lse[0] - (0.25 + math.log(M))) <= _lse_tol(0.25 + math.log(M))
+    wq.qmat_logits_destroy(e)
+
+
+def test_repeated_calls_and_graph_replay_are_identical():
+    import gc
+    gc.collect()
+    M, T, k = 248320, 8, 20
+    e = wq.qmat_logits_create(M, T, k)
+    y = torch.from_numpy(qi.logits(T, M, seed=21)).cuda()
+    outs = []
+    for i in range(3):
+        lse = torch.empty(T, device="cuda")
+        v = torch.empty((T, k), device="cuda")
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
+        torch.cuda.synchronize()
+        outs.append((lse.clone(), v.clone(), ids.clone()))
+    for o in outs[1:]:
+        assert all(torch.equal(a, b) for a, b in zip(o, outs[0]))
+    lse = torch.empty(T, device="cuda")
+    v = torch.empty((T, k), device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
+    for i in range(3):
+        lse.fill_(float("nan"))
+        ids.fill_(-5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lse, outs[0][0]) and torch.equal(v, outs[0][1]) and torch.equal(ids, outs[0][2]), i
+        wq.qmat_logits_run(e, y, k, lse=torch.empty(T, device="cuda"), top_vals=torch.empty((T, k), device="cuda"),
+                           top_ids=torch.empty((T, k), dtype=torch.int32, device="cuda"))  # eager work between
+        torch.cuda.synchronize()
+    del g
+    wq.qmat_logits_destroy(e)
+
+
+def test_head_product_then_epilogue_end_to_end():
+    # Q6 head-like matrix: product on the GPU, epilogue on its logits, against the oracle's
+    # float64 logits.  lse is 1-Lipschitz in the max norm, so |lse - lse_ref| <= max_i tol_i
+    # (the product tolerance) plus the fp32 evaluation bound; each returned value is the
+    # GPU logit of the returned row, within tol of the oracle's; and no row left out beats the
+    # smallest returned one by more than twice the tolerance.
+    M, K, T, k = 9000, 512, 8, 16
+    wl = qi.groupwise("h", 6, M, K, T, 0.005, 5)
+    qm = wq.QMat(6, wl.codes, wl.scales)
+    xd = torch.from_numpy(wl.x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    y = qm.run(xd)
+    e = wq.qmat_logits_create(M, T, k)
+    lse = torch.empty(T, device="cuda")
+    v = torch.empty((T, k), device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gemv(6, wl.codes, wl.scales, wl.x)
+    tol = oracle.REL_TOL * A + oracle.ABS_TOL
+    lse_ref = oracle.logsumexp(y_ref)
+    got = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - lse_ref) <= tol.max(axis=1) + _lse_tol(lse_ref))
+    yg = y.cpu().numpy()
+    vv, ii = v.cpu().numpy(), ids.cpu().numpy()
+    for t in range(T):
+        assert len(set(ii[t].tolist())) == k
+        assert np.array_equal(vv[t], yg[t, ii[t]])
+        assert np.all(np.abs(vv[t] - y_ref[t, ii[t]]) <= tol[t, ii[t]])
+        rest = np.setdiff1d(np.arange(M), ii[t])
+        assert y_ref[t, rest].max() <= y_ref[t, ii[t]].min() + 2 * tol[t].max()
+    wq.qmat_logits_destroy(e)
+    qm.close()
+
+
+def test_epilogue_argument_errors():
+    e = wq.qmat_logits_create(100, 4, 8)
+    y = torch.zeros((4, 100), device="cuda")
+    v = torch.empty((4, 8), device="cuda")
+    ids = torch.empty((4, 8), dtype=torch.int32, device="cuda")
+    for kw, status in [(dict(k=9), wq.QMAT_ESHAPE), (dict(k=-1), wq.QMAT_ESHAPE), (dict(k=2, T=5), wq.QMAT_ESHAPE)]:
+        with pytest.raises(wq.QmatError) as err:
+            wq.qmat_logits_run(e, y, top_vals=v, top_ids=ids, **kw)
+        assert err.value.status == status, kw
+    with pytest.raises(wq.QmatError) as err:
+        wq.qmat_logits_run(e, y, 2)  # k > 0 without outputs
+    assert err.value.status == wq.QMAT_EINVAL
+    assert wq.lib().qmat_logits_run(e, y.data_ptr(), 50, 1, 2, None, None, v.data_ptr(), ids.data_ptr(),
+                                    None) == wq.QMAT_ESHAPE  # ldy < M
+    wq.qmat_logits_run(e, y, 0, T=0)  # no-op
+    wq.qmat_logits_destroy(e)
+    for args in [(0, 4, 8), (100, 0, 8), (100, 17, 8), (100, 4, 65)]:
+        with pytest.raises(wq.QmatError) as err:
+            wq.qmat_logits_create(*args)
+        assert err.value.status == wq.QMAT_ESHAPE, args

@@ -38,6 +38,9 @@ SIGNATURES = {
     "qmat_workspace_bytes": (_sz, [_vp]),
     "qmat_destroy": (None, [_vp]),
     "qmat_last_error": (ctypes.c_char_p, []),
+    "qmat_logits_create": (_int, [ctypes.POINTER(_vp), _i64, _int, _int]),
+    "qmat_logits_run": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp]),
+    "qmat_logits_destroy": (None, [_vp]),
 }
 
 
@@ -168,6 +171,28 @@ def qmat_workspace_bytes(handle: int) -> int:
 def qmat_destroy(handle: Optional[int]) -> None:
     if handle:
         lib().qmat_destroy(handle)
+
+
+def qmat_logits_create(M: int, max_T: int, max_k: int) -> int:
+    """Epilogue handle for M logit rows, up to max_T tokens and top-k up to max_k."""
+    h = ctypes.c_void_p()
+    _check(lib().qmat_logits_create(ctypes.byref(h), M, max_T, max_k))
+    return h.value
+
+
+def qmat_logits_run(handle: int, y, k: int, lse=None, top_vals=None, top_ids=None, index=None,
+                    T: Optional[int] = None, stream=None) -> None:
+    """y: fp32 device [T, >= M] (row stride y.stride(0)); lse fp32 [T]; top_vals fp32 [T, k];
+    top_ids int32 [T, k]; index int32 [M] or None."""
+    T = y.shape[0] if T is None else T
+    ptr = lambda a: None if a is None else a.data_ptr()
+    _check(lib().qmat_logits_run(handle, y.data_ptr(), y.stride(0), T, k, ptr(index), ptr(lse), ptr(top_vals),
+                                 ptr(top_ids), _stream_handle(stream)))
+
+
+def qmat_logits_destroy(handle: Optional[int]) -> None:
+    if handle:
+        lib().qmat_logits_destroy(handle)
 
 
 class QMat:

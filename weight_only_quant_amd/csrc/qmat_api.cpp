@@ -13,6 +13,7 @@
 #include "../../include/qmat.h"
 #include "qmat_kernels.h"
 #include "qmat_layout.h"
+#include "qmat_logits.h"
 
 using namespace qmatk;
 
@@ -555,5 +556,97 @@ void qmat_destroy(qmat_t h)
 }
 
 const char *qmat_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------------ head epilogue
+
+}  // extern "C"
+
+struct qmat_logits {
+    int64_t M;
+    int max_T, max_k, B, rpb;
+    float *part_f;
+    int32_t *part_i;
+    uint32_t *counter;
+};
+
+extern "C" {
+
+int qmat_logits_create(qmat_logits_t *e, int64_t M, int max_T, int max_k)
+{
+    if (!e) return fail(QMAT_EINVAL, "qmat_logits_create: null handle pointer");
+    *e = nullptr;
+    if (M < 1 || M > (1LL << 30)) return fail(QMAT_ESHAPE, "qmat_logits_create: M=%lld outside [1, 2^30]", (long long)M);
+    if (max_T < 1 || max_T > kMaxT) return fail(QMAT_ESHAPE, "qmat_logits_create: max_T=%d outside [1,%d]", max_T, kMaxT);
+    if (max_k < 0 || max_k > 64) return fail(QMAT_ESHAPE, "qmat_logits_create: max_k=%d outside [0,64]", max_k);
+    qmat_logits *h = new (std::nothrow) qmat_logits;
+    if (!h) return fail(QMAT_ENOMEM, "qmat_logits_create: out of host memory");
+    h->M = M;
+    h->max_T = max_T;
+    h->max_k = max_k;
+    h->B = logits_blocks(M);
+    h->rpb = (int)((M + h->B - 1) / h->B);
+    h->part_f = nullptr;
+    h->part_i = nullptr;
+    h->counter = nullptr;
+    const size_t nf = (size_t)max_T * h->B * (2 + max_k), ni = (size_t)max_T * h->B * (max_k > 0 ? max_k : 1);
+    if (hipMalloc(&h->part_f, nf * sizeof(float)) != hipSuccess ||
+        hipMalloc(&h->part_i, ni * sizeof(int32_t)) != hipSuccess ||
+        hipMalloc(&h->counter, (size_t)max_T * sizeof(uint32_t)) != hipSuccess) {
+        (void)hipGetLastError();
+        if (h->part_f) (void)hipFree(h->part_f);
+        if (h->part_i) (void)hipFree(h->part_i);
+        delete h;
+        return fail(QMAT_ENOMEM, "qmat_logits_create: workspace allocation failed");
+    }
+    if (hipMemset(h->counter, 0, (size_t)max_T * sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(h->part_f);
+        (void)hipFree(h->part_i);
+        (void)hipFree(h->counter);
+        delete h;
+        return fail(QMAT_EHIP, "qmat_logits_create: counter initialisation failed");
+    }
+    *e = h;
+    return ok();
+}
+
+int qmat_logits_run(qmat_logits_t e, const float *y_dev, int64_t ldy, int T, int k, const int32_t *index_dev,
+                    float *lse_dev, float *top_vals_dev, int32_t *top_ids_dev, void *stream)
+{
+    if (!e) return fail(QMAT_EINVAL, "qmat_logits_run: null handle");
+    if (T < 0 || T > e->max_T) return fail(QMAT_ESHAPE, "qmat_logits_run: T=%d outside [0,%d]", T, e->max_T);
+    if (k < 0 || k > e->max_k) return fail(QMAT_ESHAPE, "qmat_logits_run: k=%d outside [0,%d]", k, e->max_k);
+    if (T == 0 || (k == 0 && !lse_dev)) return ok();
+    if (!y_dev) return fail(QMAT_EINVAL, "qmat_logits_run: null y");
+    if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_logits_run: y not 4-byte aligned");
+    if (ldy < e->M) return fail(QMAT_ESHAPE, "qmat_logits_run: ldy=%lld < M=%lld", (long long)ldy, (long long)e->M);
+    if (k > 0 && (!top_vals_dev || !top_ids_dev)) return fail(QMAT_EINVAL, "qmat_logits_run: null top-k output");
+    LogitsArgs a;
+    a.y = y_dev;
+    a.ldy = ldy;
+    a.M = (int)e->M;
+    a.T = T;
+    a.k = k;
+    a.index = index_dev;
+    a.lse = lse_dev;
+    a.vals = top_vals_dev;
+    a.ids = top_ids_dev;
+    a.part_f = e->part_f;
+    a.part_i = e->part_i;
+    a.counter = e->counter;
+    a.B = e->B;
+    a.rpb = e->rpb;
+    const hipError_t err = launch_logits(a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(QMAT_EHIP, "qmat_logits_run: launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+void qmat_logits_destroy(qmat_logits_t e)
+{
+    if (!e) return;
+    (void)hipFree(e->part_f);
+    (void)hipFree(e->part_i);
+    (void)hipFree(e->counter);
+    delete e;
+}
 
 }  // extern "C"
