@@ -18,6 +18,10 @@ Functions and the definitions they follow (NInfer model cards):
   dequant_fp8         "Qwen3.8-27B NVFP4 for NInfer" / "Artifact": row-scaled FP8
   gemv                y = x W^T in double, plus A = sum |w x|
   rtn_encode          the upstream round-to-nearest encoder (scale = absmax / qmax)
+  grouped_search_encode  the card's encoder: FP16 scale searched over 50 candidates (both
+                      signs) for the least importance-weighted squared error
+  float_to_e4m3 / fp8_row_encode  E4M3 nearest-even (saturating) and the row-scaled FP8
+                      encoding (r = absmax / 448)
   check               the acceptance test |y - y_ref| <= 1e-4 * A + 1e-6
   logsumexp           log sum_i exp(y_i) per token over the output-head logits (the fork's
                       "single-pass logsumexp": giveen/ninfer-ext README, upstream pull
@@ -79,6 +83,12 @@ def lib():
         L.qo_gemv.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, i64, vp, vp, i32]
         L.qo_rtn_encode.restype = i32
         L.qo_rtn_encode.argtypes = [i32, i64, vp, vp, vp]
+        L.qo_grouped_search_encode.restype = i32
+        L.qo_grouped_search_encode.argtypes = [i32, i64, vp, vp, vp, vp]
+        L.qo_float_to_e4m3_rne_sat.restype = ctypes.c_uint8
+        L.qo_float_to_e4m3_rne_sat.argtypes = [ctypes.c_float]
+        L.qo_fp8_row_encode.restype = i32
+        L.qo_fp8_row_encode.argtypes = [i64, i64, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -213,3 +223,31 @@ def topk(y: np.ndarray, k: int, index: Optional[np.ndarray] = None):
         vals[t, :n] = y[t, order]
         ids[t, :n] = order if index is None else np.asarray(index, dtype=np.int64)[order]
     return vals, ids
+
+
+def grouped_search_encode(bits: int, w: np.ndarray, h: np.ndarray):
+    """w, h: float64 [ngroups, 64] (h = per-channel importance of each group's columns)
+    -> (codes int8 [ngroups, 64], scale bits uint16 [ngroups])."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    n = w.shape[0]
+    if w.shape != (n, 64) or h.shape != (n, 64):
+        raise ValueError("w and h must be [ngroups, 64]")
+    codes = np.empty((n, 64), dtype=np.int8)
+    scales = np.empty((n,), dtype=np.uint16)
+    _check(lib().qo_grouped_search_encode(bits, n, _ptr(w), _ptr(h), _ptr(codes), _ptr(scales)), "grouped_search")
+    return codes, scales
+
+
+def float_to_e4m3(q: float) -> int:
+    return int(lib().qo_float_to_e4m3_rne_sat(float(q)))
+
+
+def fp8_row_encode(w: np.ndarray):
+    """w: float32 [M, K] -> (E4M3 bytes uint8 [M, K], row scales float32 [M])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    M, K = w.shape
+    b = np.empty((M, K), dtype=np.uint8)
+    r = np.empty((M,), dtype=np.float32)
+    _check(lib().qo_fp8_row_encode(M, K, _ptr(w), _ptr(b), _ptr(r)), "fp8_row_encode")
+    return b, r

@@ -346,3 +346,134 @@ int qo_rtn_encode(int bits, int64_t ngroups, const double *w, int8_t *codes, uin
     }
     return QO_OK;
 }
+
+/* ---------------------------------------------------------------- grouped search encoder */
+
+/* The "grouped_search" encoder of "Qwen3.8-27B for NInfer on the RTX 3090" ("What is
+ * different from the upstream artifact"): each group's FP16 scale is chosen among 50
+ * candidates as the one with the least importance-weighted squared error
+ * sum_j h_j (w_j - s c_j)^2, where h_j is the importance of input channel j (the mean squared
+ * activation of that channel: an imatrix); scales may be negative, which lets a group use the
+ * most negative code.
+ *
+ * The page does not list the candidates.  Reading: with a = max_j |w_j|, the 25 magnitudes
+ * a / (qmax + i/24), i = 0..24, run from upstream's a/qmax (the group's largest weight lands
+ * on +-qmax) to a/2^(b-1) (it lands on +-2^(b-1), the full range), each with both signs:
+ * candidate order +m_0, -m_0, +m_1, -m_1, ...  Each candidate is rounded once to FP16
+ * (nearest-even), codes are the nearest integers to w/s (half to even) clamped to the code
+ * range, the error is evaluated in double in index order, and the first candidate with the
+ * smallest error wins.  An all-zero group gets scale +0 and codes 0; QO_ERANGE if a/qmax
+ * overflows FP16.  w and h: [ngroups][64] doubles (h >= 0). */
+int qo_grouped_search_encode(int bits, int64_t ngroups, const double *w, const double *h, int8_t *codes,
+                             uint16_t *scales)
+{
+    if (!bits_ok(bits) || ngroups < 0)
+        return QO_EINVAL;
+    const int qmax = (1 << (bits - 1)) - 1, qmin = -(1 << (bits - 1));
+    for (int64_t g = 0; g < ngroups; ++g) {
+        const double *wg = w + g * 64, *hg = h + g * 64;
+        double a = 0.0;
+        for (int j = 0; j < 64; ++j) {
+            if (!isfinite(wg[j]) || !isfinite(hg[j]) || hg[j] < 0)
+                return QO_ERANGE;
+            if (fabs(wg[j]) > a)
+                a = fabs(wg[j]);
+        }
+        if (a == 0.0) {
+            scales[g] = 0;
+            for (int j = 0; j < 64; ++j)
+                codes[g * 64 + j] = 0;
+            continue;
+        }
+        if ((qo_double_to_half_rne(a / (double)qmax) & 0x7c00) == 0x7c00)
+            return QO_ERANGE;
+        double best_err = INFINITY;
+        uint16_t best_sb = 0;
+        int8_t best_c[64];
+        for (int cand = 0; cand < 50; ++cand) {
+            const int i = cand / 2;
+            const double mag = a / ((double)qmax + (double)i / 24.0);
+            const uint16_t sb = qo_double_to_half_rne(cand % 2 ? -mag : mag);
+            const double s = qo_half_to_double(sb);
+            int8_t c[64];
+            double err = 0.0;
+            for (int j = 0; j < 64; ++j) {
+                double q = (s == 0.0) ? 0.0 : rint(wg[j] / s);
+                if (q > qmax)
+                    q = qmax;
+                if (q < qmin)
+                    q = qmin;
+                c[j] = (int8_t)q;
+                const double d = wg[j] - s * q;
+                err += hg[j] * (d * d);
+            }
+            if (err < best_err) {
+                best_err = err;
+                best_sb = sb;
+                memcpy(best_c, c, sizeof(c));
+            }
+        }
+        scales[g] = best_sb;
+        memcpy(codes + g * 64, best_c, sizeof(best_c));
+    }
+    return QO_OK;
+}
+
+/* ---------------------------------------------------------------- row-scaled FP8 encoder */
+
+/* float -> OCP E4M3 byte, round to nearest even, saturating at +-448 (the FN variant has no
+ * infinity; NaN input is not allowed).  Subnormals (exponent field 0) have quantum 2^-9. */
+uint8_t qo_float_to_e4m3_rne_sat(float q)
+{
+    uint8_t sign = signbit(q) ? 0x80 : 0;
+    double a = fabs((double)q);
+    if (a >= 448.0)
+        return sign | 0x7e;
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2); /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;
+    if (E < -6) {
+        double n = rint(ldexp(a, 9)); /* multiples of 2^-9; 8 is the smallest normal */
+        return sign | (uint8_t)n;
+    }
+    double n = rint(ldexp(a, 3 - E)); /* in [8, 16] */
+    if (n == 16.0) {
+        n = 8.0;
+        E += 1;
+    }
+    if (E > 8 || (E == 8 && n > 14.0))
+        return sign | 0x7e; /* beyond 448 after rounding */
+    return sign | (uint8_t)(((E + 7) << 3) | ((int)n - 8));
+}
+
+/* Row-scaled FP8 encoding ("Qwen3.8-27B NVFP4 for NInfer", "Artifact": a tensor encoded
+ * locally as row-scaled FP8; the method is not given).  Reading: r = fl32(a / 448) with a the
+ * row's largest |w|, each byte the nearest E4M3 value (even ties, saturating) to fl32(w / r);
+ * an all-zero row gets r = 0 and zero bytes.  w: float [M][K]. */
+int qo_fp8_row_encode(int64_t M, int64_t K, const float *w, uint8_t *bytes, float *r)
+{
+    if (M < 0 || K <= 0)
+        return QO_EINVAL;
+    for (int64_t i = 0; i < M; ++i) {
+        float a = 0.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            if (!isfinite(w[i * K + j]))
+                return QO_ERANGE;
+            if (fabsf(w[i * K + j]) > a)
+                a = fabsf(w[i * K + j]);
+        }
+        const float ri = (float)((double)a / 448.0);
+        r[i] = ri;
+        for (int64_t j = 0; j < K; ++j) {
+            if (ri == 0.0f) {
+                bytes[i * K + j] = 0;
+                continue;
+            }
+            const float q = w[i * K + j] / ri;
+            bytes[i * K + j] = qo_float_to_e4m3_rne_sat(q);
+        }
+    }
+    return QO_OK;
+}

@@ -423,3 +423,116 @@ def test_logits_generator_plants_ties():
     y = qi.logits(4, 5000, 9)
     for t in range(4):
         assert np.sum(y[t] == y[t].max()) >= 2
+
+
+# ------------------------------------------------------------------ encoders
+
+def test_e4m3_encoder_round_trips_and_matches_torch():
+    # every finite E4M3 value encodes to its own byte; a dense sweep of in-range floats
+    # (|q| < 464, where torch's nearest-even conversion does not produce NaN) matches torch;
+    # beyond 448 the encoder saturates
+    for b in range(256):
+        if (b & 0x7F) == 0x7F:
+            continue
+        v = oracle.e4m3_to_double(b)
+        assert oracle.float_to_e4m3(v) == b, hex(b)
+    rng = np.random.default_rng(0)
+    q = np.concatenate([rng.uniform(-463.9, 463.9, 20000), rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 6, 20000),
+                        (np.arange(-2000, 2001) * 2.0 ** -10)]).astype(np.float32)
+    ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.float_to_e4m3(float(v)) for v in q], np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(q[i], hex(got[i]), hex(ref[i])) for i in bad[:5]]
+    for v, b in [(448.0, 0x7E), (463.9, 0x7E), (470.0, 0x7E), (1e30, 0x7E), (-5000.0, 0xFE), (-0.0, 0x80)]:
+        assert oracle.float_to_e4m3(v) == b, v
+
+
+def test_fp8_row_encode_properties():
+    rng = np.random.default_rng(1)
+    w = (rng.standard_normal((40, 192)) * np.exp(rng.uniform(-6, 3, (40, 1)))).astype(np.float32)
+    w[3] = 0.0
+    b, r = oracle.fp8_row_encode(w)
+    assert r[3] == 0 and np.all(b[3] == 0)
+    dec = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    a = np.abs(w).max(axis=1)
+    assert np.array_equal(r, (a.astype(np.float64) / 448.0).astype(np.float32))
+    for i in range(40):
+        if a[i] == 0:
+            continue
+        # the row's largest magnitude lands on +-448; every value is within half an E4M3
+        # quantum (relative 2^-4, or 2^-10 absolute among subnormals) of w / r
+        j = int(np.abs(w[i]).argmax())
+        assert abs(dec[i, j]) == 448.0
+        q = (w[i] / r[i]).astype(np.float64)
+        assert np.all(np.abs(dec[i] - q) <= np.maximum(np.abs(q) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-9))
+
+
+def _gs_error(w, h, s, c):
+    return float(np.sum(h * (w - s * c) ** 2))
+
+
+def test_grouped_search_golden_case():
+    spec = json.load(open(os.path.join(GOLDEN, "grouped_search_worked.json")))
+    for case in spec["cases"]:
+        w = np.zeros((1, 64))
+        w[0, :len(case["w_head"])] = case["w_head"]
+        h = np.ones((1, 64))
+        codes, sb = oracle.grouped_search_encode(case["bits"], w, h)
+        assert int(sb[0]) == int(case["scale_bits"], 16)
+        assert codes[0, :3].tolist() == case["codes_head"] and not codes[0, 3:].any()
+        rc, rsb = oracle.rtn_encode(case["bits"], w)
+        assert int(rsb[0]) == int(case["rtn_scale_bits"], 16) and rc[0, :3].tolist() == case["rtn_codes_head"]
+        rs = float(np.uint16(rsb[0]).view(np.float16))
+        assert abs(_gs_error(w[0], h[0], rs, rc[0]) - case["rtn_error"]) < 1e-7
+
+
+@pytest.mark.parametrize("bits", [4, 5, 6, 8])
+def test_grouped_search_is_the_best_candidate_and_never_worse_than_rtn(bits):
+    # brute force over the 50 candidates with numpy's float16 rounding: the chosen scale has
+    # the smallest weighted error (first of equals); RTN's scale is candidate 0, so the search
+    # is never worse than RTN; codes stay in range; some groups choose negative scales
+    rng = np.random.default_rng(bits)
+    n = 120
+    w = rng.standard_normal((n, 64)) * np.exp(rng.uniform(-5, 2, (n, 1)))
+    w[0] = 0.0
+    h = rng.exponential(1.0, (n, 64)) * (rng.random((n, 64)) < 0.9)
+    codes, sb = oracle.grouped_search_encode(bits, w, h)
+    rc, rsb = oracle.rtn_encode(bits, w)
+    qmax, qmin = (1 << (bits - 1)) - 1, -(1 << (bits - 1))
+    assert codes.min() >= qmin and codes.max() <= qmax
+    assert sb[0] == 0 and not codes[0].any()
+    s = sb.view(np.float16).astype(np.float64)
+    negs = 0
+    for g in range(1, n):
+        a = np.abs(w[g]).max()
+        errs = []
+        for cand in range(50):
+            i = cand // 2
+            mag = a / (qmax + i / 24.0)
+            sc = float(np.float16(-mag if cand % 2 else mag))
+            c = np.clip(np.rint(w[g] / sc), qmin, qmax) if sc != 0 else np.zeros(64)
+            errs.append(_gs_error(w[g], h[g], sc, c))
+        best = int(np.argmin(errs))
+        assert s[g] == float(np.float16(-(a / (qmax + (best // 2) / 24.0)) if best % 2 else a / (qmax + (best // 2) / 24.0)))
+        assert _gs_error(w[g], h[g], s[g], codes[g]) == errs[best]
+        rs = float(np.uint16(rsb[g]).view(np.float16))
+        assert errs[best] <= _gs_error(w[g], h[g], rs, rc[g])
+        negs += s[g] < 0
+    assert negs > 0
+
+
+def test_grouped_search_recovers_full_range_groups_exactly():
+    # a group s*c whose codes use -2^(b-1), with s a power of two: the negative-sign candidate
+    # -a/2^(b-1) reproduces it with zero error (RTN cannot)
+    rng = np.random.default_rng(7)
+    for bits in (4, 5, 6, 8):
+        qmax, qmin = (1 << (bits - 1)) - 1, -(1 << (bits - 1))
+        for e in (-12, -3, 0, 4):
+            c = rng.integers(qmin + 1, qmax + 1, 64)
+            c[rng.integers(64)] = qmin
+            sgn = 1 if rng.random() < 0.5 else -1
+            w = (sgn * 2.0 ** e * c)[None, :].astype(np.float64)
+            codes, sb = oracle.grouped_search_encode(bits, w, np.ones((1, 64)))
+            s = float(np.uint16(sb[0]).view(np.float16))
+            assert _gs_error(w[0], np.ones(64), s, codes[0]) == 0.0
+            assert np.array_equal(s * codes[0].astype(np.float64), w[0])
