@@ -89,6 +89,37 @@ size_t qmat_packed_bytes(int fmt, int64_t M, int64_t K);
 int qmat_pack(int fmt, int64_t M, int64_t K, const void *codes, const void *scales, void *out,
               size_t out_bytes);
 
+typedef enum {
+    QMAT_ENCODE_RTN = 0,            /* upstream: scale = max|w| / qmax, nearest codes (FP8: the
+                                       row maximum maps to 448) */
+    QMAT_ENCODE_GROUPED_SEARCH = 1  /* groupwise only: FP16 scale searched over 50 candidates of
+                                       both signs for the least importance-weighted error */
+} qmat_encoder;
+
+/* Quantize fp32 weights w [M][K] (host) into the logical arrays qmat_pack takes.  Host only;
+ * pure; thread-safe.
+ *  Groupwise (Q4, Q5, Q6, Q8), per 64-weight group along K, a = max |w| of the group:
+ *   - QMAT_ENCODE_RTN, upstream's encoder ("Qwen3.8-27B for NInfer on the RTX 3090", "What is
+ *     different from the upstream artifact"): scale = FP16(a / qmax), code = nearest integer
+ *     to w / scale, clamped to [-2^(b-1), qmax] (qmax = 2^(b-1) - 1).
+ *   - QMAT_ENCODE_GROUPED_SEARCH, that artifact's encoder (same section): the FP16 scale is the
+ *     candidate with the least sum_j importance[k_j] * (w_j - scale * code_j)^2 among the 50
+ *     candidates +-a / (qmax + i/24), i = 0..24 (ordered +, - for each i; the first of equal
+ *     errors wins), with codes taken against each candidate as for RTN.  Negative scales let a
+ *     group reach the most negative code.  importance: float [K] per input channel (the mean
+ *     squared activation of that channel, an imatrix), finite and >= 0; NULL means all 1.
+ *   Every FP16 scale is rounded once (nearest-even) from the double quotient; codes round half
+ *   to even.  An all-zero group gets scale +0 and codes 0.
+ *   Outputs: codes int8 [M][K], scales uint16 binary16 bits [M][K/64].
+ *  Row-scaled FP8: QMAT_ENCODE_RTN only.  r = fl32(a / 448) with a the row's max |w|; each byte
+ *   is the E4M3 value nearest (even ties, saturating at +-448) to fl32(w / r); an all-zero row
+ *   gets r = 0 and zero bytes.  Outputs: codes uint8 [M][K], scales float [M].
+ * Errors: QMAT_EINVAL (format, encoder, null pointer, FP8 with the grouped search),
+ * QMAT_ESHAPE (M, K), QMAT_ERANGE (non-finite weight or importance, negative importance, a
+ * group whose a / qmax overflows FP16). */
+int qmat_quantize(int fmt, int64_t M, int64_t K, const float *w, const float *importance, int encoder,
+                  void *codes_out, void *scales_out);
+
 /* Create a handle over a packed matrix already in device memory.
  *   packed_dev: device pointer to qmat_pack's output (bytes == qmat_packed_bytes, 16-byte
  *               aligned).  Borrowed: it must outlive the handle and is never written.

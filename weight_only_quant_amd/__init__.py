@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libqmat.so")
 QMAT_OK, QMAT_EINVAL, QMAT_ESHAPE, QMAT_ERANGE, QMAT_ESIZE, QMAT_EHIP, QMAT_ENOMEM = range(7)
 QMAT_Q4, QMAT_Q5, QMAT_Q6, QMAT_FP8_E4M3_ROW, QMAT_Q8 = 4, 5, 6, 8, 9
 QMAT_ROUTE_AUTO, QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA = 0, 1, 2
+QMAT_ENCODE_RTN, QMAT_ENCODE_GROUPED_SEARCH = 0, 1
 FORMATS = (QMAT_Q4, QMAT_Q5, QMAT_Q6, QMAT_FP8_E4M3_ROW, QMAT_Q8)
 MAX_T = 16
 
@@ -28,6 +29,7 @@ _i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_s
 SIGNATURES = {
     "qmat_packed_bytes": (_sz, [_int, _i64, _i64]),
     "qmat_pack": (_int, [_int, _i64, _i64, _vp, _vp, _vp, _sz]),
+    "qmat_quantize": (_int, [_int, _i64, _i64, _vp, _vp, _int, _vp, _vp]),
     "qmat_create": (_int, [ctypes.POINTER(_vp), _int, _i64, _i64, _vp, _sz]),
     "qmat_create_view": (_int, [ctypes.POINTER(_vp), _vp, _i64, _i64]),
     "qmat_run": (_int, [_vp, _vp, _vp, _int, _vp]),
@@ -108,6 +110,26 @@ def qmat_pack(fmt: int, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     out = np.empty(max(n, 1), dtype=np.uint8)
     _check(lib().qmat_pack(fmt, M, K, codes.ctypes.data, scales.ctypes.data, out.ctypes.data, n))
     return out[:n]
+
+
+def qmat_quantize(fmt: int, w: np.ndarray, importance: Optional[np.ndarray] = None,
+                  encoder: int = QMAT_ENCODE_RTN):
+    """Host encoder: float32 w [M, K] -> (codes, scales) as qmat_pack takes them
+    (groupwise: int8 [M, K], uint16 [M, K/64]; FP8: uint8 [M, K], float32 [M])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D [M, K]")
+    M, K = w.shape
+    imp = None if importance is None else np.ascontiguousarray(importance, dtype=np.float32)
+    if imp is not None and imp.shape != (K,):
+        raise ValueError("importance must be [K]")
+    if fmt == QMAT_FP8_E4M3_ROW:
+        codes, scales = np.empty((M, K), np.uint8), np.empty((M,), np.float32)
+    else:
+        codes, scales = np.empty((M, K), np.int8), np.empty((M, max(K // 64, 1)), np.uint16)
+    _check(lib().qmat_quantize(fmt, M, K, w.ctypes.data, None if imp is None else imp.ctypes.data, encoder,
+                               codes.ctypes.data, scales.ctypes.data))
+    return codes, scales
 
 
 def qmat_create(fmt: int, M: int, K: int, packed_dev) -> int:

@@ -11,15 +11,18 @@
 #include <vector>
 
 #include "../../include/qmat.h"
+#include "qmat_host.h"
 #include "qmat_kernels.h"
 #include "qmat_layout.h"
 #include "qmat_logits.h"
 
 using namespace qmatk;
 
-namespace {
+namespace qmath {
 
+namespace {
 thread_local char g_err[512] = "";
+}
 
 int fail(int status, const char *fmt, ...)
 {
@@ -35,6 +38,24 @@ int ok()
     g_err[0] = '\0';
     return QMAT_OK;
 }
+
+const char *last_error() { return g_err; }
+
+unsigned host_threads(int64_t n)
+{
+    unsigned nth = std::thread::hardware_concurrency();
+    if (nth == 0) nth = 1;
+    if (nth > 16) nth = 16;
+    if ((int64_t)nth > n) nth = n > 0 ? (unsigned)n : 1u;
+    return nth;
+}
+
+}  // namespace qmath
+
+using qmath::fail;
+using qmath::ok;
+
+namespace {
 
 // M and K limits keep every kernel index inside 32-bit tile/unit counts and 64-bit offsets.
 bool shape_ok(int64_t M, int64_t K)
@@ -293,10 +314,7 @@ int qmat_pack(int fmt, int64_t M, int64_t K, const void *codes, const void *scal
     }
     uint8_t *o = static_cast<uint8_t *>(out);
     const int64_t NT = num_tiles(M);
-    unsigned nth = std::thread::hardware_concurrency();
-    if (nth == 0) nth = 1;
-    if (nth > 16) nth = 16;
-    if ((int64_t)nth > NT) nth = (unsigned)NT;
+    const unsigned nth = qmath::host_threads(NT);
     auto work = [&](unsigned k) {
         for (int64_t t = (int64_t)k; t < NT; t += nth) pack_tile(p, t, o);
     };
@@ -555,7 +573,7 @@ void qmat_destroy(qmat_t h)
     delete h;
 }
 
-const char *qmat_last_error(void) { return g_err; }
+const char *qmat_last_error(void) { return qmath::last_error(); }
 
 // ------------------------------------------------------------------ head epilogue
 
