@@ -21,10 +21,11 @@ struct LogitsArgs {
     int B, rpb;             // blocks per token, rows per block
 };
 
-// Blocks per token for M rows (each block streams about 2048 rows).
+// Blocks per token for M rows (each block of 16 waves streams about 4096 rows: one round of
+// four 64-row loads per wave).
 inline int logits_blocks(int64_t M)
 {
-    int64_t b = (M + 2047) / 2048;
+    int64_t b = (M + 4095) / 4096;
     return (int)(b < 1 ? 1 : b > 512 ? 512 : b);
 }
 

@@ -8,14 +8,16 @@
 // "Qwen3.8-27B EXL3", the indexed proposal head).  Here the epilogue is format-independent: it
 // reads the logits any qmat product wrote, and maps rows through an optional index.
 //
-// Work split: grid (B, T); block b of token t streams rows [b*rpb, (b+1)*rpb) with 4 waves.
+// Work split: grid (B, T); block b of token t streams rows [b*rpb, (b+1)*rpb) with 16 waves.
 // Each lane keeps an online (max, sum of exp(y - max)); each wave keeps its 64 best (value, row)
-// pairs sorted across its lanes (lane i holds the i-th best) and merges a 64-row chunk into that
-// list only when some lane beats the current k-th best (a bitonic sort of the chunk and a
-// bitonic merge, all in registers through lane shuffles).  The block's four waves combine in
-// LDS; the block publishes (max, sum, k best) to the workspace, and the last block of the token
-// to arrive (arrival counter, reset by that block) merges the B partials in block order:
-// deterministic output, no memset between calls.
+// pairs sorted across its lanes (lane i holds the i-th best).  Each lane first orders its four
+// rows of a round; the round then enters the list as four 64-pair chunks (every lane's best, then
+// every lane's second, ...), each costing one compare against the current k-th best and a wave
+// vote, and only when some lane beats it a bitonic sort (DPP / swizzle / half-swap lane
+// exchanges) and merge.  Comparisons are branch-free selects.  The block's 16 lists merge in a fixed pairwise tree; the block publishes
+// (max, sum, k best) to the workspace, and the last block of the token to arrive (arrival
+// counter, reset by that block) merges the B partials the same way, with the log-sum-exp
+// states combined in double in a fixed order: deterministic output, no memset between calls.
 //
 // Order: value descending, equal values by ascending row.  Empty slots are (-inf, INT_MAX).
 #include <hip/hip_runtime.h>
@@ -30,34 +32,72 @@ namespace {
 
 constexpr int kRowEmpty = 0x7FFFFFFF;
 
+// (v1, r1) ranks before (v2, r2).  Bitwise, not short-circuit, operators: the comparisons
+// stay lane masks and selects instead of becoming divergent branches.
 __device__ __forceinline__ bool better(float v1, int r1, float v2, int r2)
 {
-    return v1 > v2 || (v1 == v2 && r1 < r2);
+    return (v1 > v2) | ((v1 == v2) & (r1 < r2));
 }
 
-// one compare-exchange step between lanes `lane` and `lane ^ stride`; keep_better selects
-// which of the two this lane keeps
-__device__ __forceinline__ void cmpx(float &v, int &r, int stride, bool keep_better)
+// value of lane ^ S, by the cheapest cross-lane route for each distance: DPP within a quad
+// (1, 2) or a row of 16 (8), LDS-unit swizzle within 32 lanes (4, 16), and the gfx950 swap of
+// the wave's halves (32).  None of these goes through the LDS crossbar's address path.
+template <int S> __device__ __forceinline__ int lane_xor(int v)
 {
-    const float pv = __shfl_xor(v, stride);
-    const int pr = __shfl_xor(r, stride);
-    const bool take = keep_better ? better(pv, pr, v, r) : better(v, r, pv, pr);
-    if (take) {
-        v = pv;
-        r = pr;
+    if constexpr (S == 1) return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    else if constexpr (S == 2) return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    else if constexpr (S == 4) return __builtin_amdgcn_ds_swizzle(v, 0x101F);                  // xor 4 in 32
+    else if constexpr (S == 8) return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false); // row_ror 8
+    else if constexpr (S == 16) return __builtin_amdgcn_ds_swizzle(v, 0x401F);                 // xor 16 in 32
+    else {
+        static_assert(S == 32, "lane distance");
+        const auto p = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+        return (int)((__lane_id() < 32) ? p[1] : p[0]);
     }
 }
 
-// bitonic sort of the wave's 64 (v, r) pairs, best first
-__device__ __forceinline__ void wave_sort(float &v, int &r, int lane)
+template <int S> __device__ __forceinline__ float lane_xor(float v)
 {
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1)
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const bool lower = (lane & stride) == 0, first_half_desc = (lane & size) == 0;
-            cmpx(v, r, stride, lower == first_half_desc);
-        }
+    return __builtin_bit_cast(float, lane_xor<S>(__builtin_bit_cast(int, v)));
+}
+
+// one compare-exchange step between lanes `lane` and `lane ^ S`; keep_better selects which of
+// the two this lane keeps
+template <int S> __device__ __forceinline__ void cmpx(float &v, int &r, bool keep_better)
+{
+    const float pv = lane_xor<S>(v);
+    const int pr = lane_xor<S>(r);
+    // rows are distinct except empty slots, which are identical, so "mine is better" is
+    // "partner is not better" (swapping two identical empty slots changes nothing)
+    const bool take = keep_better == better(pv, pr, v, r);
+    v = take ? pv : v;
+    r = take ? pr : r;
+}
+
+// bitonic sort of the wave's 64 (v, r) pairs, best first
+template <int SIZE, int S> __device__ __forceinline__ void sort_stage(float &v, int &r, int lane)
+{
+    if constexpr (S > 0) {
+        cmpx<S>(v, r, ((lane & S) == 0) == ((lane & SIZE) == 0));
+        sort_stage<SIZE, S / 2>(v, r, lane);
+    }
+}
+
+template <int SIZE = 2> __device__ __forceinline__ void wave_sort(float &v, int &r, int lane)
+{
+    if constexpr (SIZE <= 64) {
+        sort_stage<SIZE, SIZE / 2>(v, r, lane);
+        wave_sort<SIZE * 2>(v, r, lane);
+    }
+}
+
+// bitonic clean of a bitonic 64-sequence into best-first order
+template <int S = 32> __device__ __forceinline__ void wave_clean(float &v, int &r, int lane)
+{
+    if constexpr (S > 0) {
+        cmpx<S>(v, r, (lane & S) == 0);
+        wave_clean<S / 2>(v, r, lane);
+    }
 }
 
 // L (sorted, best first) := the 64 best of L and S (both sorted, best first)
@@ -65,12 +105,37 @@ __device__ __forceinline__ void wave_merge(float &lv, int &lr, float sv, int sr,
 {
     const float qv = __shfl(sv, 63 - lane);
     const int qr = __shfl(sr, 63 - lane);
-    if (better(qv, qr, lv, lr)) {
-        lv = qv;
-        lr = qr;
-    }
-#pragma unroll
-    for (int stride = 32; stride > 0; stride >>= 1) cmpx(lv, lr, stride, (lane & stride) == 0);
+    const bool qb = better(qv, qr, lv, lr);
+    lv = qb ? qv : lv;
+    lr = qb ? qr : lr;
+    wave_clean(lv, lr, lane);
+}
+
+// Merge the wave's 64 (v, r) pairs, one per lane, into the sorted list.  Only pairs that beat
+// the current k-th best can end in the top k: when none does (one compare and a wave vote), the
+// chunk costs nothing more; otherwise it is sorted (unless SORTED) and merged.  (Inserting a few
+// candidates one at a time measured slower than the sort: each insertion is a chain of
+// vector-to-scalar round trips.)
+template <bool SORTED>
+__device__ __forceinline__ void wave_take(float &lv, int &lr, float v, int r, int k, int lane)
+{
+    const float tv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), k - 1));
+    const int tr = __builtin_amdgcn_readlane(lr, k - 1);
+    if (!__ballot(better(v, r, tv, tr))) return;
+    if constexpr (!SORTED) wave_sort(v, r, lane);
+    wave_merge(lv, lr, v, r, lane);
+}
+
+// sort one lane's pairs a, b into best-first order
+__device__ __forceinline__ void lane_cswap(float &va, int &ra, float &vb, int &rb)
+{
+    const bool sw = better(vb, rb, va, ra);
+    const float tv = va;
+    const int tr = ra;
+    va = sw ? vb : va;
+    ra = sw ? rb : ra;
+    vb = sw ? tv : vb;
+    rb = sw ? tr : rb;
 }
 
 // (m, s) := combination of two online log-sum-exp states
@@ -110,56 +175,96 @@ __device__ __forceinline__ uint32_t publish(int32_t *p, int v)
                                  __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 16;        // waves per block
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStageWords = 8192;  // LDS words staging block partials in the final merge (32 KB)
+constexpr int kBurst = 16;         // loads each thread issues before using the first
 
-__global__ __launch_bounds__(256) void logits_kernel(LogitsArgs a)
+// (m, s) := combination of two online log-sum-exp states, in double
+__device__ __forceinline__ void lse_combine_d(double &m, double &s, double pm, double ps)
+{
+    if (pm == -INFINITY) return;
+    if (m == -INFINITY) {
+        m = pm;
+        s = ps;
+        return;
+    }
+    const double mx = fmax(m, pm);
+    s = s * exp(m - mx) + ps * exp(pm - mx);
+    m = mx;
+}
+
+__device__ __forceinline__ double shfl_xor_d(double v, int off)
+{
+    const int lo = __shfl_xor(__double2loint(v), off), hi = __shfl_xor(__double2hiint(v), off);
+    return __hiloint2double(hi, lo);
+}
+
+// The sorted lists of the block's 16 waves (in s_v / s_r) merge pairwise in a fixed tree
+// (wave w takes wave w + step); wave 0 ends with the block's list in (lv, lr).
+__device__ __forceinline__ void block_tree_merge(float (*s_v)[64], int (*s_r)[64], float &lv, int &lr, int w,
+                                                 int lane)
+{
+    for (int step = kWaves / 2; step > 0; step >>= 1) {
+        __syncthreads();
+        if (w < step) {
+            wave_merge(lv, lr, s_v[w + step][lane], s_r[w + step][lane], lane);
+            s_v[w][lane] = lv;
+            s_r[w][lane] = lr;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
 {
     __shared__ float s_v[kWaves][64];
     __shared__ int s_r[kWaves][64];
     __shared__ float s_m[kWaves], s_s[kWaves];
-    __shared__ double s_d[256];
+    __shared__ int32_t s_stage[kStageWords];
     __shared__ int s_last;
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int b = blockIdx.x, t = blockIdx.y;
-    const int k = a.k;
+    const int k = a.k, kc = a.k;
     const float *yt = a.y + (int64_t)t * a.ldy;
     const int r0 = b * a.rpb;
     const int r1 = r0 + a.rpb < a.M ? r0 + a.rpb : a.M;
 
+    // ---- stream the block's rows: 4 chunks of 64 rows per wave in flight,
+    //      rows r0 + 64 * (kWaves * (4i + j) + w) + lane
     float lv = -INFINITY, m = -INFINITY, s = 0.f;
     int lr = kRowEmpty;
-    // 4 chunks of 64 rows per wave in flight: rows r0 + 256*(4i + j) + 64*w + lane
-    for (int base = r0; base < r1; base += 4 * 256) {
+    for (int base = r0; base < r1; base += 4 * kThreads) {
         float v[4];
         int row[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            row[j] = base + 256 * j + 64 * w + lane;
+            row[j] = base + kThreads * j + 64 * w + lane;
             v[j] = row[j] < r1 ? yt[row[j]] : -INFINITY;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bool in = row[j] < r1;
-            if (in) {
+            if (row[j] < r1) {
                 if (v[j] > m) {
                     s = s * expf(m - v[j]) + 1.f;
                     m = v[j];
                 } else {
                     s += expf(v[j] - m);
                 }
+            } else {
+                row[j] = kRowEmpty;
             }
-            if (k > 0) {
-                const int rr = in ? row[j] : kRowEmpty;
-                const float tv = __shfl(lv, k - 1);
-                const int tr = __shfl(lr, k - 1);
-                if (__any(better(v[j], rr, tv, tr))) {
-                    float cv = v[j];
-                    int cr = rr;
-                    wave_sort(cv, cr, lane);
-                    wave_merge(lv, lr, cv, cr, lane);
-                }
-            }
+        }
+        if (k > 0) {
+            // each lane orders its four rows first: chunk j then holds every lane's j-th best, so
+            // once the lane maxima are in the list the later chunks rarely have a candidate
+            lane_cswap(v[0], row[0], v[1], row[1]);
+            lane_cswap(v[2], row[2], v[3], row[3]);
+            lane_cswap(v[0], row[0], v[2], row[2]);
+            lane_cswap(v[1], row[1], v[3], row[3]);
+            lane_cswap(v[1], row[1], v[2], row[2]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wave_take<false>(lv, lr, v[j], row[j], k, lane);
         }
     }
     // wave log-sum-exp
@@ -174,17 +279,22 @@ __global__ __launch_bounds__(256) void logits_kernel(LogitsArgs a)
         s_m[w] = m;
         s_s[w] = s;
     }
+    if (k > 0) block_tree_merge(s_v, s_r, lv, lr, w, lane);
     __syncthreads();
 
-    // block partial: wave 0 merges the other waves' lists and states, then publishes
-    const int kc = a.k;
+    // ---- block partial (wave 0): publish (max, sum, k best) with returning exchanges
     float *pf = a.part_f + ((int64_t)t * a.B + b) * (2 + kc);
     int32_t *pi = a.part_i + ((int64_t)t * a.B + b) * kc;
     uint32_t sink = 0;
     if (w == 0) {
-        for (int o = 1; o < kWaves; ++o) {
-            if (k > 0) wave_merge(lv, lr, s_v[o][lane], s_r[o][lane], lane);
-            lse_combine(m, s, s_m[o], s_s[o]);
+        // the 16 wave states: lanes 0..15 hold them, a butterfly combines (lane 0's result is
+        // the same every run: a fixed sequence of operations)
+        m = lane < kWaves ? s_m[lane] : -INFINITY;
+        s = lane < kWaves ? s_s[lane] : 0.f;
+#pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            const float pm = __shfl_xor(m, off), ps = __shfl_xor(s, off);
+            lse_combine(m, s, pm, ps);
         }
         if (lane < kc) {
             sink |= publish(pf + 2 + lane, lv);
@@ -204,57 +314,80 @@ __global__ __launch_bounds__(256) void logits_kernel(LogitsArgs a)
     __syncthreads();
     if (!s_last) return;
 
-    // last block of token t: merge the B partials in block order
+    // ---- last block of token t: merge the B partials.  They are staged through LDS in chunks
+    //      of cb blocks; each thread issues kBurst independent loads before using the first.
     const float *tf = a.part_f + (int64_t)t * a.B * (2 + kc);
     const int32_t *ti = a.part_i + (int64_t)t * a.B * kc;
-    // log-sum-exp: global max, then the scaled sums in double, fixed order
-    float mx = -INFINITY;
-    for (int bb = threadIdx.x; bb < a.B; bb += blockDim.x) mx = fmaxf(mx, ld_agent(tf + (int64_t)bb * (2 + kc)));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) s_m[w] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-    double acc = 0.0;
-    for (int bb = threadIdx.x; bb < a.B; bb += blockDim.x) {
-        const float bm = ld_agent(tf + (int64_t)bb * (2 + kc));
-        const float bs = ld_agent(tf + (int64_t)bb * (2 + kc) + 1);
-        if (bm != -INFINITY) acc += (double)bs * exp((double)bm - (double)mx);
-    }
-    s_d[threadIdx.x] = acc;
-    // top-k: wave w merges the lists of blocks w, w + 4, ... (each already sorted, best first);
-    // a list whose best entry does not beat the current k-th best is skipped whole
+    const int stride_f = 2 + kc, per = 2 + 2 * kc;
+    const int cb = kStageWords / per < a.B ? kStageWords / per : a.B;
+    float *st_f = reinterpret_cast<float *>(s_stage);
+    int32_t *st_i = s_stage + cb * stride_f;
+    double tm = -INFINITY, ts = 0.0;  // wave 0 lane l: blocks l, l + 64, ... in order
     lv = -INFINITY;
     lr = kRowEmpty;
-    if (k > 0) {
-        for (int bb = w; bb < a.B; bb += kWaves) {
-            const float *bf = tf + (int64_t)bb * (2 + kc) + 2;
-            const float cv0 = ld_agent(bf);
-            const int cr0 = ld_agent(ti + (int64_t)bb * kc);
-            if (!better(cv0, cr0, __shfl(lv, k - 1), __shfl(lr, k - 1))) continue;
-            float cv = lane < kc ? ld_agent(bf + lane) : -INFINITY;
-            int cr = lane < kc ? ld_agent(ti + (int64_t)bb * kc + lane) : kRowEmpty;
-            wave_merge(lv, lr, cv, cr, lane);
+    for (int c0 = 0; c0 < a.B; c0 += cb) {
+        const int n = a.B - c0 < cb ? a.B - c0 : cb;
+        const int nf = n * stride_f, ni = n * kc;
+        __syncthreads();  // the previous chunk's readers are done
+        for (int e0 = threadIdx.x; e0 < nf; e0 += kBurst * kThreads) {
+            float v[kBurst];
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int e = e0 + kThreads * i;
+                v[i] = e < nf ? ld_agent(tf + (int64_t)c0 * stride_f + e) : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i)
+                if (e0 + kThreads * i < nf) st_f[e0 + kThreads * i] = v[i];
         }
-    }
-    __syncthreads();  // s_m reads above are done before s_v / s_r are reused
-    s_v[w][lane] = lv;
-    s_r[w][lane] = lr;
-    __syncthreads();
-    if (w == 0) {
+        for (int e0 = threadIdx.x; e0 < ni; e0 += kBurst * kThreads) {
+            int v[kBurst];
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int e = e0 + kThreads * i;
+                v[i] = e < ni ? ld_agent(ti + (int64_t)c0 * kc + e) : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i)
+                if (e0 + kThreads * i < ni) st_i[e0 + kThreads * i] = v[i];
+        }
+        __syncthreads();
+        if (w == 0)
+            for (int e = lane; e < n; e += 64)
+                lse_combine_d(tm, ts, (double)st_f[e * stride_f], (double)st_f[e * stride_f + 1]);
+        // top-k: wave w takes the block lists w, w + 16, ... of the chunk (lane i reads entry i)
         if (k > 0)
-            for (int o = 1; o < kWaves; ++o) wave_merge(lv, lr, s_v[o][lane], s_r[o][lane], lane);
+            for (int e = w; e < n; e += kWaves) {
+                const float cv = lane < kc ? st_f[e * stride_f + 2 + lane] : -INFINITY;
+                const int cr = lane < kc ? st_i[e * kc + lane] : kRowEmpty;
+                wave_take<true>(lv, lr, cv, cr, k, lane);
+            }
+    }
+    if (k > 0) {
+        __syncthreads();  // the stage is free; s_v / s_r take the wave lists
+        s_v[w][lane] = lv;
+        s_r[w][lane] = lr;
+        block_tree_merge(s_v, s_r, lv, lr, w, lane);
+    }
+    if (w == 0) {
         if (lane < kc) {
             a.vals[(int64_t)t * kc + lane] = lv;
             a.ids[(int64_t)t * kc + lane] = lr == kRowEmpty ? -1 : (a.index ? a.index[lr] : lr);
         }
-        if (lane == 0 && a.lse) {
-            double tot = 0.0;
-            for (int i = 0; i < 256; ++i) tot += s_d[i];
-            a.lse[t] = (float)((double)mx + log(tot));
+        // the 64 lane states combine in a fixed butterfly
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const double pm = shfl_xor_d(tm, off), ps = shfl_xor_d(ts, off);
+            // both lanes of a pair combine the same two states in the same order
+            double m1 = (lane & off) ? pm : tm, s1 = (lane & off) ? ps : ts;
+            const double m2 = (lane & off) ? tm : pm, s2 = (lane & off) ? ts : ps;
+            lse_combine_d(m1, s1, m2, s2);
+            tm = m1;
+            ts = s1;
         }
+        if (lane == 0 && a.lse) a.lse[t] = (float)(tm + log(ts));
+        if (lane == 0) __hip_atomic_store(&a.counter[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (threadIdx.x == 0) __hip_atomic_store(&a.counter[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -264,7 +397,7 @@ hipError_t launch_logits(const LogitsArgs &a, hipStream_t st)
     LogitsArgs arg = a;
     void *args[] = {&arg};
     return hipLaunchKernel(reinterpret_cast<const void *>(&logits_kernel), dim3((unsigned)a.B, (unsigned)a.T),
-                           dim3(256), args, 0, st);
+                           dim3(kThreads), args, 0, st);
 }
 
 }  // namespace qmatk
