@@ -30,6 +30,8 @@ METRIC = "weight GB/s & % HBM peak, Q4 MLP and Q6 vocab head at T=1 and T=8; µs
 HBM_PEAK_GBS = 8000.0
 PRIMARY = ("q4_gate_up_34816x5120", 1)
 ROTATE_BYTES = 512 << 20
+PREFILL_T = (512, 2048)                      # prefill chunk sizes timed on the GEMM route
+PREFILL_SHAPES = ("q5_down_5120x17408", "fp8_proj_5120x5120")
 
 
 def log(*a):
@@ -200,6 +202,33 @@ def measure_epilogue(res, T, k, steps, warmup):
     return {"us_per_call": round(us, 3), "GBps": round(nb / us / 1e3, 1), "bytes": nb, "k": k}
 
 
+def measure_prefill(res, T, steps=20, warmup=3):
+    """A prefill-sized product (the GEMM route) on the resident matrix with T synthetic bf16
+    activation rows; throughput in TFLOP/s (2 T M K per call)."""
+    import torch
+    import weight_only_quant_amd as wq
+    wl = res.wl
+    g = torch.Generator(device="cuda")
+    g.manual_seed(T)
+    x = torch.randn((T, wl.K), generator=g, device="cuda").to(torch.bfloat16)
+    y = torch.empty((T, wl.M), device="cuda")
+    hs = res.handles
+    for i in range(warmup):
+        wq.qmat_run(hs[i % len(hs)], x, y, T=T)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        wq.qmat_run(hs[i % len(hs)], x, y, T=T)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    tf = 2.0 * T * wl.M * wl.K / us / 1e6
+    del x, y
+    return {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1), "pct_bf16_mfma_peak": round(100 * tf / 2500.0, 2),
+            "route": "gemm"}
+
+
 def cpu_baseline(res, T, target_s=12.0):
     """The CPU oracle (as it stands) on a bounded sample of the same workload: whole passes
     over all rows (or a row subset when one pass would exceed the budget), repeated until
@@ -333,6 +362,11 @@ def main():
             continue
         extra[f"{name}_T{T2}"] = measure(res, T2, args.steps, args.warmup)
         log(f"[bench] {name} T={T2}: {extra[f'{name}_T{T2}']}")
+    # prefill-sized token counts (the GEMM route)
+    for T2 in PREFILL_T:
+        key = f"{name}_prefill_T{T2}"
+        extra[key] = measure_prefill(res, T2)
+        log(f"[bench] {key}: {extra[key]}")
     res.close()
     del res
     torch.cuda.empty_cache()
@@ -346,6 +380,11 @@ def main():
                 steps = args.steps if r.wl.M * r.wl.K < 1e9 else max(50, args.steps // 4)
                 extra[f"{n}_T{T2}"] = measure(r, T2, steps, args.warmup)
                 log(f"[bench] {n} T={T2}: {extra[f'{n}_T{T2}']}")
+                if n in PREFILL_SHAPES and T2 == qi.CONFIGS[n][3][0]:
+                    for T3 in PREFILL_T:
+                        key = f"{n}_prefill_T{T3}"
+                        extra[key] = measure_prefill(r, T3)
+                        log(f"[bench] {key}: {extra[key]}")
                 if n == "q6_head_248320x5120":
                     key = f"head_epilogue_lse_top20_248320_T{T2}"
                     extra[key] = measure_epilogue(r, T2, 20, args.steps, 20)

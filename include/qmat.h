@@ -63,7 +63,9 @@ typedef enum {
 typedef enum {
     QMAT_ROUTE_AUTO = 0, /* the library's choice for (format, shape, T) */
     QMAT_ROUTE_VALU = 1, /* vector-ALU dot products; T > 4 runs as several passes */
-    QMAT_ROUTE_MFMA = 2  /* bf16 matrix-core tiles (16 tokens x 16 rows x 32 k) */
+    QMAT_ROUTE_MFMA = 2, /* bf16 matrix-core tiles (16 tokens x 16 rows x 32 k) */
+    QMAT_ROUTE_GEMM = 3  /* prefill-sized T: 64-token x 256-row matrix-core tiles, activations
+                            staged in LDS; the automatic route for T > 16 */
 } qmat_route;
 
 typedef struct qmat *qmat_t;
@@ -140,8 +142,12 @@ int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packe
 int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows);
 
 /* y = x . W^T.  x: device bf16 [T][K] (16-byte aligned); y: device fp32 [T][M], fully
- * overwritten.  T == 0 is a no-op.  Asynchronous on stream; no allocation, no sync.
- * Errors: QMAT_EINVAL (null handle/pointers, misaligned x), QMAT_ESHAPE (T > 16 or T < 0),
+ * overwritten.  T == 0 is a no-op.  Decode and verify sizes (T <= 16) take the small-T routes;
+ * prefill sizes (17 <= T <= 4194240) the GEMM route, where each unpacked weight feeds the
+ * matrix cores for 64 tokens (the pages' prefill, where the groupwise route is capped by the
+ * 4-bit -> bf16 decoding: "Qwen3.6-35B-A3B NVFP4" / "Qwen3.8-27B EXL3" speed notes).
+ * Asynchronous on stream; no allocation, no sync.
+ * Errors: QMAT_EINVAL (null handle/pointers, misaligned x), QMAT_ESHAPE (T < 0 or too large),
  * QMAT_EHIP (launch failure). */
 int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream);
 
@@ -154,7 +160,8 @@ int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream
  * plan gives the same y for the same inputs run after run (different plans may differ in the
  * last bits: the summation order differs). */
 typedef struct {
-    int route;       /* QMAT_ROUTE_VALU or QMAT_ROUTE_MFMA */
+    int route;       /* QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA, or QMAT_ROUTE_GEMM (then the other fields
+                        are not read) */
     int depth;       /* 128-wide k units each wave keeps in flight: 1 or 2 */
     int waves;       /* waves per workgroup: 1, 2, 4 or 8 */
     int splits;      /* workgroups per leading tile: >= 1 */

@@ -232,6 +232,68 @@ def test_row_views(fmt):
     wq.qmat_destroy(parent)
 
 
+# ------------------------------------------------------------------ prefill GEMM route
+
+GEMM_SHAPES = [(200, 320), (64, 1024), (1, 64), (257, 2176), (300, 192)]
+
+
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
+@pytest.mark.parametrize("M,K", GEMM_SHAPES)
+def test_gemm_parity(fmt, M, K):
+    # token counts below, at and across the 64-token tile (ragged last tile), on the explicit
+    # GEMM route and (T > 16) the automatic one
+    Tmax = 130
+    wl = _workload(fmt, M, K, Tmax, 500 + M + K + fmt)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    for T in (1, 17, 64, 100, 130):
+        say(f"gemm fmt={fmt} M={M} K={K} T={T}")
+        y = torch.full((T, M), float("nan"), device="cuda")
+        if T > 16 and T % 2:
+            wq.qmat_run(qm.handle, xd[:T], y, T=T)
+        else:
+            wq.qmat_run_ex(qm.handle, xd[:T], y, T, route=wq.QMAT_ROUTE_GEMM)
+        torch.cuda.synchronize()
+        sub = qi.Workload(wl.name, fmt, M, K, T, wl.codes, wl.scales, wl.x[:T])
+        _check_y(y, sub, f"gemm fmt={fmt} {M}x{K} T={T}")
+
+
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
+def test_gemm_bit_exact_on_exact_inputs(fmt):
+    M, K, T = 130, 1024, 70
+    say(f"gemm exact fmt={fmt}")
+    wl = _exact_workload(fmt, M, K, T, 9)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    y = torch.empty((T, M), device="cuda")
+    wq.qmat_run(qm.handle, _x_dev(wl.x), y, T=T)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.gemv(fmt, wl.codes, wl.scales, wl.x)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref)
+
+
+def test_gemm_plan_and_graph_replay():
+    import gc
+    gc.collect()
+    wl = _workload(4, 320, 640, 96, 3)
+    qm = wq.QMat(4, wl.codes, wl.scales)
+    assert wq.qmat_get_plan(qm.handle, 96).route == wq.QMAT_ROUTE_GEMM
+    assert wq.qmat_get_plan(qm.handle, 16).route == wq.QMAT_ROUTE_MFMA
+    xd = _x_dev(wl.x)
+    y_eager = torch.empty((96, 320), device="cuda")
+    wq.qmat_run(qm.handle, xd, y_eager, T=96)
+    y = torch.empty_like(y_eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wq.qmat_run(qm.handle, xd, y, T=96)
+    for i in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), i
+        wq.qmat_run(qm.handle, xd, y_eager, T=96)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def _exact_workload(fmt, M, K, T, seed):
     """Inputs whose products and partial sums are all exact in fp32: small integer bf16
     activations and power-of-two scales (FP8: integer-valued E4M3 bytes)."""
@@ -298,8 +360,11 @@ def test_t_zero_is_noop_and_bad_args():
     wq.qmat_run(qm.handle, xd, y, T=0)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
-    with pytest.raises(wq.QmatError) as e:
-        wq.qmat_run(qm.handle, xd, y, T=17)
+    with pytest.raises(wq.QmatError) as e:  # beyond the largest GEMM launch: rejected on the host
+        wq.qmat_run(qm.handle, xd, y, T=65535 * 64 + 1)
+    assert e.value.status == wq.QMAT_ESHAPE
+    with pytest.raises(wq.QmatError) as e:  # the small-T routes stop at 16
+        wq.qmat_run_ex(qm.handle, xd, y, 17, route=wq.QMAT_ROUTE_MFMA)
     assert e.value.status == wq.QMAT_ESHAPE
     with pytest.raises(wq.QmatError) as e:
         wq.qmat_run(qm.handle, xd, y, T=-1)
@@ -361,6 +426,25 @@ def _sample_rows(M, n=1500, seed=0):
     rows = set(range(min(64, M))) | set(range(max(0, M - 64), M))
     rows |= set(rng.integers(0, M, n).tolist())
     return sorted(rows)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,T", [("q4_gate_up_34816x5120", 512), ("q5_down_5120x17408", 256),
+                                    ("fp8_proj_5120x5120", 512)])
+def test_full_size_prefill_sampled_rows(name, T):
+    """Prefill-sized T on full benchmark shapes (the GEMM route): sampled rows vs the oracle."""
+    fmt, M, K, _, mult = qi.CONFIGS[name]
+    say(f"prefill {name} T={T}: generating")
+    wl = qi.fp8_rows(name, M, K, T, mult, 1) if fmt == 8 else qi.groupwise(name, fmt, M, K, T, mult, 1)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    y = torch.full((T, M), float("nan"), device="cuda")
+    wq.qmat_run(qm.handle, _x_dev(wl.x), y, T=T)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    rows = _sample_rows(M, n=200, seed=2)
+    worst = _check_y(y, wl, f"prefill {name} T={T}", rows=rows)
+    say(f"  worst ratio {worst:.3g}")
+    qm.close()
 
 
 @pytest.mark.slow

@@ -433,8 +433,34 @@ int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows)
 
 namespace {
 
+// The prefill GEMM route (any T >= 1; the automatic choice above the small-T limit).
+int run_gemm(qmat_t h, const void *x_dev, float *y_dev, int T, void *stream)
+{
+    if (T < 0 || T > kGemmMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d]", T, kGemmMaxT);
+    if (T == 0) return ok();
+    if (!x_dev || !y_dev) return fail(QMAT_EINVAL, "qmat_run: null x or y");
+    if (reinterpret_cast<uintptr_t>(x_dev) % 16) return fail(QMAT_EINVAL, "qmat_run: x not 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_run: y not 4-byte aligned");
+    RunArgs a{};
+    a.codes = h->codes;
+    a.scales = h->scales;
+    a.x = static_cast<const uint16_t *>(x_dev);
+    a.y = y_dev;
+    a.ldy = h->M;
+    a.M = (int)h->M;
+    a.K = (int)h->K;
+    a.T = T;
+    a.NT = (int)h->NT;
+    a.NU = (int)h->NU;
+    a.S = 1;
+    const hipError_t e = launch_gemm(h->fmt, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QMAT_EHIP, "qmat_run: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, void *stream)
 {
+    if (p.route == kRouteGemm) return run_gemm(h, x_dev, y_dev, T, stream);
     if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d]", T, kMaxT);
     if (T == 0) return ok();
     if (!x_dev || !y_dev) return fail(QMAT_EINVAL, "qmat_run: null x or y");
@@ -490,9 +516,11 @@ int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int
                 void *stream)
 {
     if (!h) return fail(QMAT_EINVAL, "qmat_run: null handle");
-    if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d]", T, kMaxT);
+    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_GEMM) return fail(QMAT_EINVAL, "qmat_run: bad route %d", route);
+    if (route == QMAT_ROUTE_GEMM || (route == QMAT_ROUTE_AUTO && T > kMaxT))
+        return run_gemm(h, x_dev, y_dev, T, stream);
+    if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d] on this route", T, kMaxT);
     if (T == 0) return ok();
-    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA) return fail(QMAT_EINVAL, "qmat_run: bad route %d", route);
     if (!(waves == 0 || waves == 1 || waves == 2 || waves == 4 || waves == 8))
         return fail(QMAT_EINVAL, "qmat_run: waves must be 0, 1, 2, 4 or 8");
     if (splits < 0) return fail(QMAT_EINVAL, "qmat_run: splits must be >= 0");
@@ -513,8 +541,9 @@ int qmat_run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const qmat_p
 {
     if (!h) return fail(QMAT_EINVAL, "qmat_run_plan: null handle");
     if (!plan) return fail(QMAT_EINVAL, "qmat_run_plan: null plan");
+    if (plan->route == QMAT_ROUTE_GEMM) return run_gemm(h, x_dev, y_dev, T, stream);
     if (plan->route != QMAT_ROUTE_VALU && plan->route != QMAT_ROUTE_MFMA)
-        return fail(QMAT_EINVAL, "qmat_run_plan: route must be QMAT_ROUTE_VALU or QMAT_ROUTE_MFMA");
+        return fail(QMAT_EINVAL, "qmat_run_plan: route must be QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA or QMAT_ROUTE_GEMM");
     const Plan p{plan->route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma, plan->depth, plan->waves, plan->splits,
                  plan->tail_tiles, plan->tail_splits};
     return run_plan(h, x_dev, y_dev, T, p, stream);
@@ -523,8 +552,13 @@ int qmat_run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const qmat_p
 int qmat_get_plan(qmat_t h, int T, int route, qmat_plan *plan)
 {
     if (!h || !plan) return fail(QMAT_EINVAL, "qmat_get_plan: null argument");
+    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_GEMM) return fail(QMAT_EINVAL, "qmat_get_plan: bad route %d", route);
+    if (route == QMAT_ROUTE_GEMM || (route == QMAT_ROUTE_AUTO && T > kMaxT)) {
+        if (T < 1 || T > kGemmMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kGemmMaxT);
+        *plan = qmat_plan{QMAT_ROUTE_GEMM, 1, 4, 1, 0, 1};
+        return ok();
+    }
     if (T < 1 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kMaxT);
-    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA) return fail(QMAT_EINVAL, "qmat_get_plan: bad route %d", route);
     const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
     const Plan &p = h->plan[r - 1][T];
     plan->route = r == kRouteValu ? QMAT_ROUTE_VALU : QMAT_ROUTE_MFMA;

@@ -40,7 +40,7 @@ struct DequantArgs {
     int M, K, NT, NU;
 };
 
-enum Route { kRouteValu = 1, kRouteMfma = 2 };
+enum Route { kRouteValu = 1, kRouteMfma = 2, kRouteGemm = 3 };
 
 // Tokens one vector-ALU launch handles; larger T runs as several launches.
 constexpr int kValuMaxT = 4;
@@ -49,6 +49,11 @@ constexpr int kValuMaxT = 4;
 constexpr int kMaxDepth = 2;
 hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, hipStream_t stream);
 hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t stream);
+
+// Prefill GEMM route: any T >= 1 (tiles of 64 tokens x 256 rows; a.S, a.ws unused).
+hipError_t launch_gemm(int fmt, const RunArgs &a, hipStream_t stream);
+// Largest T of one GEMM launch (grid.y = ceil(T / 64) <= 65535).
+constexpr int kGemmMaxT = 65535 * 64;
 
 // Workgroups of (64 * waves) threads of the product kernel for (fmt, route, T) that one compute
 // unit holds at once (0 on error).

@@ -571,6 +571,140 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
     });
 }
 
+// ------------------------------------------------------------------ GEMM route (prefill, T > 16)
+
+// Prefill-sized products: the weights are reused by many tokens, so the MFMA does most of the
+// work and each unpacked weight feeds kGemmTB / 16 matrix instructions.  A workgroup is 4 waves;
+// wave w owns row tile 4 * blockIdx.x + w, and the workgroup a tile of kGemmTB tokens
+// (blockIdx.y).  Per 128-wide k unit the workgroup stages the token tile's activations in LDS
+// (shared by its 4 waves, double-buffered, one barrier per unit) while each wave streams its
+// tile's packed unit from HBM one unit ahead.  Per 64-group, the MFMA sums code * x into P and
+// the group scale enters once per (token, row): acc += scale * P (exact products, fp32 sums, as
+// on the small-T routes).  Row-scaled FP8 has no group scale: the MFMA accumulates straight
+// into acc and the row scale is applied at the end.
+constexpr int kGemmTB = 64;               // tokens per workgroup tile
+constexpr int kGemmRS = kUnitK + 8;       // LDS row stride of a staged token (bf16 elements)
+
+template <int FMT>
+__global__ __launch_bounds__(256) void gemm_kernel(RunArgs a)
+{
+    constexpr int NB = Fmt<FMT>::NB, NTB = kGemmTB / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGemmTB * kGemmRS];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tile = 4 * blockIdx.x + w;
+    const bool has_tile = tile < a.NT;
+    const int tok0 = blockIdx.y * kGemmTB;
+
+    // activations of unit u for the token tile: thread i stages 16-byte pieces i, i + 256, ...
+    // of the kGemmTB x 128 block (token = piece / 16, k octet = piece % 16); rows past T and
+    // columns past K are zero
+    auto x_fetch = [&](int u, u32x4_t (&xr)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int piece = threadIdx.x + 256 * j, tt = piece >> 4, ko = piece & 15;
+            const int t = tok0 + tt, k = u * kUnitK + 8 * ko;
+            xr[j] = (t < a.T && k < a.K)
+                        ? *reinterpret_cast<const u32x4_t *>(a.x + (int64_t)t * a.K + k)
+                        : (u32x4_t){0u, 0u, 0u, 0u};
+        }
+    };
+    auto x_store = [&](int buf, const u32x4_t (&xr)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int piece = threadIdx.x + 256 * j, tt = piece >> 4, ko = piece & 15;
+            *reinterpret_cast<u32x4_t *>(&xs[buf][tt * kGemmRS + 8 * ko]) = xr[j];
+        }
+    };
+
+    f32x4_t acc[4][NTB];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < NTB; ++n) acc[m][n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    Unit<NB, 1> cur, nxt;
+    u32x4_t xr[4];
+    x_fetch(0, xr);
+    if (has_tile) load_weights<FMT>(a, tile, 0, lane, cur);
+    x_store(0, xr);
+    __syncthreads();
+    const int oct = lane >> 4, tl = lane & 15;
+    for (int u = 0; u < a.NU; ++u) {
+        const int buf = u & 1;
+        const bool more = u + 1 < a.NU;
+        if (more) {
+            x_fetch(u + 1, xr);
+            if (has_tile) load_weights<FMT>(a, tile, u + 1, lane, nxt);
+        }
+        if (has_tile) {
+            const uint32_t *W = reinterpret_cast<const uint32_t *>(cur.c);
+            const uint16_t *xb = xs[buf];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                f32x4_t P[4][NTB];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int ka = 2 * g + ks;
+                    bf16x8_t A[NTB];
+#pragma unroll
+                    for (int n = 0; n < NTB; ++n)
+                        A[n] = *reinterpret_cast<const bf16x8_t *>(&xb[(16 * n + tl) * kGemmRS + 32 * ka + 8 * oct]);
+#define QMAT_GEMM_ROW(MM, KA)                                                                           \
+    {                                                                                                   \
+        uint32_t b[4];                                                                                  \
+        bf16x8_of<FMT, KA, MM>(W, b);                                                                   \
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, (u32x4_t){b[0], b[1], b[2], b[3]});             \
+        _Pragma("unroll") for (int n = 0; n < NTB; ++n) {                                               \
+            if constexpr (FMT == 8)                                                                     \
+                acc[MM][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[n], B, acc[MM][n], 0, 0, 0);    \
+            else                                                                                        \
+                P[MM][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                                     \
+                    A[n], B, ks == 0 ? (f32x4_t){0.f, 0.f, 0.f, 0.f} : P[MM][n], 0, 0, 0);             \
+        }                                                                                               \
+    }
+                    if (ka == 0) { QMAT_GEMM_ROW(0, 0) QMAT_GEMM_ROW(1, 0) QMAT_GEMM_ROW(2, 0) QMAT_GEMM_ROW(3, 0) }
+                    else if (ka == 1) { QMAT_GEMM_ROW(0, 1) QMAT_GEMM_ROW(1, 1) QMAT_GEMM_ROW(2, 1) QMAT_GEMM_ROW(3, 1) }
+                    else if (ka == 2) { QMAT_GEMM_ROW(0, 2) QMAT_GEMM_ROW(1, 2) QMAT_GEMM_ROW(2, 2) QMAT_GEMM_ROW(3, 2) }
+                    else { QMAT_GEMM_ROW(0, 3) QMAT_GEMM_ROW(1, 3) QMAT_GEMM_ROW(2, 3) QMAT_GEMM_ROW(3, 3) }
+#undef QMAT_GEMM_ROW
+                }
+                if constexpr (FMT != 8) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const float sf = group_scale(cur.sc, g, m);
+#pragma unroll
+                        for (int n = 0; n < NTB; ++n)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(sf, P[m][n][i], acc[m][n][i]);
+                    }
+                }
+            }
+        }
+        if (more) {
+            x_store(buf ^ 1, xr);
+            if (has_tile) cur = nxt;
+        }
+        __syncthreads();
+    }
+    if (!has_tile) return;
+    f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
+    if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)tile * 16 + tl];
+    // D[m][n]: lane holds tokens 16n + 4 * oct + i of row 16m + tl
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int row = tile * kTileRows + 16 * m + tl;
+        if (row >= a.M) continue;
+#pragma unroll
+        for (int n = 0; n < NTB; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = tok0 + 16 * n + 4 * oct + i;
+                if (t < a.T) a.y[(int64_t)t * a.ldy + row] = acc[m][n][i] * rs[m];
+            }
+    }
+}
+
 // ------------------------------------------------------------------ dequant (checking path)
 
 template <int FMT, int KA, int MM>
@@ -700,6 +834,20 @@ int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int NU, i
 }
 
 template <int FMT> static const void *dequant_kernel_ptr() { return reinterpret_cast<const void *>(&dequant_kernel<FMT>); }
+
+template <int FMT> static const void *gemm_kernel_ptr() { return reinterpret_cast<const void *>(&gemm_kernel<FMT>); }
+
+hipError_t launch_gemm(int fmt, const RunArgs &a, hipStream_t st)
+{
+    const void *k = fmt == 4 ? gemm_kernel_ptr<4>() : fmt == 5 ? gemm_kernel_ptr<5>()
+                  : fmt == 6 ? gemm_kernel_ptr<6>() : fmt == 8 ? gemm_kernel_ptr<8>()
+                  : fmt == 9 ? gemm_kernel_ptr<9>() : nullptr;
+    if (!k) return hipErrorInvalidValue;
+    RunArgs arg = a;
+    void *args[] = {&arg};
+    return hipLaunchKernel(k, dim3((unsigned)((a.NT + 3) / 4), (unsigned)((a.T + kGemmTB - 1) / kGemmTB)), dim3(256),
+                           args, 0, st);
+}
 
 hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t st)
 {
