@@ -125,8 +125,9 @@ int qmat_quantize(int fmt, int64_t M, int64_t K, const float *w, const float *im
 /* Create a handle over a packed matrix already in device memory.
  *   packed_dev: device pointer to qmat_pack's output (bytes == qmat_packed_bytes, 16-byte
  *               aligned).  Borrowed: it must outlive the handle and is never written.
- * The handle owns a small split-K workspace (device) that it allocates here; calls that
- * share one handle must therefore be ordered (one stream, or synchronized streams).
+ * The handle owns a split-K workspace (device) that it allocates here: small-T partial sums,
+ * and for matrices of fewer than 1024 rows per CU up to 32 MB for the GEMM route's k splits.  Calls that share one handle must therefore be ordered (one stream, or
+ * synchronized streams).
  * Errors: QMAT_EINVAL, QMAT_ESHAPE, QMAT_ESIZE (bytes mismatch), QMAT_ENOMEM, QMAT_EHIP. */
 int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packed_dev, size_t bytes);
 
@@ -145,7 +146,9 @@ int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows);
  * overwritten.  T == 0 is a no-op.  Decode and verify sizes (T <= 16) take the small-T routes;
  * prefill sizes (17 <= T <= 4194240) the GEMM route, where each unpacked weight feeds the
  * matrix cores for 64 tokens (the pages' prefill, where the groupwise route is capped by the
- * 4-bit -> bf16 decoding: "Qwen3.6-35B-A3B NVFP4" / "Qwen3.8-27B EXL3" speed notes).
+ * 4-bit -> bf16 decoding: "Qwen3.6-35B-A3B NVFP4" / "Qwen3.8-27B EXL3" speed notes).  When a
+ * narrow matrix at a small prefill T gives too few tiles to fill the GPU, the GEMM route splits
+ * K and sums the splits through the workspace in a fixed order (deterministic).
  * Asynchronous on stream; no allocation, no sync.
  * Errors: QMAT_EINVAL (null handle/pointers, misaligned x), QMAT_ESHAPE (T < 0 or too large),
  * QMAT_EHIP (launch failure). */
@@ -160,8 +163,8 @@ int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream
  * plan gives the same y for the same inputs run after run (different plans may differ in the
  * last bits: the summation order differs). */
 typedef struct {
-    int route;       /* QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA, or QMAT_ROUTE_GEMM (then the other fields
-                        are not read) */
+    int route;       /* QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA, or QMAT_ROUTE_GEMM (then only splits is
+                        read: the k splits of every 64-token x 256-row tile, 1..16) */
     int depth;       /* 128-wide k units each wave keeps in flight: 1 or 2 */
     int waves;       /* waves per workgroup: 1, 2, 4 or 8 */
     int splits;      /* workgroups per leading tile: >= 1 */
@@ -175,7 +178,8 @@ typedef struct {
  *   depth:  replaces plan.depth (0 = keep).
  *   waves:  replaces plan.waves (0 = keep).
  *   splits: replaces plan.splits and removes the trailing-tile split, so every tile is shared
- *           by `splits` workgroups (0 = keep the automatic plan's splits and tail).
+ *           by `splits` workgroups (0 = keep the automatic plan's splits and tail); on the GEMM
+ *           route the k splits, 1..16 (0 = automatic).
  * Errors: as qmat_run, plus QMAT_EINVAL (route, depth, waves) and QMAT_ESIZE (the splits at
  * this T need more workspace than was reserved at create time). */
 int qmat_run_ex(qmat_t handle, const void *x_dev, float *y_dev, int T, int route, int depth,
@@ -189,7 +193,8 @@ int qmat_run_plan(qmat_t handle, const void *x_dev, float *y_dev, int T, const q
 
 /* The plan qmat_run (route QMAT_ROUTE_AUTO) or qmat_run_ex with only a route would use for T
  * tokens; plan->route is the route taken.  Host only.
- * Errors: QMAT_EINVAL (null argument, bad route), QMAT_ESHAPE (T outside [1, 16]). */
+ * Errors: QMAT_EINVAL (null argument, bad route), QMAT_ESHAPE (T outside [1, 16] on the
+ * small-T routes, outside [1, 4194240] on the GEMM route). */
 int qmat_get_plan(qmat_t handle, int T, int route, qmat_plan *plan);
 
 /* Expand the packed matrix to fp32 w [M][K] (device), bit-exact: groupwise

@@ -294,6 +294,82 @@ def test_gemm_plan_and_graph_replay():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
+def test_gemm_split_k(fmt):
+    # k splits forced through explicit plans (ragged unit counts per split, ragged last token
+    # tile): each within tolerance, each repeatable bit for bit (fixed summation order, counters
+    # reset by the last wave), and an automatic split on a narrow matrix
+    M, K, Tmax = 200, 2048, 130
+    wl = _workload(fmt, M, K, Tmax, 77 + fmt)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    for T in (17, 64, 130):
+        sub = qi.Workload(wl.name, fmt, M, K, T, wl.codes, wl.scales, wl.x[:T])
+        for S in (2, 3, 5, 16):
+            say(f"gemm split fmt={fmt} T={T} S={S}")
+            plan = wq.qmat_plan(wq.QMAT_ROUTE_GEMM, 1, 4, S, 0, 1)
+            y1 = torch.full((T, M), float("nan"), device="cuda")
+            y2 = torch.full((T, M), float("nan"), device="cuda")
+            wq.qmat_run_plan(qm.handle, xd[:T], y1, plan, T=T)
+            wq.qmat_run_plan(qm.handle, xd[:T], y2, plan, T=T)
+            torch.cuda.synchronize()
+            assert torch.equal(y1, y2), (T, S)
+            _check_y(y1, sub, f"gemm split fmt={fmt} T={T} S={S}")
+    p = wq.qmat_get_plan(qm.handle, 64)
+    assert p.route == wq.QMAT_ROUTE_GEMM and p.splits > 1, p.as_tuple()
+    y = torch.full((64, M), float("nan"), device="cuda")
+    wq.qmat_run(qm.handle, xd[:64], y, T=64)
+    torch.cuda.synchronize()
+    _check_y(y, qi.Workload(wl.name, fmt, M, K, 64, wl.codes, wl.scales, wl.x[:64]), f"gemm auto split fmt={fmt}")
+    qm.close()
+
+
+@pytest.mark.parametrize("fmt", [4, 8])
+def test_gemm_split_k_bit_exact_and_graph_replay(fmt):
+    M, K, T = 130, 2048, 70
+    wl = _exact_workload(fmt, M, K, T, 19)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    y_ref, _ = oracle.gemv(fmt, wl.codes, wl.scales, wl.x)
+    plan = wq.qmat_plan(wq.QMAT_ROUTE_GEMM, 1, 4, 3, 0, 1)
+    y = torch.empty((T, M), device="cuda")
+    wq.qmat_run_plan(qm.handle, xd, y, plan, T=T)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref)
+    yg = torch.empty_like(y)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wq.qmat_run_plan(qm.handle, xd, yg, plan, T=T)
+    for i in range(3):
+        yg.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y), i
+        wq.qmat_run_plan(qm.handle, xd, y, plan, T=T)  # eager work between replays
+        torch.cuda.synchronize()
+    del g
+    qm.close()
+
+
+def test_gemm_split_k_argument_errors():
+    wl = _workload(4, 200, 512, 20, 5)
+    qm = wq.QMat(4, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    y = torch.empty((20, 200), device="cuda")
+    for S, status in [(0, wq.QMAT_EINVAL), (5, wq.QMAT_EINVAL), (17, wq.QMAT_EINVAL)]:  # NU = 4
+        with pytest.raises(wq.QmatError) as e:
+            wq.qmat_run_plan(qm.handle, xd, y, wq.qmat_plan(wq.QMAT_ROUTE_GEMM, 1, 4, S, 0, 1), T=20)
+        assert e.value.status == status, S
+    big = 4 << 20  # 16 Mi floats of workspace would be needed: rejected on the host, nothing launched
+    T = big // (4 * 256) + 64
+    xb = torch.zeros((T, 512), dtype=torch.bfloat16, device="cuda")
+    yb = torch.empty((T, 200), device="cuda")
+    with pytest.raises(wq.QmatError) as e:
+        wq.qmat_run_plan(qm.handle, xb, yb, wq.qmat_plan(wq.QMAT_ROUTE_GEMM, 1, 4, 4, 0, 1), T=T)
+    assert e.value.status == wq.QMAT_ESIZE
+    qm.close()
+
+
 def _exact_workload(fmt, M, K, T, seed):
     """Inputs whose products and partial sums are all exact in fp32: small integer bf16
     activations and power-of-two scales (FP8: integer-valued E4M3 bytes)."""

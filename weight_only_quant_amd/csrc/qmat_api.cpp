@@ -251,6 +251,7 @@ struct qmat {
     float *ws;
     size_t ws_floats;
     uint32_t *counters;
+    int64_t n_counters;
     int device;
     int cus;
     Plan plan[2][kMaxT + 1];  // [route - 1][tokens per launch]
@@ -336,6 +337,30 @@ int qmat_pack(int fmt, int64_t M, int64_t K, const void *codes, const void *scal
 
 namespace {
 
+// The GEMM route's share of a handle's workspace is capped (a model holds hundreds of narrow
+// matrices); automatic k splits are limited to what fits.
+constexpr size_t kGemmSplitWsFloats = (size_t)8 << 20;  // 32 MB
+
+// k splits of the GEMM route: the workgroups (row blocks x token tiles x S) run in waves of
+// two per CU, so the time goes as ceil(workgroups / slots) / S in units of one whole-K
+// workgroup, plus about 1% of that per split for the partial sums' second pass.  The
+// cheapest S with >= 4 units per split, at most kGemmMaxS, whose partials fit ws_cap floats.
+int gemm_auto_splits(int64_t NT, int64_t NU, int T, int cus, size_t ws_cap = kGemmSplitWsFloats)
+{
+    const int64_t slots = 2LL * cus, w0 = (int64_t)gemm_row_blocks((int)NT) * gemm_token_tiles(T);
+    int best = 1;
+    double best_cost = (double)((w0 + slots - 1) / slots);
+    for (int S = 2; S <= kGemmMaxS && NU / S >= 4; ++S) {
+        if (gemm_workspace_floats(T, (int)NT, S) > ws_cap) break;
+        const double cost = (double)((w0 * S + slots - 1) / slots) / S + 0.01 * S;
+        if (cost < best_cost - 1e-9) {
+            best = S;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 // A handle over M x K rows whose packed tiles start at (codes, scales): plans for every route
 // and T, and the split-K workspace they need.
 int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
@@ -354,6 +379,7 @@ int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *co
     h->ws = nullptr;
     h->counters = nullptr;
     h->ws_floats = 0;
+    h->n_counters = 0;
     if (hipGetDevice(&h->device) != hipSuccess) {
         delete h;
         return fail(QMAT_EHIP, "%s: hipGetDevice failed", who);
@@ -375,6 +401,14 @@ int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *co
             if (f > need_ws) need_ws = f;
         }
     if (h->Mpad <= 4096 && need_ws < (size_t)8 * kMaxT * h->Mpad) need_ws = (size_t)8 * kMaxT * h->Mpad;
+    // the GEMM route's automatic k splits (each within the cap by construction); beyond
+    // 2 workgroup waves of row blocks x token tiles no split pays
+    for (int ntt = 1; gemm_row_blocks((int)h->NT) * (int64_t)ntt <= 4LL * h->cus; ++ntt) {
+        const int T = ntt * kGemmTokens;
+        const size_t f = gemm_workspace_floats(T, (int)h->NT, gemm_auto_splits(h->NT, h->NU, T, h->cus));
+        if (f > need_ws) need_ws = f;
+    }
+    h->n_counters = h->NT;
     if (need_ws > 0) {
         h->ws_floats = need_ws;
         if (hipMalloc(&h->ws, h->ws_floats * sizeof(float)) != hipSuccess) {
@@ -382,13 +416,13 @@ int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *co
             delete h;
             return fail(QMAT_ENOMEM, "%s: workspace allocation failed", who);
         }
-        if (hipMalloc(&h->counters, (size_t)h->NT * sizeof(uint32_t)) != hipSuccess) {
+        if (hipMalloc(&h->counters, (size_t)h->n_counters * sizeof(uint32_t)) != hipSuccess) {
             (void)hipGetLastError();
             (void)hipFree(h->ws);
             delete h;
             return fail(QMAT_ENOMEM, "%s: counter allocation failed", who);
         }
-        if (hipMemset(h->counters, 0, (size_t)h->NT * sizeof(uint32_t)) != hipSuccess ||
+        if (hipMemset(h->counters, 0, (size_t)h->n_counters * sizeof(uint32_t)) != hipSuccess ||
             hipDeviceSynchronize() != hipSuccess) {
             (void)hipFree(h->ws);
             (void)hipFree(h->counters);
@@ -433,15 +467,24 @@ int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows)
 
 namespace {
 
-// The prefill GEMM route (any T >= 1; the automatic choice above the small-T limit).
-int run_gemm(qmat_t h, const void *x_dev, float *y_dev, int T, void *stream)
+// The prefill GEMM route (any T >= 1; the automatic choice above the small-T limit) with
+// S k splits (0: automatic).
+int run_gemm(qmat_t h, const void *x_dev, float *y_dev, int T, int S, void *stream)
 {
     if (T < 0 || T > kGemmMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d]", T, kGemmMaxT);
+    if (S < 0 || S > kGemmMaxS || S > h->NU)
+        return fail(QMAT_EINVAL, "qmat_run: GEMM splits %d outside [0, min(%d, units %lld)]", S, kGemmMaxS,
+                    (long long)h->NU);
     if (T == 0) return ok();
     if (!x_dev || !y_dev) return fail(QMAT_EINVAL, "qmat_run: null x or y");
     if (reinterpret_cast<uintptr_t>(x_dev) % 16) return fail(QMAT_EINVAL, "qmat_run: x not 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_run: y not 4-byte aligned");
+    if (S == 0) S = gemm_auto_splits(h->NT, h->NU, T, h->cus, h->ws_floats);
+    if (S > 1 && gemm_workspace_floats(T, (int)h->NT, S) > h->ws_floats)
+        return fail(QMAT_ESIZE, "qmat_run: %d GEMM splits at T=%d exceed the workspace", S, T);
     RunArgs a{};
+    a.ws = h->ws;
+    a.counters = h->counters;
     a.codes = h->codes;
     a.scales = h->scales;
     a.x = static_cast<const uint16_t *>(x_dev);
@@ -452,7 +495,7 @@ int run_gemm(qmat_t h, const void *x_dev, float *y_dev, int T, void *stream)
     a.T = T;
     a.NT = (int)h->NT;
     a.NU = (int)h->NU;
-    a.S = 1;
+    a.S = S;
     const hipError_t e = launch_gemm(h->fmt, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(QMAT_EHIP, "qmat_run: launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -460,7 +503,7 @@ int run_gemm(qmat_t h, const void *x_dev, float *y_dev, int T, void *stream)
 
 int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, void *stream)
 {
-    if (p.route == kRouteGemm) return run_gemm(h, x_dev, y_dev, T, stream);
+    if (p.route == kRouteGemm) return run_gemm(h, x_dev, y_dev, T, p.splits, stream);
     if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d]", T, kMaxT);
     if (T == 0) return ok();
     if (!x_dev || !y_dev) return fail(QMAT_EINVAL, "qmat_run: null x or y");
@@ -518,7 +561,7 @@ int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int
     if (!h) return fail(QMAT_EINVAL, "qmat_run: null handle");
     if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_GEMM) return fail(QMAT_EINVAL, "qmat_run: bad route %d", route);
     if (route == QMAT_ROUTE_GEMM || (route == QMAT_ROUTE_AUTO && T > kMaxT))
-        return run_gemm(h, x_dev, y_dev, T, stream);
+        return run_gemm(h, x_dev, y_dev, T, splits, stream);
     if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d] on this route", T, kMaxT);
     if (T == 0) return ok();
     if (!(waves == 0 || waves == 1 || waves == 2 || waves == 4 || waves == 8))
@@ -541,7 +584,10 @@ int qmat_run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const qmat_p
 {
     if (!h) return fail(QMAT_EINVAL, "qmat_run_plan: null handle");
     if (!plan) return fail(QMAT_EINVAL, "qmat_run_plan: null plan");
-    if (plan->route == QMAT_ROUTE_GEMM) return run_gemm(h, x_dev, y_dev, T, stream);
+    if (plan->route == QMAT_ROUTE_GEMM) {
+        if (plan->splits < 1) return fail(QMAT_EINVAL, "qmat_run_plan: splits must be >= 1");
+        return run_gemm(h, x_dev, y_dev, T, plan->splits, stream);
+    }
     if (plan->route != QMAT_ROUTE_VALU && plan->route != QMAT_ROUTE_MFMA)
         return fail(QMAT_EINVAL, "qmat_run_plan: route must be QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA or QMAT_ROUTE_GEMM");
     const Plan p{plan->route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma, plan->depth, plan->waves, plan->splits,
@@ -555,7 +601,7 @@ int qmat_get_plan(qmat_t h, int T, int route, qmat_plan *plan)
     if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_GEMM) return fail(QMAT_EINVAL, "qmat_get_plan: bad route %d", route);
     if (route == QMAT_ROUTE_GEMM || (route == QMAT_ROUTE_AUTO && T > kMaxT)) {
         if (T < 1 || T > kGemmMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kGemmMaxT);
-        *plan = qmat_plan{QMAT_ROUTE_GEMM, 1, 4, 1, 0, 1};
+        *plan = qmat_plan{QMAT_ROUTE_GEMM, 1, 4, gemm_auto_splits(h->NT, h->NU, T, h->cus, h->ws_floats), 0, 1};
         return ok();
     }
     if (T < 1 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kMaxT);
@@ -596,7 +642,7 @@ int qmat_dequant(qmat_t h, float *w_dev, void *stream)
 size_t qmat_workspace_bytes(qmat_t h)
 {
     if (!h) return 0;
-    return h->ws_floats * sizeof(float) + (h->counters ? (size_t)h->NT * sizeof(uint32_t) : 0);
+    return h->ws_floats * sizeof(float) + (h->counters ? (size_t)h->n_counters * sizeof(uint32_t) : 0);
 }
 
 void qmat_destroy(qmat_t h)
