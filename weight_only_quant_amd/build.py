@@ -9,7 +9,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmat.so")
 SOURCES = [os.path.join(CSRC, "qmat_api.cpp"), os.path.join(CSRC, "qmat_encode.cpp"),
-           os.path.join(CSRC, "qmat_kernels.hip"), os.path.join(CSRC, "qmat_logits.hip")]
+           os.path.join(CSRC, "qmat_kernels.hip"), os.path.join(CSRC, "qmat_gemm.hip"),
+           os.path.join(CSRC, "qmat_logits.hip")]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 (v_pk_*_f32) instructions.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

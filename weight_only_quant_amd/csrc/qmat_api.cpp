@@ -12,6 +12,7 @@
 
 #include "../../include/qmat.h"
 #include "qmat_host.h"
+#include "qmat_gemm.h"
 #include "qmat_kernels.h"
 #include "qmat_layout.h"
 #include "qmat_logits.h"

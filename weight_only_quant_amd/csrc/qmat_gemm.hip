@@ -1,0 +1,287 @@
+// gfx950 (CDNA4) prefill GEMM route of the weight-only quantized product y = x . W^T: T > 16
+// tokens (any T >= 1 on request), matrix-core tiles of 64 tokens x 256 rows, the same exact
+// code conversions as the small-T routes (qmat_device.h).
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "qmat_device.h"
+#include "qmat_gemm.h"
+#include "qmat_kernels.h"
+#include "qmat_layout.h"
+
+namespace qmatk {
+
+// Blocks [J0, J1) of a lane's unit slots, plus the scale slot with the last of them (a unit
+// fetched in parts), as ordinary cached loads: on the GEMM route every token tile reads the
+// same weights, and the workgroups that share them run together on one XCD, so they should
+// stay in its L2.
+template <int FMT, int J0, int J1, int NB, int XN>
+__device__ __forceinline__ void load_weight_blocks(const RunArgs &a, int tile, int u, uint32_t lane,
+                                                   Unit<NB, XN> &r)
+{
+    const int64_t tu = (int64_t)tile * a.NU + u;
+    const char *cb = reinterpret_cast<const char *>(a.codes) + tu * (NB * kBlockBytes);
+#pragma unroll
+    for (int j = J0; j < J1; ++j)
+        r.c[j] = *reinterpret_cast<const u32x4_t *>(cb + j * kBlockBytes + 16u * lane);
+    if constexpr (FMT != 8 && J1 == NB) {
+        const char *sb = reinterpret_cast<const char *>(a.scales) + tu * kScaleBlockBytes;
+        r.sc = *reinterpret_cast<const u32x4_t *>(sb + 16u * (lane & 15));
+    }
+}
+
+// ------------------------------------------------------------------ GEMM route (prefill, T > 16)
+
+// Prefill-sized products: the weights are reused by many tokens, so the MFMA does most of the
+// work and each unpacked weight fragment feeds kGemmTB / 16 matrix instructions.  A workgroup
+// is 4 waves; wave w owns row tile 4 * rb + w (64 rows), the workgroup a tile of kGemmTB
+// tokens.  Per 128-wide k unit the workgroup stages the token tile's activations in LDS (shared
+// by its 4 waves, double-buffered, one barrier per unit) while each wave streams its tile's
+// packed unit from HBM one unit ahead.  Per 64-group and 16-row slice m, two MFMAs sum
+// code * x into P and the group scale enters once per (token, row): acc += scale * P (exact
+// products, fp32 sums, as on the small-T routes).  Row-scaled FP8 has no group scale: the MFMA
+// accumulates straight into acc and the row scale is applied at the end.
+//
+// Two workgroups per CU (at most 256 vector registers per lane) so that one wave's unpack and
+// scale arithmetic overlaps the other's matrix instructions and memory waits.
+//
+// Block order: the hardware deals workgroups to the 8 XCDs in turn (block b to XCD b mod 8).
+// Each XCD is given a contiguous range of the work list (row block major, then token tile,
+// then k split), so the workgroups one XCD runs at the same time share row blocks (their
+// weights stay in that XCD's L2) and token tiles (their activations too).
+//
+// Split-K (a.S > 1, when row blocks x token tiles fill the chip's workgroup slots badly):
+// split sp takes units [NU sp / S, NU (sp+1) / S).  Split 0 writes its partial to y, split
+// sp > 0 stores its 64 x kGemmTB partial tile per wave to workspace region sp - 1 (ntt *
+// kGemmTB token rows x NT * 64 floats: no store needs a bounds test); a second kernel, ordered
+// after this one on the stream, adds regions 0 .. S-2 to y in split order (deterministic).  The
+// partials are megabytes here, so a second launch is cheaper than making them visible to other
+// workgroups inside this kernel.
+constexpr int kGemmTB = kGemmTokens;      // tokens per workgroup tile
+constexpr int kGemmRS = kUnitK + 8;       // LDS row stride of a staged token (bf16 elements)
+constexpr int kXcds = 8;
+
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(RunArgs a, int nrb, int ntt)
+{
+    constexpr int NB = Fmt<FMT>::NB, NTB = kGemmTB / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGemmTB * kGemmRS];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // block -> (row block, token tile, k split)
+    const int S = a.S;
+    const int64_t total = (int64_t)nrb * ntt * S, grid = (int64_t)gridDim.x * gridDim.y;
+    const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int xcd = (int)(b % kXcds);
+    const int64_t per = grid / kXcds, extra = grid % kXcds;
+    const int64_t wi = xcd * per + (xcd < extra ? xcd : extra) + b / kXcds;
+    if (wi >= total) return;
+    const int64_t q = wi / S;
+    const int sp = (int)(wi - q * S);
+    const int rb = (int)(q / ntt), tt = (int)(q - (int64_t)rb * ntt);
+    const int u0 = (int)((int64_t)a.NU * sp / S), u1 = (int)((int64_t)a.NU * (sp + 1) / S);
+    const int tile = 4 * rb + w;
+    const bool has_tile = tile < a.NT;
+    const int tok0 = tt * kGemmTB;
+
+    // activations of unit u for the token tile: thread i stages 16-byte pieces i, i + 256, ...
+    // of the kGemmTB x 128 block (token = piece / 16, k octet = piece % 16); rows past T and
+    // columns past K are zero
+    auto x_fetch = [&](int u, u32x4_t (&xr)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int piece = threadIdx.x + 256 * j, tq = piece >> 4, ko = piece & 15;
+            const int t = tok0 + tq, k = u * kUnitK + 8 * ko;
+            xr[j] = (t < a.T && k < a.K)
+                        ? *reinterpret_cast<const u32x4_t *>(a.x + (int64_t)t * a.K + k)
+                        : (u32x4_t){0u, 0u, 0u, 0u};
+        }
+    };
+    auto x_store = [&](int buf, const u32x4_t (&xr)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int piece = threadIdx.x + 256 * j, tq = piece >> 4, ko = piece & 15;
+            *reinterpret_cast<u32x4_t *>(&xs[buf][tq * kGemmRS + 8 * ko]) = xr[j];
+        }
+    };
+
+    f32x4_t acc[4][NTB];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < NTB; ++n) acc[m][n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    const int oct = lane >> 4, tl = lane & 15;
+
+    // group g of a unit: A fragments from LDS, then per row slice m: unpack, 2 MFMAs per
+    // token block, scale
+    auto compute = [&](const Unit<NB, 1> &cur, const uint16_t *xb, auto gc) {
+        constexpr int g = decltype(gc)::value;
+        const uint32_t *W = reinterpret_cast<const uint32_t *>(cur.c);
+        {
+            bf16x8_t A[2][NTB];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int n = 0; n < NTB; ++n)
+                    A[ks][n] = *reinterpret_cast<const bf16x8_t *>(
+                        &xb[(16 * n + tl) * kGemmRS + 32 * (2 * g + ks) + 8 * oct]);
+#define QMAT_GEMM_SLICE(MM, G)                                                                          \
+    {                                                                                                   \
+        uint32_t b0[4], b1[4];                                                                          \
+        bf16x8_of<FMT, 2 * (G), MM>(W, b0);                                                             \
+        bf16x8_of<FMT, 2 * (G) + 1, MM>(W, b1);                                                         \
+        const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, (u32x4_t){b0[0], b0[1], b0[2], b0[3]});        \
+        const bf16x8_t B1 = __builtin_bit_cast(bf16x8_t, (u32x4_t){b1[0], b1[1], b1[2], b1[3]});        \
+        if constexpr (FMT == 8) {                                                                       \
+            _Pragma("unroll") for (int n = 0; n < NTB; ++n) {                                           \
+                acc[MM][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][n], B0, acc[MM][n], 0, 0, 0); \
+                acc[MM][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][n], B1, acc[MM][n], 0, 0, 0); \
+            }                                                                                           \
+        } else {                                                                                        \
+            const float sf = group_scale(cur.sc, G, MM);                                                \
+            _Pragma("unroll") for (int n = 0; n < NTB; ++n) {                                           \
+                f32x4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][n], B0,                        \
+                                                                    (f32x4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
+                P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][n], B1, P, 0, 0, 0);                  \
+                _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[MM][n][i] = fmaf(sf, P[i], acc[MM][n][i]); \
+            }                                                                                           \
+        }                                                                                               \
+    }
+            if (g == 0) { QMAT_GEMM_SLICE(0, 0) QMAT_GEMM_SLICE(1, 0) QMAT_GEMM_SLICE(2, 0) QMAT_GEMM_SLICE(3, 0) }
+            else { QMAT_GEMM_SLICE(0, 1) QMAT_GEMM_SLICE(1, 1) QMAT_GEMM_SLICE(2, 1) QMAT_GEMM_SLICE(3, 1) }
+#undef QMAT_GEMM_SLICE
+        }
+    };
+
+    // unit u: prefetch unit u + 1 (activations to registers, weights to nxt), compute u from
+    // cur and LDS buffer u & 1, then stage the prefetched activations in the other buffer.
+    // The loop is unrolled by two so that cur and nxt swap roles without register copies.
+    // Q8 (8 KB units) fetches the second half of nxt only once group 0 of cur is done with
+    // its half (group 0 reads blocks 0-3, group 1 blocks 4-7), keeping 1.5 units live.
+    constexpr bool kHalves = FMT == 9;
+    u32x4_t xr[4];
+    auto step = [&](int u, Unit<NB, 1> &cur, Unit<NB, 1> &nxt) {
+        const int buf = (u - u0) & 1;
+        const bool more = u + 1 < u1;
+        if (more) {
+            x_fetch(u + 1, xr);
+            if (has_tile) load_weight_blocks<FMT, 0, kHalves ? NB / 2 : NB>(a, tile, u + 1, lane, nxt);
+        }
+        if (has_tile) {
+            compute(cur, xs[buf], std::integral_constant<int, 0>());
+            if constexpr (kHalves)
+                if (more) load_weight_blocks<FMT, NB / 2, NB>(a, tile, u + 1, lane, nxt);
+            compute(cur, xs[buf], std::integral_constant<int, 1>());
+        }
+        if (more) x_store(buf ^ 1, xr);
+        __syncthreads();
+    };
+
+    Unit<NB, 1> wa, wb;
+    x_fetch(u0, xr);
+    if (has_tile) load_weight_blocks<FMT, 0, NB>(a, tile, u0, lane, wa);
+    x_store(0, xr);
+    __syncthreads();
+    for (int u = u0; u < u1; u += 2) {
+        step(u, wa, wb);
+        if (u + 1 < u1) step(u + 1, wb, wa);
+    }
+    if (!has_tile) return;
+    f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
+    if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)tile * 16 + tl];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < NTB; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][n][i] *= rs[m];
+    // D[m][n]: lane holds tokens 16n + 4 * oct + i of row 16m + tl
+    if (sp == 0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int row = tile * kTileRows + 16 * m + tl;
+            if (row >= a.M) continue;
+#pragma unroll
+            for (int n = 0; n < NTB; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tok0 + 16 * n + 4 * oct + i;
+                    if (t < a.T) a.y[(int64_t)t * a.ldy + row] = acc[m][n][i];
+                }
+        }
+        return;
+    }
+    const int64_t ld = (int64_t)a.NT * kTileRows;  // workspace row stride (padded M)
+    float *wsp = a.ws + ((int64_t)(sp - 1) * ntt * kGemmTB + tok0) * ld + tile * kTileRows + tl;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < NTB; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wsp[(int64_t)(16 * n + 4 * oct + i) * ld + 16 * m] = acc[m][n][i];
+}
+
+// y[t][r] += ws[0][t][r] + ... + ws[S-2][t][r], added one partial at a time in split order.
+// One thread per (token, 4 consecutive padded rows): 16-byte partial loads, up to eight
+// partials in flight at a time.
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restrict__ ws, float *__restrict__ y,
+                                                         int T, int M, int ldy, int64_t ld, int64_t tpad, int S)
+{
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, per_t = ld / 4;
+    if (q >= (int64_t)T * per_t) return;
+    const int t = (int)(q / per_t);
+    const int r = 4 * (int)(q - (int64_t)t * per_t);
+    if (r >= M) return;
+    float *yr = y + (int64_t)t * ldy + r;
+    f32x4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = r + e < M ? yr[e] : 0.0f;
+    const f32x4_t *p = reinterpret_cast<const f32x4_t *>(ws + (int64_t)t * ld + r);
+    const int64_t step = tpad * ld / 4;  // one split region, in float4
+    const int n = S - 1;
+    for (int s0 = 0; s0 < n; s0 += 8) {
+        f32x4_t b[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = p[(int64_t)(s0 + j < n ? s0 + j : n - 1) * step];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (s0 + j < n) v += b[j];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (r + e < M) yr[e] = v[e];
+}
+
+// ------------------------------------------------------------------ launcher
+
+template <int FMT> static const void *gemm_kernel_ptr() { return reinterpret_cast<const void *>(&gemm_kernel<FMT>); }
+
+hipError_t launch_gemm(int fmt, const RunArgs &a, hipStream_t st)
+{
+    const void *k = fmt == 4 ? gemm_kernel_ptr<4>() : fmt == 5 ? gemm_kernel_ptr<5>()
+                  : fmt == 6 ? gemm_kernel_ptr<6>() : fmt == 8 ? gemm_kernel_ptr<8>()
+                  : fmt == 9 ? gemm_kernel_ptr<9>() : nullptr;
+    if (!k) return hipErrorInvalidValue;
+    RunArgs arg = a;
+    int nrb = gemm_row_blocks(a.NT), ntt = gemm_token_tiles(a.T);
+    // a 1-D grid while it fits the dispatch limits, else rows of 2^23 blocks (the last row
+    // partly idle); either way a multiple of 8 blocks per row keeps b mod 8 the XCD
+    const int64_t total = (int64_t)nrb * ntt * a.S, kRow = 1 << 23;
+    const unsigned gx = (unsigned)(total < kRow ? total : kRow), gy = (unsigned)((total + gx - 1) / gx);
+    void *args[] = {&arg, &nrb, &ntt};
+    hipError_t e = hipLaunchKernel(k, dim3(gx, gy), dim3(256), args, 0, st);
+    if (e != hipSuccess || a.S == 1) return e;
+    const float *ws = a.ws;
+    float *y = a.y;
+    int T = a.T, M = a.M, ldy = a.ldy, S = a.S;
+    int64_t ld = (int64_t)a.NT * kTileRows, tpad = (int64_t)ntt * kGemmTB;
+    const int64_t n = (int64_t)T * (ld / 4);
+    void *rargs[] = {&ws, &y, &T, &M, &ldy, &ld, &tpad, &S};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_reduce_kernel), dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), rargs, 0, st);
+}
+
+}  // namespace qmatk

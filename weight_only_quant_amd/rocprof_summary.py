@@ -9,7 +9,7 @@ trace:   per (kernel, grid size) dispatch count and mean/median/min duration.
 traffic: HBM bytes per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE (KiB per
          dispatch), each scaled by what the same counter reports for a device copy of known
          size (the counters need not cover every memory channel).  The JSON also records the
-         SHA-256 of the kernel source so that a later change to the kernels invalidates it.
+         SHA-256 of the small-T kernels' sources so that a later change to them invalidates it.
 """
 from __future__ import annotations
 
@@ -22,12 +22,17 @@ import os
 import statistics
 import sys
 
-KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "qmat_kernels.hip")
+# the sources of the small-T product kernels (the benchmark's timed kernels)
+KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", n)
+                  for n in ("qmat_kernels.hip", "qmat_device.h", "qmat_kernels.h", "qmat_layout.h")]
 
 
 def kernel_source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _short(name: str) -> str:
