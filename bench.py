@@ -202,7 +202,7 @@ def measure_epilogue(res, T, k, steps, warmup):
     return {"us_per_call": round(us, 3), "GBps": round(nb / us / 1e3, 1), "bytes": nb, "k": k}
 
 
-def measure_prefill(res, T, steps=20, warmup=3):
+def measure_prefill(res, T, steps=20, warmup=3, reference=False):
     """A prefill-sized product (the GEMM route) on the resident matrix with T synthetic bf16
     activation rows; throughput in TFLOP/s (2 T M K per call)."""
     import torch
@@ -224,9 +224,26 @@ def measure_prefill(res, T, steps=20, warmup=3):
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / steps * 1e3
     tf = 2.0 * T * wl.M * wl.K / us / 1e6
+    out = {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1), "pct_bf16_mfma_peak": round(100 * tf / 2500.0, 2),
+           "route": "gemm"}
+    if reference:
+        # context, not the product: the vendor bf16 GEMM (torch.matmul -> hipBLASLt) on an
+        # unquantized bf16 weight of the same shape, the practical matrix-core rate on this GPU
+        w = torch.randn((wl.M, wl.K), generator=g, device="cuda").to(torch.bfloat16)
+        for i in range(warmup):
+            torch.matmul(x, w.t())
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(steps):
+            torch.matmul(x, w.t())
+        b.record()
+        torch.cuda.synchronize()
+        ref_us = a.elapsed_time(b) / steps * 1e3
+        out["bf16_vendor_gemm_us"] = round(ref_us, 2)
+        out["bf16_vendor_gemm_TFLOPs"] = round(2.0 * T * wl.M * wl.K / ref_us / 1e6, 1)
+        del w
     del x, y
-    return {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1), "pct_bf16_mfma_peak": round(100 * tf / 2500.0, 2),
-            "route": "gemm"}
+    return out
 
 
 def cpu_baseline(res, T, target_s=12.0):
@@ -365,7 +382,7 @@ def main():
     # prefill-sized token counts (the GEMM route)
     for T2 in PREFILL_T:
         key = f"{name}_prefill_T{T2}"
-        extra[key] = measure_prefill(res, T2)
+        extra[key] = measure_prefill(res, T2, reference=True)
         log(f"[bench] {key}: {extra[key]}")
     res.close()
     del res

@@ -87,22 +87,33 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(RunArgs a, int nrb, int nt
     const int tok0 = tt * kGemmTB;
 
     // activations of unit u for the token tile: thread i stages 16-byte pieces i, i + 256, ...
-    // of the kGemmTB x 128 block (token = piece / 16, k octet = piece % 16); rows past T and
-    // columns past K are zero
-    auto x_fetch = [&](int u, u32x4_t (&xr)[4]) {
+    // of the kGemmTB x 128 block (token = piece / 16, k octet = piece % 16).  No zero fill:
+    // token rows past T are read as row T - 1 (their outputs are never written), and columns
+    // past K (the half unit of a K = 64 mod 128 matrix) are read inside the row, where they
+    // meet the zero codes of the padding group (x is finite by contract).  The row offsets are
+    // fixed for the whole kernel; a unit adds a wave-uniform column.
+    const int ko = threadIdx.x & 15;
+    int64_t xoff[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int piece = threadIdx.x + 256 * j, tq = piece >> 4, ko = piece & 15;
-            const int t = tok0 + tq, k = u * kUnitK + 8 * ko;
-            xr[j] = (t < a.T && k < a.K)
-                        ? *reinterpret_cast<const u32x4_t *>(a.x + (int64_t)t * a.K + k)
-                        : (u32x4_t){0u, 0u, 0u, 0u};
+    for (int j = 0; j < 4; ++j) {
+        const int t = tok0 + ((threadIdx.x + 256 * j) >> 4);
+        xoff[j] = (int64_t)(t < a.T ? t : a.T - 1) * a.K + 8 * ko;
+    }
+    auto x_fetch = [&](int u, u32x4_t (&xr)[4]) {
+        const int kb = u * kUnitK;
+        if (kb + kUnitK <= a.K) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xr[j] = *reinterpret_cast<const u32x4_t *>(a.x + xoff[j] + kb);
+        } else {
+            const int kc = (kb + 8 * ko < a.K ? kb + 8 * ko : a.K - 8) - 8 * ko;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xr[j] = *reinterpret_cast<const u32x4_t *>(a.x + xoff[j] + kc);
         }
     };
     auto x_store = [&](int buf, const u32x4_t (&xr)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int piece = threadIdx.x + 256 * j, tq = piece >> 4, ko = piece & 15;
+            const int tq = (threadIdx.x + 256 * j) >> 4;
             *reinterpret_cast<u32x4_t *>(&xs[buf][tq * kGemmRS + 8 * ko]) = xr[j];
         }
     };
