@@ -63,9 +63,10 @@ constexpr int kGemmRS = kUnitK + 8;       // LDS row stride of a staged token (b
 constexpr int kXcds = 8;
 
 template <int FMT>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(RunArgs a, int nrb, int ntt)
+__global__ __launch_bounds__(256, kGemmTB <= 64 ? 2 : 1) void gemm_kernel(RunArgs a, int nrb, int ntt)
 {
     constexpr int NB = Fmt<FMT>::NB, NTB = kGemmTB / 16;
+    constexpr int XP = kGemmTB * (kUnitK / 8) / 256;  // 16-byte activation pieces per thread and unit
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGemmTB * kGemmRS];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -93,26 +94,26 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(RunArgs a, int nrb, int nt
     // meet the zero codes of the padding group (x is finite by contract).  The row offsets are
     // fixed for the whole kernel; a unit adds a wave-uniform column.
     const int ko = threadIdx.x & 15;
-    int64_t xoff[4];
+    int64_t xoff[XP];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < XP; ++j) {
         const int t = tok0 + ((threadIdx.x + 256 * j) >> 4);
         xoff[j] = (int64_t)(t < a.T ? t : a.T - 1) * a.K + 8 * ko;
     }
-    auto x_fetch = [&](int u, u32x4_t (&xr)[4]) {
+    auto x_fetch = [&](int u, u32x4_t (&xr)[XP]) {
         const int kb = u * kUnitK;
         if (kb + kUnitK <= a.K) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xr[j] = *reinterpret_cast<const u32x4_t *>(a.x + xoff[j] + kb);
+            for (int j = 0; j < XP; ++j) xr[j] = *reinterpret_cast<const u32x4_t *>(a.x + xoff[j] + kb);
         } else {
             const int kc = (kb + 8 * ko < a.K ? kb + 8 * ko : a.K - 8) - 8 * ko;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xr[j] = *reinterpret_cast<const u32x4_t *>(a.x + xoff[j] + kc);
+            for (int j = 0; j < XP; ++j) xr[j] = *reinterpret_cast<const u32x4_t *>(a.x + xoff[j] + kc);
         }
     };
-    auto x_store = [&](int buf, const u32x4_t (&xr)[4]) {
+    auto x_store = [&](int buf, const u32x4_t (&xr)[XP]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < XP; ++j) {
             const int tq = (threadIdx.x + 256 * j) >> 4;
             *reinterpret_cast<u32x4_t *>(&xs[buf][tq * kGemmRS + 8 * ko]) = xr[j];
         }
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(RunArgs a, int nrb, int nt
     // Q8 (8 KB units) fetches the second half of nxt only once group 0 of cur is done with
     // its half (group 0 reads blocks 0-3, group 1 blocks 4-7), keeping 1.5 units live.
     constexpr bool kHalves = FMT == 9;
-    u32x4_t xr[4];
+    u32x4_t xr[XP];
     auto step = [&](int u, Unit<NB, 1> &cur, Unit<NB, 1> &nxt) {
         const int buf = (u - u0) & 1;
         const bool more = u + 1 < u1;
