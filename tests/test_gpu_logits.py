@@ -30,11 +30,11 @@ def gpu():
     wq.lib()
 
 
-# fp32 evaluation bound of the log-sum-exp: each lane sums at most a few dozen terms, the
-# partial sums meet in <= 12 pairwise combinations, each term and each rescaling carries one
-# expf error (a few ulp), and the final log is taken in double: relative error of the sum
-# <= 64 * 2^-24 (about 4e-6), i.e. the same absolute error on lse, plus the final rounding
-# of lse to fp32 (2^-24 |lse|).
+# fp32 evaluation bound of the log-sum-exp: each lane sums a few terms online, each term is
+# then rescaled by at most two more exponentials (wave, block) and summed over <= 64 lanes at
+# each level, each exponential and addition carrying an ulp-level error, and the last level and
+# the final log are taken in double: relative error of the sum <= 64 * 2^-24 (about 4e-6),
+# i.e. the same absolute error on lse, plus the final rounding of lse to fp32 (2^-24 |lse|).
 def _lse_tol(ref):
     return 64 * 2.0 ** -24 + 2.0 ** -23 * np.abs(ref)
 

@@ -74,11 +74,12 @@ template <int S> __device__ __forceinline__ void cmpx(float &v, int &r, bool kee
     r = take ? pr : r;
 }
 
-// bitonic sort of the wave's 64 (v, r) pairs, best first
+// bitonic sort of the wave's 64 (v, r) pairs, worst first (lane 63 holds the best: the order
+// a sorted list merges against without reversing it)
 template <int SIZE, int S> __device__ __forceinline__ void sort_stage(float &v, int &r, int lane)
 {
     if constexpr (S > 0) {
-        cmpx<S>(v, r, ((lane & S) == 0) == ((lane & SIZE) == 0));
+        cmpx<S>(v, r, ((lane & S) == 0) != ((lane & SIZE) == 0));
         sort_stage<SIZE, S / 2>(v, r, lane);
     }
 }
@@ -100,11 +101,10 @@ template <int S = 32> __device__ __forceinline__ void wave_clean(float &v, int &
     }
 }
 
-// L (sorted, best first) := the 64 best of L and S (both sorted, best first)
-__device__ __forceinline__ void wave_merge(float &lv, int &lr, float sv, int sr, int lane)
+// L (sorted, best first) := the 64 best of L and Q, with Q sorted worst first: lane by lane
+// the better of the two is the upper half of a bitonic sequence, which one clean sorts.
+__device__ __forceinline__ void wave_merge(float &lv, int &lr, float qv, int qr, int lane)
 {
-    const float qv = __shfl(sv, 63 - lane);
-    const int qr = __shfl(sr, 63 - lane);
     const bool qb = better(qv, qr, lv, lr);
     lv = qb ? qv : lv;
     lr = qb ? qr : lr;
@@ -113,7 +113,8 @@ __device__ __forceinline__ void wave_merge(float &lv, int &lr, float sv, int sr,
 
 // Merge the wave's 64 (v, r) pairs, one per lane, into the sorted list.  Only pairs that beat
 // the current k-th best can end in the top k: when none does (one compare and a wave vote), the
-// chunk costs nothing more; otherwise it is sorted (unless SORTED) and merged.  (Inserting a few
+// chunk costs nothing more; otherwise it is sorted worst first (unless SORTED: then it already
+// is) and merged.  (Inserting a few
 // candidates one at a time measured slower than the sort: each insertion is a chain of
 // vector-to-scalar round trips.)
 template <bool SORTED>
@@ -138,17 +139,40 @@ __device__ __forceinline__ void lane_cswap(float &va, int &ra, float &vb, int &r
     rb = sw ? tr : rb;
 }
 
-// (m, s) := combination of two online log-sum-exp states
-__device__ __forceinline__ void lse_combine(float &m, float &s, float pm, float ps)
+// The log-sum-exp state (max, sum of exp(v - max)) of the whole wave from the lanes' states:
+// the wave max, one exponential per lane to rescale its sum, then a sum over the lanes, all
+// through the lane exchanges above.  Every lane ends with the max; lane 0's sum is the one
+// used (its order of additions is the same every run).
+template <int S> __device__ __forceinline__ double lane_xor(double v)
 {
-    if (pm == -INFINITY) return;
-    if (m == -INFINITY) {
-        m = pm;
-        s = ps;
-        return;
-    }
-    const float mx = fmaxf(m, pm);
-    s = s * expf(m - mx) + ps * expf(pm - mx);
+    const int lo = lane_xor<S>(__double2loint(v)), hi = lane_xor<S>(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+
+template <typename F> __device__ __forceinline__ F wave_max(F v)
+{
+    v = fmax(v, lane_xor<1>(v));
+    v = fmax(v, lane_xor<2>(v));
+    v = fmax(v, lane_xor<4>(v));
+    v = fmax(v, lane_xor<8>(v));
+    v = fmax(v, lane_xor<16>(v));
+    return fmax(v, lane_xor<32>(v));
+}
+
+template <typename F> __device__ __forceinline__ F wave_sum(F v)
+{
+    v += lane_xor<1>(v);
+    v += lane_xor<2>(v);
+    v += lane_xor<4>(v);
+    v += lane_xor<8>(v);
+    v += lane_xor<16>(v);
+    return v + lane_xor<32>(v);
+}
+
+template <typename F> __device__ __forceinline__ void wave_lse(F &m, F &s)
+{
+    const F mx = wave_max(m);
+    s = wave_sum(m == -INFINITY ? F(0) : s * exp(m - mx));
     m = mx;
 }
 
@@ -194,11 +218,6 @@ __device__ __forceinline__ void lse_combine_d(double &m, double &s, double pm, d
     m = mx;
 }
 
-__device__ __forceinline__ double shfl_xor_d(double v, int off)
-{
-    const int lo = __shfl_xor(__double2loint(v), off), hi = __shfl_xor(__double2hiint(v), off);
-    return __hiloint2double(hi, lo);
-}
 
 // The sorted lists of the block's 16 waves (in s_v / s_r) merge pairwise in a fixed tree
 // (wave w takes wave w + step); wave 0 ends with the block's list in (lv, lr).
@@ -208,7 +227,7 @@ __device__ __forceinline__ void block_tree_merge(float (*s_v)[64], int (*s_r)[64
     for (int step = kWaves / 2; step > 0; step >>= 1) {
         __syncthreads();
         if (w < step) {
-            wave_merge(lv, lr, s_v[w + step][lane], s_r[w + step][lane], lane);
+            wave_merge(lv, lr, s_v[w + step][63 - lane], s_r[w + step][63 - lane], lane);
             s_v[w][lane] = lv;
             s_r[w][lane] = lr;
         }
@@ -267,12 +286,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
             for (int j = 0; j < 4; ++j) wave_take<false>(lv, lr, v[j], row[j], k, lane);
         }
     }
-    // wave log-sum-exp
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float pm = __shfl_xor(m, off), ps = __shfl_xor(s, off);
-        lse_combine(m, s, pm, ps);
-    }
+    wave_lse(m, s);
     s_v[w][lane] = lv;
     s_r[w][lane] = lr;
     if (lane == 0) {
@@ -287,15 +301,10 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
     int32_t *pi = a.part_i + ((int64_t)t * a.B + b) * kc;
     uint32_t sink = 0;
     if (w == 0) {
-        // the 16 wave states: lanes 0..15 hold them, a butterfly combines (lane 0's result is
-        // the same every run: a fixed sequence of operations)
+        // the 16 wave states: lanes 0..15 hold them, lane 0 ends with the block's state
         m = lane < kWaves ? s_m[lane] : -INFINITY;
         s = lane < kWaves ? s_s[lane] : 0.f;
-#pragma unroll
-        for (int off = 1; off < kWaves; off <<= 1) {
-            const float pm = __shfl_xor(m, off), ps = __shfl_xor(s, off);
-            lse_combine(m, s, pm, ps);
-        }
+        wave_lse(m, s);
         if (lane < kc) {
             sink |= publish(pf + 2 + lane, lv);
             sink |= publish(pi + lane, lr);
@@ -358,8 +367,10 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
         // top-k: wave w takes the block lists w, w + 16, ... of the chunk (lane i reads entry i)
         if (k > 0)
             for (int e = w; e < n; e += kWaves) {
-                const float cv = lane < kc ? st_f[e * stride_f + 2 + lane] : -INFINITY;
-                const int cr = lane < kc ? st_i[e * kc + lane] : kRowEmpty;
+                // the block's list, read worst first (empty slots, then entry kc - 1 ... 0)
+                const int q = 63 - lane;
+                const float cv = q < kc ? st_f[e * stride_f + 2 + q] : -INFINITY;
+                const int cr = q < kc ? st_i[e * kc + q] : kRowEmpty;
                 wave_take<true>(lv, lr, cv, cr, k, lane);
             }
     }
@@ -374,17 +385,8 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
             a.vals[(int64_t)t * kc + lane] = lv;
             a.ids[(int64_t)t * kc + lane] = lr == kRowEmpty ? -1 : (a.index ? a.index[lr] : lr);
         }
-        // the 64 lane states combine in a fixed butterfly
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const double pm = shfl_xor_d(tm, off), ps = shfl_xor_d(ts, off);
-            // both lanes of a pair combine the same two states in the same order
-            double m1 = (lane & off) ? pm : tm, s1 = (lane & off) ? ps : ts;
-            const double m2 = (lane & off) ? tm : pm, s2 = (lane & off) ? ts : ps;
-            lse_combine_d(m1, s1, m2, s2);
-            tm = m1;
-            ts = s1;
-        }
+        // the 64 lane states (in double), lane 0 ends with the token's
+        wave_lse(tm, ts);
         if (lane == 0 && a.lse) a.lse[t] = (float)(tm + log(ts));
         if (lane == 0) __hip_atomic_store(&a.counter[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
