@@ -47,9 +47,12 @@ __device__ __forceinline__ void load_weight_blocks(const RunArgs &a, int tile, i
 // scale arithmetic overlaps the other's matrix instructions and memory waits.
 //
 // Block order: the hardware deals workgroups to the 8 XCDs in turn (block b to XCD b mod 8).
-// Each XCD is given a contiguous range of the work list (row block major, then token tile,
-// then k split), so the workgroups one XCD runs at the same time share row blocks (their
-// weights stay in that XCD's L2) and token tiles (their activations too).
+// Each XCD is given a contiguous range of the work list, which is ordered in patches of 8 row
+// blocks x 8 token tiles (then k splits), so the ~64 workgroups one XCD runs at the same time
+// share 8 row blocks' weights and 8 token tiles' activations through its L2: a row block's
+// weights are fetched once per 8 token tiles and a token tile's activations once per 8 row
+// blocks (row-block-major order re-read the activations for every pair of row blocks, plain
+// order re-read the weights on every XCD).
 //
 // Split-K (a.S > 1, when row blocks x token tiles fill the chip's workgroup slots badly):
 // split sp takes units [NU sp / S, NU (sp+1) / S).  Split 0 writes its partial to y, split
@@ -79,9 +82,20 @@ __global__ __launch_bounds__(256, kGemmTB <= 64 ? 2 : 1) void gemm_kernel(RunArg
     const int64_t per = grid / kXcds, extra = grid % kXcds;
     const int64_t wi = xcd * per + (xcd < extra ? xcd : extra) + b / kXcds;
     if (wi >= total) return;
-    const int64_t q = wi / S;
-    const int sp = (int)(wi - q * S);
-    const int rb = (int)(q / ntt), tt = (int)(q - (int64_t)rb * ntt);
+    // the work list in patches of Pr row blocks x Pt token tiles (x S splits), patch rows
+    // outermost: about one patch (64 workgroups) runs on an XCD at a time
+    constexpr int Pt = 8, Pr = 8;
+    const int64_t prow = (int64_t)Pr * ntt * S;
+    const int pr = (int)(wi / prow);
+    const int64_t r1 = wi - pr * prow;
+    const int R = nrb - pr * Pr < Pr ? nrb - pr * Pr : Pr;  // row blocks in this patch row
+    const int pt = (int)(r1 / ((int64_t)R * Pt * S));
+    const int64_t r2 = r1 - (int64_t)pt * R * Pt * S;
+    const int C = ntt - pt * Pt < Pt ? ntt - pt * Pt : Pt;  // token tiles in this patch
+    const int ir = (int)(r2 / ((int64_t)C * S));
+    const int64_t r3 = r2 - (int64_t)ir * C * S;
+    const int it = (int)(r3 / S), sp = (int)(r3 - (int64_t)it * S);
+    const int rb = pr * Pr + ir, tt = pt * Pt + it;
     const int u0 = (int)((int64_t)a.NU * sp / S), u1 = (int)((int64_t)a.NU * (sp + 1) / S);
     const int tile = 4 * rb + w;
     const bool has_tile = tile < a.NT;
