@@ -36,11 +36,11 @@ __device__ __forceinline__ void load_weight_blocks(const RunArgs &a, int tile, i
 // Prefill-sized products: the weights are reused by many tokens, so the MFMA does most of the
 // work and each unpacked weight fragment feeds kGemmTB / 16 matrix instructions.  A workgroup
 // is 4 waves; wave w owns row tile 4 * rb + w (64 rows), the workgroup a tile of kGemmTB
-// tokens.  Per 128-wide k unit the workgroup stages the token tile's activations in LDS (shared
-// by its 4 waves, double-buffered, one barrier per unit) while each wave streams its tile's
-// packed unit from HBM one unit ahead.  Per 64-group and 16-row slice m, two MFMAs sum
-// code * x into P and the group scale enters once per (token, row): acc += scale * P (exact
-// products, fp32 sums, as on the small-T routes).  Row-scaled FP8 has no group scale: the MFMA
+// tokens.  Per 128-wide k unit the workgroup loads the token tile's activations straight from
+// global memory into LDS (shared by its 4 waves, double-buffered, one barrier per unit) while
+// each wave streams its tile's packed unit one unit ahead.  Per 64-group and 16-row slice m,
+// two MFMAs sum code * x into P and the group scale enters once per (token, row):
+// acc += scale * P (exact products, fp32 sums, as on the small-T routes).  Row-scaled FP8 has no group scale: the MFMA
 // accumulates straight into acc and the row scale is applied at the end.
 //
 // Two workgroups per CU (at most 256 vector registers per lane) so that one wave's unpack and
@@ -62,7 +62,6 @@ __device__ __forceinline__ void load_weight_blocks(const RunArgs &a, int tile, i
 // partials are megabytes here, so a second launch is cheaper than making them visible to other
 // workgroups inside this kernel.
 constexpr int kGemmTB = kGemmTokens;      // tokens per workgroup tile
-constexpr int kGemmRS = kUnitK + 8;       // LDS row stride of a staged token (bf16 elements)
 constexpr int kXcds = 8;
 
 template <int FMT>
@@ -70,7 +69,7 @@ __global__ __launch_bounds__(256, kGemmTB <= 64 ? 2 : 1) void gemm_kernel(RunArg
 {
     constexpr int NB = Fmt<FMT>::NB, NTB = kGemmTB / 16;
     constexpr int XP = kGemmTB * (kUnitK / 8) / 256;  // 16-byte activation pieces per thread and unit
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGemmTB * kGemmRS];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGemmTB * kUnitK];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -107,29 +106,30 @@ __global__ __launch_bounds__(256, kGemmTB <= 64 ? 2 : 1) void gemm_kernel(RunArg
     // past K (the half unit of a K = 64 mod 128 matrix) are read inside the row, where they
     // meet the zero codes of the padding group (x is finite by contract).  The row offsets are
     // fixed for the whole kernel; a unit adds a wave-uniform column.
-    const int ko = threadIdx.x & 15;
+    // activations of unit u, loaded straight into LDS: wave instruction j of wave w fills LDS
+    // pieces 256 j + 64 w + lane (16 bytes each, contiguous); piece p holds token p / 16 and
+    // k octet (p % 16) ^ (token % 16), an XOR swizzle that keeps the fragment reads free of
+    // bank conflicts without padding.
+    const int lane16 = threadIdx.x & 15;
     int64_t xoff[XP];
+    int xko[XP];
 #pragma unroll
     for (int j = 0; j < XP; ++j) {
-        const int t = tok0 + ((threadIdx.x + 256 * j) >> 4);
-        xoff[j] = (int64_t)(t < a.T ? t : a.T - 1) * a.K + 8 * ko;
+        const int tq = (threadIdx.x + 256 * j) >> 4;
+        const int t = tok0 + tq;
+        xko[j] = lane16 ^ (tq & 15);
+        xoff[j] = (int64_t)(t < a.T ? t : a.T - 1) * a.K + 8 * xko[j];
     }
-    auto x_fetch = [&](int u, u32x4_t (&xr)[XP]) {
+    auto x_dma = [&](int u, int buf) {
         const int kb = u * kUnitK;
-        if (kb + kUnitK <= a.K) {
-#pragma unroll
-            for (int j = 0; j < XP; ++j) xr[j] = *reinterpret_cast<const u32x4_t *>(a.x + xoff[j] + kb);
-        } else {
-            const int kc = (kb + 8 * ko < a.K ? kb + 8 * ko : a.K - 8) - 8 * ko;
-#pragma unroll
-            for (int j = 0; j < XP; ++j) xr[j] = *reinterpret_cast<const u32x4_t *>(a.x + xoff[j] + kc);
-        }
-    };
-    auto x_store = [&](int buf, const u32x4_t (&xr)[XP]) {
 #pragma unroll
         for (int j = 0; j < XP; ++j) {
-            const int tq = (threadIdx.x + 256 * j) >> 4;
-            *reinterpret_cast<u32x4_t *>(&xs[buf][tq * kGemmRS + 8 * ko]) = xr[j];
+            int64_t off = xoff[j] + kb;
+            if (kb + kUnitK > a.K) {
+                const int kc = kb + 8 * xko[j] < a.K ? kb : a.K - 8 - 8 * xko[j];
+                off = xoff[j] + kc;
+            }
+            __builtin_amdgcn_global_load_lds(a.x + off, &xs[buf][(256 * j + 64 * w) * 8], 16, 0, 0);
         }
     };
 
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256, kGemmTB <= 64 ? 2 : 1) void gemm_kernel(RunArg
 #pragma unroll
                 for (int n = 0; n < NTB; ++n)
                     A[ks][n] = *reinterpret_cast<const bf16x8_t *>(
-                        &xb[(16 * n + tl) * kGemmRS + 32 * (2 * g + ks) + 8 * oct]);
+                        &xb[(16 * n + tl) * kUnitK + 8 * ((4 * (2 * g + ks) + oct) ^ tl)]);
 #define QMAT_GEMM_SLICE(MM, G)                                                                          \
     {                                                                                                   \
         uint32_t b0[4], b1[4];                                                                          \
@@ -188,12 +188,11 @@ __global__ __launch_bounds__(256, kGemmTB <= 64 ? 2 : 1) void gemm_kernel(RunArg
     // Q8 (8 KB units) fetches the second half of nxt only once group 0 of cur is done with
     // its half (group 0 reads blocks 0-3, group 1 blocks 4-7), keeping 1.5 units live.
     constexpr bool kHalves = FMT == 9;
-    u32x4_t xr[XP];
     auto step = [&](int u, Unit<NB, 1> &cur, Unit<NB, 1> &nxt) {
         const int buf = (u - u0) & 1;
         const bool more = u + 1 < u1;
         if (more) {
-            x_fetch(u + 1, xr);
+            x_dma(u + 1, buf ^ 1);
             if (has_tile) load_weight_blocks<FMT, 0, kHalves ? NB / 2 : NB>(a, tile, u + 1, lane, nxt);
         }
         if (has_tile) {
@@ -202,14 +201,14 @@ __global__ __launch_bounds__(256, kGemmTB <= 64 ? 2 : 1) void gemm_kernel(RunArg
                 if (more) load_weight_blocks<FMT, NB / 2, NB>(a, tile, u + 1, lane, nxt);
             compute(cur, xs[buf], std::integral_constant<int, 1>());
         }
-        if (more) x_store(buf ^ 1, xr);
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's activation loads are in LDS
         __syncthreads();
     };
 
     Unit<NB, 1> wa, wb;
-    x_fetch(u0, xr);
+    x_dma(u0, 0);
     if (has_tile) load_weight_blocks<FMT, 0, NB>(a, tile, u0, lane, wa);
-    x_store(0, xr);
+    __builtin_amdgcn_s_waitcnt(0xF70);
     __syncthreads();
     for (int u = u0; u < u1; u += 2) {
         step(u, wa, wb);
