@@ -310,7 +310,7 @@ def main():
     global EAGER_ONLY
     EAGER_ONLY = args.eager_only
     if args.gpus != 1:
-        log("bench.py: this build runs on one GPU only (the product shards by rows with no "
+        log("bench.py: the benchmark runs on one GPU only (the product shards by rows with no "
             "collective; see the design notes); --gpus must be 1")
         sys.exit(2)
 
