@@ -198,14 +198,14 @@ def test_row_views(fmt):
     # range, a single partial tile) give the sub-matrix's product and dequantization; the view
     # outlives its parent handle
     M, K, T = 455, 704, 5
-    wl = _workload(fmt, M, K, T, 41 + fmt)
+    wl = _workload(fmt, M, K, 40, 41 + fmt)
     qm = wq.QMat(fmt, wl.codes, wl.scales)
     xd = _x_dev(wl.x)
     for row0, rows in [(0, 192), (192, 263), (128, 64), (448, 7), (64, 1), (0, M)]:
         say(f"view fmt={fmt} rows [{row0}, {row0 + rows})")
         v = wq.qmat_create_view(qm.handle, row0, rows)
         sub = qi.Workload("v", fmt, rows, K, T, wl.codes[row0:row0 + rows], wl.scales[row0:row0 + rows], wl.x)
-        for Tr in (1, T):
+        for Tr in (1, T, 40):  # 40: the prefill GEMM route on the view
             y = torch.full((Tr, rows), float("nan"), device="cuda")
             wq.qmat_run(v, xd[:Tr], y, T=Tr)
             torch.cuda.synchronize()
@@ -220,9 +220,9 @@ def test_row_views(fmt):
     v = wq.qmat_create_view(qm.handle, 256, 199)
     qm.close()  # the parent handle goes first; the packed blob (qm.packed) stays alive
     y = torch.empty((T, 199), device="cuda")
-    wq.qmat_run(v, xd, y, T=T)
+    wq.qmat_run(v, xd[:T], y, T=T)
     torch.cuda.synchronize()
-    _check_y(y, qi.Workload("v", fmt, 199, K, T, wl.codes[256:], wl.scales[256:], wl.x), "view after parent")
+    _check_y(y, qi.Workload("v", fmt, 199, K, T, wl.codes[256:], wl.scales[256:], wl.x[:T]), "view after parent")
     wq.qmat_destroy(v)
     parent = wq.qmat_create(fmt, M, K, qm.packed)
     for row0, rows in [(1, 64), (-64, 64), (0, 0), (448, 8), (512, 1)]:
@@ -321,6 +321,22 @@ def test_gemm_split_k(fmt):
     wq.qmat_run(qm.handle, xd[:64], y, T=64)
     torch.cuda.synchronize()
     _check_y(y, qi.Workload(wl.name, fmt, M, K, 64, wl.codes, wl.scales, wl.x[:64]), f"gemm auto split fmt={fmt}")
+    qm.close()
+
+
+@pytest.mark.parametrize("fmt", [4, 8])
+def test_gemm_block_order_ragged_patches(fmt):
+    # more than one 8 x 8 patch of (row block, token tile) work in both directions, each with a
+    # ragged remainder: 10 row blocks (37 tiles, the last partial) x 10 token tiles (T = 581)
+    M, K, T = 64 * 37 - 20, 256, 581
+    say(f"gemm patches fmt={fmt}")
+    wl = _workload(fmt, M, K, T, 123 + fmt)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    y = torch.full((T, M), float("nan"), device="cuda")
+    wq.qmat_run(qm.handle, _x_dev(wl.x), y, T=T)
+    torch.cuda.synchronize()
+    assert wq.qmat_get_plan(qm.handle, T).splits == 1
+    _check_y(y, wl, f"gemm patches fmt={fmt}")
     qm.close()
 
 
