@@ -79,8 +79,9 @@ class Resident:
 
 
 def time_run(res, T, steps, warmup):
-    """Eager stream launches.  Returns (ms_per_step over the timed region, mean and median
-    per-launch kernel ms from HIP events bracketing each launch on the launch stream)."""
+    """Eager stream launches.  Returns (ms_per_step over the timed region, and the per-launch
+    kernel ms from HIP events bracketing each launch on the launch stream: mean, median, 10th
+    and 90th percentiles)."""
     import torch
     import weight_only_quant_amd as wq
     stream = torch.cuda.current_stream()
@@ -100,7 +101,8 @@ def time_run(res, T, steps, warmup):
     torch.cuda.synchronize()
     total = start.elapsed_time(end)
     per = [a.elapsed_time(b) for a, b in ev]
-    return total / steps, float(np.mean(per)), float(np.median(per))
+    return (total / steps, float(np.mean(per)), float(np.median(per)), float(np.percentile(per, 10)),
+            float(np.percentile(per, 90)))
 
 
 def time_graph(res, T, steps, warmup):
@@ -146,6 +148,14 @@ def measured_traffic(workload):
         return None
 
 
+def qmat_packed_size(name):
+    """Packed bytes (codes + scales) of a benchmark workload."""
+    import qmat_inputs as qi
+    import weight_only_quant_amd as wq
+    c = qi.CONFIGS[name]
+    return wq.qmat_packed_bytes(c[0], c[1], c[2])
+
+
 def plan_str(res, T):
     import weight_only_quant_amd as wq
     p = wq.qmat_get_plan(res.handles[0], T)
@@ -158,12 +168,13 @@ EAGER_ONLY = False
 
 
 def measure(res, T, steps, warmup):
-    ms_e, k_mean, k_med = time_run(res, T, steps, warmup)
+    ms_e, k_mean, k_med, k_p10, k_p90 = time_run(res, T, steps, warmup)
     ms_g = ms_e if EAGER_ONLY else time_graph(res, T, steps, warmup)
     wl = res.wl
     ab = alg_bytes(wl.fmt, wl.M, wl.K, T)
     return {"us_per_call": round(ms_g * 1e3, 3), "eager_us_per_call": round(ms_e * 1e3, 3),
             "kernel_us": round(k_mean * 1e3, 3), "kernel_us_median": round(k_med * 1e3, 3),
+            "kernel_us_p10": round(k_p10 * 1e3, 3), "kernel_us_p90": round(k_p90 * 1e3, 3),
             "GBps": round(ab / (ms_g * 1e-3) / 1e9, 1), "kernel_GBps": round(ab / (k_mean * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * ab / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
             "bytes": ab, "plan": plan_str(res, T)}
@@ -274,23 +285,41 @@ def cpu_baseline(res, T, target_s=12.0):
                       f"(fp64 scalar C, {threads} threads)"}
 
 
-def read_ceiling_gbs():
-    """Achieved bandwidth of torch's sum over a 4 GiB buffer (a plain read stream), for context."""
-    import torch
-    buf = torch.ones((1 << 30,), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        buf.sum()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    n = 10
-    for _ in range(n):
-        buf.sum()
-    e.record()
-    torch.cuda.synchronize()
-    gbs = buf.numel() * 4 * n / (s.elapsed_time(e) * 1e-3) / 1e9
-    del buf
-    return round(gbs, 1)
+def read_ceilings(window_bytes):
+    """Practical read-bandwidth ceilings from the read-stream probe (libqmat_probe.so, a plain
+    16-byte-per-lane nontemporal read; best of a few launch shapes): over a 1 GiB buffer, and
+    over windows of the headline matrix's size rotated through that buffer (so each read
+    streams from HBM, as the rotated weight copies do)."""
+    from weight_only_quant_amd import probe
+    big, big_shapes = probe.best_read_gbs(1 << 30)
+    w = window_bytes // 1024 * 1024
+    win, _ = probe.best_read_gbs(1 << 30, window=w, reps=100)
+    return {"GBps_1GiB": big, "shapes_1GiB": big_shapes, "GBps_window": win, "window_bytes": w}
+
+
+def cpu_context(target_s=1.0):
+    """The host CPU model and the oracle's single-thread time on the small Q4 case (256 x 1024,
+    T = 1), the one the measurement plan times on one core."""
+    import oracle
+    import qmat_inputs as qi
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    wl = qi.config("q4_small_256x1024")
+    n, t0 = 0, time.time()
+    while True:
+        oracle.gemv(wl.fmt, wl.codes, wl.scales, wl.x[:1], nthreads=1)
+        n += 1
+        if time.time() - t0 >= target_s:
+            break
+    us = (time.time() - t0) / n * 1e6
+    return {"cpu_model": model, "host_threads": os.cpu_count(),
+            "q4_small_256x1024_T1_single_thread_us": round(us, 1)}
 
 
 def main():
@@ -410,8 +439,18 @@ def main():
             del r
             torch.cuda.empty_cache()
     if not args.no_ceiling:
-        out["read_stream_ceiling_GBps"] = read_ceiling_gbs()
-        log(f"[bench] torch.sum read stream: {out['read_stream_ceiling_GBps']} GB/s")
+        c = read_ceilings(qmat_packed_size(name))
+        out["read_stream_ceiling_GBps"] = c["GBps_1GiB"]
+        out["read_stream"] = c
+        out["pct_of_read_ceiling"] = round(100 * value / c["GBps_1GiB"], 2)
+        out["pct_of_same_size_read"] = round(100 * value / c["GBps_window"], 2)
+        for v in extra.values():
+            if "GBps" in v and "bytes" in v and "k" not in v:
+                v["pct_of_read_ceiling"] = round(100 * v["GBps"] / c["GBps_1GiB"], 2)
+        log(f"[bench] read stream: {c}")
+    if not args.no_cpu_baseline:
+        out["cpu_context"] = cpu_context()
+        log(f"[bench] cpu context {out['cpu_context']}")
     out["extra"] = extra
     print(json.dumps(out), flush=True)
 

@@ -138,3 +138,36 @@ def test_run_and_dequant_reject_null_handle():
     assert L.qmat_dequant(None, 16, None) == wq.QMAT_EINVAL
     assert L.qmat_workspace_bytes(None) == 0
     L.qmat_destroy(None)
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "qmat_probe.h")
+
+
+def test_probe_library_exports_its_header_and_validates():
+    from weight_only_quant_amd import probe
+    src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(qmat_probe_[a-z_]+)\s*\(", src)))
+    assert names == sorted(probe.SIGNATURES)
+    L = probe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # out words: one per lane of every launched wave
+    W = L.qmat_probe_read_out_words
+    assert W(2048, 1, 4, 0) == 256              # 2 waves: one 4-wave workgroup
+    assert W(1024 * 8, 2, 4, 0) == 256          # 4 waves: one
+    assert W(1024 * 9, 2, 4, 0) == 2 * 256      # 5 waves: two
+    assert W(1024 * 9, 2, 1, 0) == 5 * 64       # one-wave workgroups
+    assert W(1024 * 9, 0, 8, 100) == 13 * 512   # grid-stride: 100 waves in 8-wave workgroups
+    for args in [(0, 1, 4, 0), (1000, 1, 4, 0), (1024, 0, 4, 0), (1024, 65537, 4, 0), (-1024, 1, 4, 0),
+                 (1024, 1, 0, 0), (1024, 1, 9, 0), (1024, 1, 4, -1), (1024, 1, 4, (1 << 24) + 1)]:
+        assert W(*args) == 0, args
+    # host-side validation returns before any GPU call
+    R = L.qmat_probe_read
+    assert R(None, 1024, 1, 0, 1, 1, 0, 16, 64, None) == 1
+    assert R(8, 1024, 1, 0, 1, 1, 0, 16, 64, None) == 1          # misaligned buffer
+    assert R(16, 1000, 1, 0, 1, 1, 0, 16, 64, None) == 1         # not a multiple of 1 KB
+    assert R(16, 1024, 1, 0, 3, 1, 0, 16, 64, None) == 1         # unroll
+    assert R(16, 1024, 1, 0, 1, 1, 65537, 16, 64, None) == 1     # lds bytes
+    assert R(16, 1024, 1, 0, 1, 9, 0, 16, 64 * 9, None) == 1     # waves per workgroup
+    assert R(16, 1024, 1, 0, 1, 1, 0, None, 64, None) == 1       # null out
+    assert R(16, 1024, 1, 0, 1, 1, 0, 16, 63, None) == 1         # out too small

@@ -1,4 +1,5 @@
-"""Build the qmat shared library (libqmat.so) for gfx950 with hipcc, in place."""
+"""Build the qmat shared library (libqmat.so) and the read-stream probe used by the benchmark
+(libqmat_probe.so) for gfx950 with hipcc, in place."""
 from __future__ import annotations
 
 import os
@@ -11,6 +12,8 @@ LIB = os.path.join(HERE, "libqmat.so")
 SOURCES = [os.path.join(CSRC, "qmat_api.cpp"), os.path.join(CSRC, "qmat_encode.cpp"),
            os.path.join(CSRC, "qmat_kernels.hip"), os.path.join(CSRC, "qmat_gemm.hip"),
            os.path.join(CSRC, "qmat_logits.hip")]
+PROBE_LIB = os.path.join(HERE, "libqmat_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "qmat_probe.hip")]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 (v_pk_*_f32) instructions.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
@@ -26,14 +29,22 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *SOURCES]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    if verbose:
-        print(" ".join(cmd))
-    os.replace(tmp, LIB)
+    """Compile both libraries (two hipcc processes side by side); returns libqmat.so's path."""
+    jobs = []
+    for lib, sources in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        cmd = [hipcc(), *HIPCC_FLAGS, "-o", lib + ".tmp", *sources]
+        jobs.append((lib, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    errors = []
+    for lib, cmd, proc in jobs:
+        out, err = proc.communicate()
+        if proc.returncode != 0:
+            errors.append(f"hipcc failed for {os.path.basename(lib)}:\n{out}{err}")
+        elif verbose:
+            print(" ".join(cmd))
+    if errors:
+        raise RuntimeError("\n".join(errors))
+    for lib, _, _ in jobs:
+        os.replace(lib + ".tmp", lib)
     return LIB
 
 
