@@ -4,8 +4,12 @@
     python -m weight_only_quant_amd.rocprof_summary traffic --fetch <fetch.csv> --write <write.csv>
         --copy-fetch <copy_fetch.csv> --copy-write <copy_write.csv> --copy-bytes N
         --kernel <substring> --grid <grid size> --workload <name> --alg-bytes N --out traffic.json
+    python -m weight_only_quant_amd.rocprof_summary counters <counter_collection.csv> --names A,B,...
+        [--kernels <substring>,...] [--out summary.md]
 
 trace:   per (kernel, grid size) dispatch count and mean/median/min duration.
+counters: per (kernel, grid) dispatch count and the mean per dispatch of each named counter
+         (rocprofv3 --pmc output, one row per dispatch and counter).
 traffic: HBM bytes per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE (KiB per
          dispatch), each scaled by what the same counter reports for a device copy of known
          size (the counters need not cover every memory channel).  The JSON also records the
@@ -66,6 +70,20 @@ def counter_mean(path: str, counter: str, kernel: str, grid: str = None) -> floa
     return sum(vals) / len(vals)
 
 
+def counter_table(path: str, names, kernels=None):
+    """{(kernel, grid): {counter: mean per dispatch}} plus each key's dispatch count."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        k = _short(r["Kernel_Name"])
+        if r["Counter_Name"] not in names or (kernels and not any(s in k for s in kernels)):
+            continue
+        vals[(k, int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = {}
+    for key, d in vals.items():
+        out[key] = ({n: sum(v) / len(v) for n, v in d.items()}, max(len(v) for v in d.values()))
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -73,6 +91,12 @@ def main(argv=None):
     t.add_argument("csv")
     t.add_argument("--out")
     t.add_argument("--command", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--names", required=True)
+    c.add_argument("--kernels", default="")
+    c.add_argument("--out")
+    c.add_argument("--command", default="")
     f = sub.add_parser("traffic")
     for a in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "grid", "workload", "out"):
         f.add_argument("--" + a.replace("_", "-"), required=True)
@@ -86,6 +110,24 @@ def main(argv=None):
         for r in rows:
             lines.append(f"| {r['kernel']} | {r['grid']} | {r['workgroup']} | {r['calls']} | {r['mean_us']:.2f} | "
                          f"{r['median_us']:.2f} | {r['min_us']:.2f} |")
+        text = "\n".join(lines) + "\n"
+        if args.command:
+            text = f"Command: `{args.command}`\n\n" + text
+        if args.out:
+            with open(args.out, "w") as fh:
+                fh.write(text)
+        print(text)
+        return
+    if args.cmd == "counters":
+        names = args.names.split(",")
+        kernels = [k for k in args.kernels.split(",") if k]
+        table = counter_table(args.csv, names, kernels)
+        lines = ["| kernel | grid | dispatches | " + " | ".join(names) + " |",
+                 "|---|---|---|" + "---|" * len(names)]
+        for (k, g), (means, n) in sorted(table.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+            cells = [f"{means[x]:.4g}" if x in means else "" for x in names]
+            short = k if len(k) <= 64 else k[:48] + "..." + k[-12:]
+            lines.append(f"| {short} | {g} | {n} | " + " | ".join(cells) + " |")
         text = "\n".join(lines) + "\n"
         if args.command:
             text = f"Command: `{args.command}`\n\n" + text
