@@ -27,6 +27,9 @@
  *    After a failure, qmat_last_error() returns a message for the calling thread.
  *  - "host" pointers are ordinary CPU memory; "device" pointers are HIP device memory of
  *    the current device.  The library never frees caller memory.
+ *  - A handle (qmat_t, qmat_logits_t) belongs to the device that was current when it was
+ *    created; a call on it, or a view of it, made while another device is current returns
+ *    QMAT_EINVAL.
  *  - stream: a hipStream_t passed as void* (NULL = the null stream).  qmat_run and
  *    qmat_dequant are asynchronous on that stream, allocate nothing, never synchronize,
  *    and may be captured into a HIP graph.

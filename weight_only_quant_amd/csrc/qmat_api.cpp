@@ -260,6 +260,18 @@ struct qmat {
 
 namespace {
 
+// A handle's device memory belongs to the device that was current when it was created; every
+// call on it must find that device current again (its kernels launch on the current device).
+int device_ok(int device, const char *who)
+{
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(QMAT_EHIP, "%s: hipGetDevice failed", who);
+    if (cur != device)
+        return fail(QMAT_EINVAL, "%s: the handle belongs to device %d but device %d is current", who, device, cur);
+    return QMAT_OK;
+}
+
+
 // tokens one launch of a route handles when the call has T tokens
 int launch_tokens(int route, int T) { return route == kRouteValu ? (T < kValuMaxT ? T : kValuMaxT) : T; }
 
@@ -456,6 +468,7 @@ int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows)
     if (!view) return fail(QMAT_EINVAL, "qmat_create_view: null view pointer");
     *view = nullptr;
     if (!parent) return fail(QMAT_EINVAL, "qmat_create_view: null parent");
+    if (const int st = device_ok(parent->device, "qmat_create_view")) return st;
     if (row0 < 0 || rows < 1 || row0 % kTileRows || row0 + rows > parent->M)
         return fail(QMAT_ESHAPE, "qmat_create_view: rows [%lld, %lld) not a 64-aligned range of the parent's %lld rows",
                     (long long)row0, (long long)(row0 + rows), (long long)parent->M);
@@ -480,6 +493,7 @@ int run_gemm(qmat_t h, const void *x_dev, float *y_dev, int T, int S, void *stre
     if (!x_dev || !y_dev) return fail(QMAT_EINVAL, "qmat_run: null x or y");
     if (reinterpret_cast<uintptr_t>(x_dev) % 16) return fail(QMAT_EINVAL, "qmat_run: x not 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_run: y not 4-byte aligned");
+    if (const int st = device_ok(h->device, "qmat_run")) return st;
     if (S == 0) S = gemm_auto_splits(h->NT, h->NU, T, h->cus, h->ws_floats);
     if (S > 1 && gemm_workspace_floats(T, (int)h->NT, S) > h->ws_floats)
         return fail(QMAT_ESIZE, "qmat_run: %d GEMM splits at T=%d exceed the workspace", S, T);
@@ -511,6 +525,7 @@ int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, vo
     if (reinterpret_cast<uintptr_t>(x_dev) % 16) return fail(QMAT_EINVAL, "qmat_run: x not 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_run: y not 4-byte aligned");
     if (p.route != kRouteValu && p.route != kRouteMfma) return fail(QMAT_EINVAL, "qmat_run: bad route");
+    if (const int st = device_ok(h->device, "qmat_run")) return st;
     if (!(p.waves == 1 || p.waves == 2 || p.waves == 4 || p.waves == 8))
         return fail(QMAT_EINVAL, "qmat_run: waves must be 1, 2, 4 or 8");
     if (p.depth < 1 || p.depth > kMaxDepth) return fail(QMAT_EINVAL, "qmat_run: depth must be 1..%d", kMaxDepth);
@@ -627,6 +642,7 @@ int qmat_dequant(qmat_t h, float *w_dev, void *stream)
     if (!h) return fail(QMAT_EINVAL, "qmat_dequant: null handle");
     if (!w_dev) return fail(QMAT_EINVAL, "qmat_dequant: null output");
     if (reinterpret_cast<uintptr_t>(w_dev) % 16) return fail(QMAT_EINVAL, "qmat_dequant: output not 16-byte aligned");
+    if (const int st = device_ok(h->device, "qmat_dequant")) return st;
     DequantArgs a;
     a.codes = h->codes;
     a.scales = h->scales;
@@ -666,6 +682,7 @@ struct qmat_logits {
     float *part_f;
     int32_t *part_i;
     uint32_t *counter;
+    int device;
 };
 
 extern "C" {
@@ -687,6 +704,10 @@ int qmat_logits_create(qmat_logits_t *e, int64_t M, int max_T, int max_k)
     h->part_f = nullptr;
     h->part_i = nullptr;
     h->counter = nullptr;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return fail(QMAT_EHIP, "qmat_logits_create: hipGetDevice failed");
+    }
     const size_t nf = (size_t)max_T * h->B * (2 + max_k), ni = (size_t)max_T * h->B * (max_k > 0 ? max_k : 1);
     if (hipMalloc(&h->part_f, nf * sizeof(float)) != hipSuccess ||
         hipMalloc(&h->part_i, ni * sizeof(int32_t)) != hipSuccess ||
@@ -719,6 +740,7 @@ int qmat_logits_run(qmat_logits_t e, const float *y_dev, int64_t ldy, int T, int
     if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_logits_run: y not 4-byte aligned");
     if (ldy < e->M) return fail(QMAT_ESHAPE, "qmat_logits_run: ldy=%lld < M=%lld", (long long)ldy, (long long)e->M);
     if (k > 0 && (!top_vals_dev || !top_ids_dev)) return fail(QMAT_EINVAL, "qmat_logits_run: null top-k output");
+    if (const int st = device_ok(e->device, "qmat_logits_run")) return st;
     LogitsArgs a;
     a.y = y_dev;
     a.ldy = ldy;
