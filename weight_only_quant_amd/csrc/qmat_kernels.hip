@@ -196,6 +196,16 @@ __device__ __forceinline__ u32x4_t load_x8(const RunArgs &a, int kb, uint32_t la
     return *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const char *>(a.x) + 2 * (int64_t)kc + lane_off);
 }
 
+// The same 8 activations through a raw buffer resource over x (T x K bf16): lane_off past
+// the end of the buffer (kPastEnd) returns zeros and makes no memory request.
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // raw 32-bit data format (gfx9 resource word 3)
+constexpr uint32_t kPastEnd = 0x7FFFFFF0u;
+__device__ __forceinline__ u32x4_t load_x8_buf(const RunArgs &a, __amdgpu_buffer_rsrc_t xr, int kb, uint32_t lane_off)
+{
+    const int kc = kb < a.K - 32 ? kb : a.K - 32;
+    return __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(lane_off + 2u * (uint32_t)kc), 0, 0);
+}
+
 // Software pipeline over a wave's units [u0, u1): a ring of D units in flight; a slot is
 // refilled with unit u + D right after unit u has been consumed from it.  mid() runs once
 // after the first loads are issued (their latency hides it).  The steady-state loop has no
@@ -380,9 +390,12 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
     const Slice s = make_slice(a);
     const uint32_t lane = threadIdx.x & 63;
     const int tok = lane & 15, oct = lane >> 4;
-    // A rows of tokens >= T only feed D rows that are never stored: load a valid token instead
-    const int tok_c = tok < a.T ? tok : a.T - 1;
-    const uint32_t xoff = 2u * (uint32_t)(tok_c * a.K) + 16u * oct;
+    // A rows of tokens >= T only feed D rows that are never stored: those lanes read the
+    // activations through a buffer resource at an offset past its end, which returns zeros
+    // without a memory request (at T = 1, 15 lanes in 16)
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.x), (short)0, 2 * a.T * a.K, kRawBufferWord3);
+    const uint32_t xoff = tok < a.T ? 2u * (uint32_t)(tok * a.K) + 16u * oct : kPastEnd;
     f32x4_t acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -393,7 +406,7 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
             load_weights<FMT>(a, s.tile, u, lane, r);
 #pragma unroll
             for (int ka = 0; ka < 4; ++ka)
-                r.x[ka] = load_x8(a, u * kUnitK + 32 * ka, xoff);
+                r.x[ka] = load_x8_buf(a, xr, u * kUnitK + 32 * ka, xoff);
         },
         [&]() {},
         [&](const Unit<NB, XN> &U, int) {
