@@ -180,19 +180,23 @@ struct Plan {
 //  - Matrices of at least 2048 row tiles: one tile per workgroup, never split; 4 waves share a
 //    tile's k units at T = 1 (a single token leaves registers for two units in flight), 1 wave
 //    otherwise.
-//  - At least one tile per compute unit: 4 waves per workgroup, two units in flight at T = 1 and
-//    one above (the multi-token accumulators would otherwise halve the resident waves).  When
+//  - At least one tile per compute unit: 4 waves per workgroup, two units in flight up to T = 4
+//    and one above (from T = 12 the multi-token accumulators of a two-unit ring leave too few
+//    resident waves: 25-30% slower; at T = 2-4 the ring is 6-7% faster, T = 6-8 tie).  When
 //    the tile count is not a multiple of the compute-unit count, the leftover tiles would form a
 //    second, nearly empty round of workgroups on a few compute units (measured: 34816 rows take
 //    4 us longer than 32768).  Those trailing tiles are instead split along K over up to 8
-//    workgroups each, enough to give every compute unit a share, and dispatched first; the whole
-//    grid stays within one round of resident workgroups.
-//  - Fewer tiles than compute units: 4 waves per workgroup up to T = 4, 8 beyond, and every tile
-//    split along K across workgroups until about 8 waves per compute unit exist, at most 3 ways
-//    (every split adds a round of partial-sum traffic and a last-arrival reduction at the end of
-//    the kernel; 4 and more splits measured slower on every shape).  Two units in flight per
-//    wave, except with 8-wave workgroups at T > 1, whose register footprint would leave room
-//    for only one workgroup per compute unit.
+//    workgroups each, enough to give every compute unit a share, and dispatched first.  The
+//    short trailing workgroups may run beyond one round of resident workgroups (two-unit rings
+//    at T = 2-4 leave room for two 4-wave workgroups per compute unit, which the whole tiles
+//    fill), as long as the whole tiles themselves fit in one round.
+//  - Fewer tiles than compute units: every tile split along K across workgroups until about 8
+//    waves per compute unit exist, at most 3 ways (every split adds a round of partial-sum
+//    traffic and a last-arrival reduction at the end of the kernel; 4 and more splits measured
+//    slower on every shape).  4 waves per workgroup with two units in flight up to T = 4, 8
+//    waves with one unit beyond (a two-unit ring in 8-wave workgroups would leave room for only
+//    one workgroup per compute unit); but when 4 waves would get fewer than 8 units each (short
+//    K, e.g. 5120), 8 waves with one unit in flight at every T (2-3% faster at T = 1-4).
 //
 // Vector-ALU kernel (explicit requests only): two units in flight, 4 waves per workgroup,
 // single-wave workgroups for wide matrices, splits up to about 4 waves per compute unit.
@@ -204,7 +208,7 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
             p.waves = Tl == 1 ? 4 : 1;
         } else if (NT >= cus) {
             p.waves = 4;
-            p.depth = Tl == 1 ? 2 : 1;
+            p.depth = Tl <= 4 ? 2 : 1;
             while (p.waves > 1 && NU < (int64_t)p.waves) p.waves /= 2;
             const int64_t rem = NT % cus;
             if (rem > 0) {
@@ -212,14 +216,15 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
                 int64_t st = cus / rem;
                 if (st > 8) st = 8;
                 if (st > NU) st = NU;
-                while (st > 1 && (NT - rem) + rem * st > resident) --st;
+                if (NT - rem > resident) st = 1;
                 if (st > 1) {
                     p.tail_tiles = (int)rem;
                     p.tail_splits = (int)st;
                 }
             }
         } else {
-            p.waves = Tl <= 4 ? 4 : 8;
+            const bool short_k = NU < 8LL * 4 * 3;  // < 8 units per wave with 4 waves and 3 splits
+            p.waves = Tl <= 4 && !short_k ? 4 : 8;
             const int64_t target_waves = 8LL * cus;
             int64_t splits = (target_waves + NT * p.waves - 1) / (NT * p.waves);
             if (splits > 3) splits = 3;
@@ -227,7 +232,7 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
             if (splits < 1) splits = 1;
             p.splits = (int)splits;
             while (p.waves > 1 && NU < (int64_t)p.waves * p.splits) p.waves /= 2;
-            if (Tl > 1 && p.waves == 8) p.depth = 1;
+            if (p.waves == 8) p.depth = 1;
         }
         return p;
     }
