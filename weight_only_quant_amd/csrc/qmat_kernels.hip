@@ -35,6 +35,7 @@ namespace qmatk {
 
 struct Slice {
     int tile, sp, S, w, nw, u0, u1;
+    int sl, nsl;  // this wave's slice of the tile's k units and the number of slices
     int wsrow, wsld;  // the tile's first row and the row count of its workspace region
     int64_t wsoff;    // start of that region in the workspace (floats)
 };
@@ -66,6 +67,8 @@ __device__ __forceinline__ Slice make_slice(const RunArgs &a)
         s.wsoff = 0;
     }
     const int nsl = s.S * s.nw, sl = s.sp * s.nw + s.w;
+    s.sl = sl;
+    s.nsl = nsl;
     s.u0 = (int)(((int64_t)a.NU * sl) / nsl);
     s.u1 = (int)(((int64_t)a.NU * (sl + 1)) / nsl);
     return s;
@@ -400,9 +403,18 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
+    // Depth-2 kernels take every nsl-th unit of the tile from unit sl, so that the waves
+    // sharing a tile read neighbouring units at the same time (one moving region per tile
+    // instead of one per wave); depth-1 kernels take a contiguous run [u0, u1).
+    int ui0 = s.u0, ui1 = s.u1;
+    if constexpr (D_ == 2) {
+        ui0 = 0;
+        ui1 = s.sl < a.NU ? (a.NU - s.sl + s.nsl - 1) / s.nsl : 0;
+    }
     Unit<NB, XN> buf[D_];
-    pipeline<D_>(s.u0, s.u1, buf,
+    pipeline<D_>(ui0, ui1, buf,
         [&](Unit<NB, XN> &r, int u) {
+            if constexpr (D_ == 2) u = s.sl + u * s.nsl;
             load_weights<FMT>(a, s.tile, u, lane, r);
 #pragma unroll
             for (int ka = 0; ka < 4; ++ka)
