@@ -40,7 +40,11 @@ def kernel_source_sha256() -> str:
 
 
 def _short(name: str) -> str:
-    return name.replace("void qmatk::", "").replace("(qmatk::RunArgs)", "").replace("(qmatk::DequantArgs)", "")
+    n = name.replace("void qmatk::", "").replace("(qmatk::RunArgs)", "").replace("(qmatk::DequantArgs)", "")
+    n = n.replace("void (anonymous namespace)::", "")
+    if n.startswith("read_stream_kernel<") and "(" in n:
+        n = n[:n.index("(")]  # the read-stream probe: template arguments only
+    return n
 
 
 def trace_summary(path: str):
