@@ -33,9 +33,12 @@
 namespace qmatk {
 // ------------------------------------------------------------------ split bookkeeping
 
+// [u0, u1): a contiguous run of the tile's k units for this wave; sl, nsl: the wave's slice
+// index and the tile's number of slices (the same share, for kernels that take every nsl-th
+// unit from sl).
 struct Slice {
     int tile, sp, S, w, nw, u0, u1;
-    int sl, nsl;  // this wave's slice of the tile's k units and the number of slices
+    int sl, nsl;
     int wsrow, wsld;  // the tile's first row and the row count of its workspace region
     int64_t wsoff;    // start of that region in the workspace (floats)
 };
@@ -209,11 +212,12 @@ __device__ __forceinline__ u32x4_t load_x8_buf(const RunArgs &a, __amdgpu_buffer
     return __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(lane_off + 2u * (uint32_t)kc), 0, 0);
 }
 
-// Software pipeline over a wave's units [u0, u1): a ring of D units in flight; a slot is
-// refilled with unit u + D right after unit u has been consumed from it.  mid() runs once
-// after the first loads are issued (their latency hides it).  The steady-state loop has no
-// branches inside, so the compiler's wait counting sees that only the slot being consumed
-// has to have arrived; the guarded tail handles the last units.
+// Software pipeline over iterations [u0, u1) of a wave (each one k unit, which load() maps to
+// the unit index): a ring of D units in flight; a slot is refilled with iteration u + D right
+// after iteration u has been consumed from it.  mid() runs once after the first loads are
+// issued (their latency hides it).  The steady-state loop has no branches inside, so the
+// compiler's wait counting sees that only the slot being consumed has to have arrived; the
+// guarded tail handles the last units.
 template <int D, typename U, typename Load, typename Mid, typename Use>
 __device__ __forceinline__ void pipeline(int u0, int u1, U (&buf)[D], Load load, Mid mid, Use use)
 {

@@ -23,6 +23,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -31,11 +32,21 @@ KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc
                   for n in ("qmat_kernels.hip", "qmat_device.h", "qmat_kernels.h", "qmat_layout.h")]
 
 
-def kernel_source_sha256() -> str:
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (so that editing a comment does
+    not count as a change of the measured kernels; string literals are not special-cased, which
+    is safe for these sources: none holds a comment marker inside a string)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_sha256(sources=None) -> str:
+    """SHA-256 over the small-T kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for p in sources or KERNEL_SOURCES:
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
