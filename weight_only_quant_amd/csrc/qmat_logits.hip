@@ -14,10 +14,11 @@
 // rows of a round; the round then enters the list as four 64-pair chunks (every lane's best, then
 // every lane's second, ...), each costing one compare against the current k-th best and a wave
 // vote, and only when some lane beats it a bitonic sort (DPP / swizzle / half-swap lane
-// exchanges) and merge.  Comparisons are branch-free selects.  The block's 16 lists merge in a fixed pairwise tree; the block publishes
-// (max, sum, k best) to the workspace, and the last block of the token to arrive (arrival
-// counter, reset by that block) merges the B partials the same way, with the log-sum-exp
-// states combined in double in a fixed order: deterministic output, no memset between calls.
+// exchanges) and merge.  Comparisons are branch-free selects.  The block's 16 lists merge in a
+// fixed pairwise tree; the block publishes (max, sum, k best) to the workspace, and the last
+// block of the token to arrive (arrival counter, reset by that block) merges the B partials
+// the same way, with the log-sum-exp states combined in double in a fixed order:
+// deterministic output, no memset between calls.
 //
 // Order: value descending, equal values by ascending row.  Empty slots are (-inf, INT_MAX).
 #include <hip/hip_runtime.h>
