@@ -174,6 +174,50 @@ def test_run_tail_plans(fmt, route, T):
         _check_y(y1, wl, label)
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_random_shapes_and_plans(case):
+    # Seeded random small problems: ragged M, K any multiple of 64 (half units included), every
+    # format, T = 1..16, and random valid launch shapes on both small-T routes (waves that get
+    # no k unit, trailing splits over all or some tiles, deep splits of short K), each checked
+    # against the oracle and for identical bits on a second call.
+    rng = np.random.default_rng(1000 + case)
+    for i in range(8):
+        fmt = int(rng.choice([4, 5, 6, 8, qi.Q8]))
+        M = int(rng.integers(1, 700))
+        K = 64 * int(rng.integers(1, 40))
+        T = int(rng.integers(1, 17))
+        route = str(rng.choice(["valu", "mfma"]))
+        NT, NU = (M + 63) // 64, (K + 127) // 128
+        waves = int(rng.choice([1, 2, 4, 8]))
+        depth = int(rng.choice([1, 2]))
+        splits = int(rng.integers(1, 9))
+        tail_tiles = int(rng.integers(0, NT + 1)) if rng.random() < 0.5 else 0
+        tail_splits = int(rng.integers(1, 9))
+        # keep within the documented limits: splits * waves <= 64 * NU (and the same for tails)
+        while splits * waves > 64 * NU:
+            splits = max(1, splits // 2)
+        while tail_splits * waves > 64 * NU:
+            tail_splits = max(1, tail_splits // 2)
+        wl = _workload(fmt, M, K, T, 5000 + 100 * case + i)
+        qm = wq.QMat(fmt, wl.codes, wl.scales)
+        xd = _x_dev(wl.x)
+        plan = wq.qmat_plan(ROUTES[route], depth, waves, splits, tail_tiles, tail_splits)
+        label = f"random case={case}.{i} fmt={fmt} M={M} K={K} T={T} plan={plan.as_tuple()}"
+        say(label)
+        y1 = torch.full((T, M), float("nan"), device="cuda")
+        y2 = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run_plan(qm.handle, xd, y1, plan, T=T)
+        wq.qmat_run_plan(qm.handle, xd, y2, plan, T=T)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), label
+        _check_y(y1, wl, label)
+        # and the automatic plan at the same size
+        y3 = qm.run(xd)
+        torch.cuda.synchronize()
+        _check_y(y3, wl, label + " auto")
+        qm.close()
+
+
 def test_run_plan_rejects_bad_fields():
     say("run_plan errors")
     wl = _workload(4, 130, 256, 1, 5)
