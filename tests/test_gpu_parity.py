@@ -488,6 +488,28 @@ def test_zero_and_sparse_codes(fmt):
         _check_y(y, qi.Workload("s", fmt, M, K, T, codes, wl.scales, wl.x), f"sparse {route}")
 
 
+@pytest.mark.parametrize("fmt,T", [(4, 16), (8, 1), (qi.Q8, 5), (6, 3)])
+def test_largest_k(fmt, T):
+    # K at the largest size the library accepts (2^20: 8192 k units per tile) with a ragged row
+    # count, on the automatic plan (k splits of a narrow matrix) and an explicit deep split with
+    # a trailing-tile split; every output element against the oracle
+    M, K = 70, 1 << 20
+    wl = _workload(fmt, M, K, T, 910 + fmt + T)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    say(f"largest K fmt={fmt} T={T} auto plan {wq.qmat_get_plan(qm.handle, T).as_tuple()}")
+    y = qm.run(xd)
+    torch.cuda.synchronize()
+    _check_y(y, wl, f"K=2^20 fmt={fmt} T={T} auto")
+    plan = wq.qmat_plan(wq.QMAT_ROUTE_MFMA, 2, 8, 8, 1, 5)
+    say(f"largest K fmt={fmt} T={T} plan {plan.as_tuple()}")
+    y2 = torch.full((T, M), float("nan"), device="cuda")
+    wq.qmat_run_plan(qm.handle, xd, y2, plan, T=T)
+    torch.cuda.synchronize()
+    _check_y(y2, wl, f"K=2^20 fmt={fmt} T={T} plan")
+    qm.close()
+
+
 def test_t_zero_is_noop_and_bad_args():
     wl = _workload(4, 64, 128, 1, 1)
     qm = wq.QMat(4, wl.codes, wl.scales)
