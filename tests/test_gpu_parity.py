@@ -510,6 +510,22 @@ def test_largest_k(fmt, T):
     qm.close()
 
 
+def test_largest_k_gemm():
+    # the prefill GEMM route at the largest K (its activation staging offsets and k splits over
+    # 8192 units), T = 80 (a ragged second token tile), every output against the oracle
+    M, K, T = 70, 1 << 20, 80
+    wl = _workload(4, M, K, T, 977)
+    qm = wq.QMat(4, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    for S in (0, 16):
+        say(f"largest K GEMM T={T} splits={S}")
+        y = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run_ex(qm.handle, xd, y, T, route=wq.QMAT_ROUTE_GEMM, splits=S)
+        torch.cuda.synchronize()
+        _check_y(y, wl, f"K=2^20 GEMM splits={S}")
+    qm.close()
+
+
 def test_t_zero_is_noop_and_bad_args():
     wl = _workload(4, 64, 128, 1, 1)
     qm = wq.QMat(4, wl.codes, wl.scales)
