@@ -55,10 +55,4 @@ hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t stream);
 // unit holds at once (0 on error).
 int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int NU, int S);
 
-// Dynamic LDS bytes of one product launch (activation stage + reduction area).
-size_t run_lds_bytes_for(int route, int waves, int T, int NU, int S);
-
-// Dynamic LDS one workgroup may use.
-constexpr size_t kMaxLds = 64 * 1024;
-
 }  // namespace qmatk

@@ -575,7 +575,6 @@ static size_t run_lds_bytes(int route, int waves, int T, int NU, int S)
     return waves > 1 ? (size_t)waves * T * kTileRows * sizeof(float) : 0;
 }
 
-size_t run_lds_bytes_for(int route, int waves, int T, int NU, int S) { return run_lds_bytes(route, waves, T, NU, S); }
 
 hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, hipStream_t st)
 {
