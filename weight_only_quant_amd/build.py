@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmat.so")
-SOURCES = [os.path.join(CSRC, "qmat_api.cpp"), os.path.join(CSRC, "qmat_encode.cpp"),
+SOURCES = [os.path.join(CSRC, "qmat_host.cpp"), os.path.join(CSRC, "qmat_pack.cpp"),
+           os.path.join(CSRC, "qmat_api.cpp"), os.path.join(CSRC, "qmat_encode.cpp"),
            os.path.join(CSRC, "qmat_kernels.hip"), os.path.join(CSRC, "qmat_gemm.hip"),
            os.path.join(CSRC, "qmat_logits.hip")]
 PROBE_LIB = os.path.join(HERE, "libqmat_probe.so")
