@@ -171,7 +171,7 @@ extern "C" int qmat_quantize(int fmt, int64_t M, int64_t K, const float *w, cons
 {
     using namespace qmatk;
     if (!format_ok(fmt)) return fail(QMAT_EINVAL, "qmat_quantize: unknown format %d", fmt);
-    if (M < 1 || K < 64 || K % 64 || M > (1LL << 30) || K > (1LL << 20))
+    if (!qmath::shape_ok(M, K))
         return fail(QMAT_ESHAPE, "qmat_quantize: bad shape M=%lld K=%lld", (long long)M, (long long)K);
     if (!w || !codes_out || !scales_out) return fail(QMAT_EINVAL, "qmat_quantize: null pointer");
     if (encoder != QMAT_ENCODE_RTN && encoder != QMAT_ENCODE_GROUPED_SEARCH)
