@@ -3,13 +3,7 @@
 // host helpers are in qmat_pack.cpp and qmat_host.cpp (no HIP there).
 #include <hip/hip_runtime.h>
 
-#include <cmath>
-#include <cstdarg>
-#include <cstdio>
-#include <cstring>
 #include <new>
-#include <thread>
-#include <vector>
 
 #include "../../include/qmat.h"
 #include "qmat_host.h"
@@ -26,13 +20,11 @@ using qmath::shape_ok;
 
 namespace {
 
-
 // ------------------------------------------------------------------ planning
 
 struct Plan {
     int route, depth, waves, splits, tail_tiles, tail_splits;
 };
-
 
 // Launch shape for one (route, tokens-per-launch), from graph-timed sweeps of depth x waves x
 // splits x trailing-tile splits over the benchmark shapes on MI355X.
@@ -136,7 +128,6 @@ int device_ok(int device, const char *who)
         return fail(QMAT_EINVAL, "%s: the handle belongs to device %d but device %d is current", who, device, cur);
     return QMAT_OK;
 }
-
 
 // tokens one launch of a route handles when the call has T tokens
 int launch_tokens(int route, int T) { return route == kRouteValu ? (T < kValuMaxT ? T : kValuMaxT) : T; }
