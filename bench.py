@@ -297,6 +297,12 @@ def read_ceilings(window_bytes):
     return {"GBps_1GiB": big, "shapes_1GiB": big_shapes, "GBps_window": win, "window_bytes": w}
 
 
+def read_probe_window(window_bytes):
+    """Best plain-read rate (GB/s) over windows of window_bytes rotated through 1 GiB."""
+    from weight_only_quant_amd import probe
+    return probe.best_read_gbs(1 << 30, window=window_bytes, reps=100)
+
+
 def cpu_context(target_s=1.0):
     """The host CPU model and the oracle's single-thread time on the small Q4 case (256 x 1024,
     T = 1), the one the measurement plan times on one core."""
@@ -444,9 +450,23 @@ def main():
         out["read_stream"] = c
         out["pct_of_read_ceiling"] = round(100 * value / c["GBps_1GiB"], 2)
         out["pct_of_same_size_read"] = round(100 * value / c["GBps_window"], 2)
-        for v in extra.values():
-            if "GBps" in v and "bytes" in v and "k" not in v:
-                v["pct_of_read_ceiling"] = round(100 * v["GBps"] / c["GBps_1GiB"], 2)
+        out["same_size_read_us"] = round(c["window_bytes"] / (c["GBps_window"] * 1e3), 3)
+        # every product line against the 1 GiB read, and the matrices that rotate (< 512 MB)
+        # also against a plain read of their own packed size (fixed launch, first-byte and drain
+        # costs included), timed the same way
+        windows = {name: c["GBps_window"]}
+        for key, v in extra.items():
+            if not ("GBps" in v and "bytes" in v and "k" not in v):
+                continue
+            v["pct_of_read_ceiling"] = round(100 * v["GBps"] / c["GBps_1GiB"], 2)
+            wname = key.rsplit("_T", 1)[0]
+            size = qmat_packed_size(wname) // 1024 * 1024 if wname in qi.CONFIGS else 0
+            if not 0 < size < (512 << 20):
+                continue
+            if wname not in windows:
+                windows[wname], _ = read_probe_window(size)
+            v["same_size_read_us"] = round(size / (windows[wname] * 1e3), 3)
+            v["pct_of_same_size_read"] = round(100 * v["same_size_read_us"] / v["us_per_call"], 2)
         log(f"[bench] read stream: {c}")
     if not args.no_cpu_baseline:
         out["cpu_context"] = cpu_context()
