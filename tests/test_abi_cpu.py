@@ -171,3 +171,36 @@ def test_probe_library_exports_its_header_and_validates():
     assert R(16, 1024, 1, 0, 1, 9, 0, 16, 64 * 9, None) == 1     # waves per workgroup
     assert R(16, 1024, 1, 0, 1, 1, 0, None, 64, None) == 1       # null out
     assert R(16, 1024, 1, 0, 1, 1, 0, 16, 63, None) == 1         # out too small
+
+
+def test_missing_library_fails_loudly():
+    """With libqmat.so absent every binding call raises ImportError: there is no other path."""
+    import subprocess
+    import sys
+    code = ("import weight_only_quant_amd as wq\n"
+            "wq.LIB_PATH = '/nonexistent/libqmat.so'\n"
+            "wq._lib = None\n"
+            "try:\n"
+            "    wq.qmat_packed_bytes(wq.QMAT_Q4, 64, 128)\n"
+            "except ImportError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('no error')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("raised:") and "no non-HIP path" in r.stdout, r.stdout
+
+
+def test_product_code_never_uses_the_oracle():
+    """The package (binding, build script, kernels, host sources) names no oracle module or
+    oracle function: the oracle is test infrastructure only."""
+    pkg = os.path.join(ROOT, "weight_only_quant_amd")
+    offenders = []
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if not f.endswith((".py", ".hip", ".cpp", ".h")):
+                continue
+            src = open(os.path.join(dirpath, f), encoding="utf-8").read()
+            if re.search(r"\bimport\s+oracle\b|\bfrom\s+oracle\b|\bqo_[a-z_0-9]+\s*\(|qmat_oracle", src):
+                offenders.append(f)
+    assert not offenders, offenders
