@@ -218,6 +218,60 @@ def test_random_shapes_and_plans(case):
         qm.close()
 
 
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
+@pytest.mark.parametrize("T", [1, 2, 7, 12, 16])
+def test_run_pair_plans(fmt, T):
+    # two row tiles per wave (one activation fragment for both): an odd tile count (the last
+    # workgroup has one tile), a ragged last tile and a half k unit; every wave count and both
+    # depths.  In tolerance, deterministic, and the same bits as one tile per wave with the same
+    # waves and depth (per tile the arithmetic and the reduction order are the same).
+    M, K = 7 * 64 - 9, 1472   # 7 tiles, the last ragged; 12 k units, the last a half unit
+    wl = _workload(fmt, M, K, T, 71 + fmt + T)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    for depth in (1, 2):
+        for waves in (1, 2, 4, 8):
+            pair = wq.qmat_plan(wq.QMAT_ROUTE_MFMA, depth, waves, 1, 0, 1, 2)
+            single = wq.qmat_plan(wq.QMAT_ROUTE_MFMA, depth, waves, 1, 0, 1, 1)
+            label = f"pair fmt={fmt} T={T} plan={pair.as_tuple()}"
+            say(label)
+            y1 = torch.full((T, M), float("nan"), device="cuda")
+            y2 = torch.full((T, M), float("nan"), device="cuda")
+            y0 = torch.full((T, M), float("nan"), device="cuda")
+            wq.qmat_run_plan(qm.handle, xd, y1, pair, T=T)
+            wq.qmat_run_plan(qm.handle, xd, y2, pair, T=T)
+            wq.qmat_run_plan(qm.handle, xd, y0, single, T=T)
+            torch.cuda.synchronize()
+            assert torch.equal(y1, y2), label
+            assert torch.equal(y1, y0), label + " differs from one tile per wave"
+            _check_y(y1, wl, label)
+    qm.close()
+
+
+@pytest.mark.parametrize("fmt,T", [(4, 16), (6, 12), (8, 16), (qi.Q8, 13)])
+def test_pair_plan_on_head_sized_matrix(fmt, T):
+    # the automatic plan of a matrix of >= 2048 row tiles at verify-sized T streams two tiles
+    # per wave; with an odd tile count and a ragged last tile it matches the oracle on sampled
+    # rows (the last tile included) and one tile per wave bit for bit
+    M, K = 2049 * 64 - 7, 320
+    wl = _workload(fmt, M, K, T, 91 + fmt)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    p = wq.qmat_get_plan(qm.handle, T)
+    say(f"head-sized fmt={fmt} T={T} auto plan {p.as_tuple()}")
+    assert p.route == wq.QMAT_ROUTE_MFMA and p.tiles == 2 and p.splits == 1 and p.tail_tiles == 0
+    xd = _x_dev(wl.x)
+    y = torch.full((T, M), float("nan"), device="cuda")
+    y0 = torch.full((T, M), float("nan"), device="cuda")
+    wq.qmat_run(qm.handle, xd, y, T=T)
+    wq.qmat_run_plan(qm.handle, xd, y0, wq.qmat_plan(p.route, p.depth, p.waves, 1, 0, 1, 1), T=T)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    assert torch.equal(y, y0)
+    rows = sorted(set(_sample_rows(M, n=400, seed=3)) | set(range(M - 57, M)))
+    _check_y(y, wl, f"head-sized fmt={fmt} T={T}", rows=rows)
+    qm.close()
+
+
 def test_run_plan_rejects_bad_fields():
     say("run_plan errors")
     wl = _workload(4, 130, 256, 1, 5)
@@ -228,6 +282,12 @@ def test_run_plan_rejects_bad_fields():
     bad = [(0, 1, 4, 1, 0, 1), (2, 3, 4, 1, 0, 1), (2, 1, 3, 1, 0, 1), (2, 1, 4, 0, 0, 1),
            (2, 1, 4, 1, NT + 1, 1), (2, 1, 4, 1, -1, 1), (2, 1, 4, 1, 1, 0)]
     for fields in bad:
+        with pytest.raises(wq.QmatError) as e:
+            wq.qmat_run_plan(qm.handle, xd, y, wq.qmat_plan(*fields), T=1)
+        assert e.value.status == wq.QMAT_EINVAL, fields
+    # tiles: 1 or 2; two tiles per wave only on the MFMA route without k or trailing splits
+    for fields in [(2, 1, 4, 1, 0, 1, 3), (2, 1, 4, 1, 0, 1, -1), (1, 1, 4, 1, 0, 1, 2), (2, 1, 4, 2, 0, 1, 2),
+                   (2, 1, 4, 1, 1, 2, 2)]:
         with pytest.raises(wq.QmatError) as e:
             wq.qmat_run_plan(qm.handle, xd, y, wq.qmat_plan(*fields), T=1)
         assert e.value.status == wq.QMAT_EINVAL, fields

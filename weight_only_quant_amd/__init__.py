@@ -167,10 +167,10 @@ def qmat_dequant(handle: int, w, stream=None) -> None:
 class qmat_plan(ctypes.Structure):
     """The C struct qmat_plan (launch shape of the product kernel)."""
     _fields_ = [("route", _int), ("depth", _int), ("waves", _int), ("splits", _int),
-                ("tail_tiles", _int), ("tail_splits", _int)]
+                ("tail_tiles", _int), ("tail_splits", _int), ("tiles", _int)]
 
     def as_tuple(self):
-        return (self.route, self.depth, self.waves, self.splits, self.tail_tiles, self.tail_splits)
+        return (self.route, self.depth, self.waves, self.splits, self.tail_tiles, self.tail_splits, self.tiles)
 
 
 def qmat_get_plan(handle: int, T: int, route: int = QMAT_ROUTE_AUTO) -> qmat_plan:

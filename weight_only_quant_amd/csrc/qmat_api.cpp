@@ -24,6 +24,7 @@ namespace {
 
 struct Plan {
     int route, depth, waves, splits, tail_tiles, tail_splits;
+    int tiles = 1;  // row tiles per wave (2: mfma_pair_kernel)
 };
 
 // Launch shape for one (route, tokens-per-launch), from graph-timed sweeps of depth x waves x
@@ -32,7 +33,10 @@ struct Plan {
 // MFMA kernel.
 //  - Matrices of at least 2048 row tiles: one tile per workgroup, never split; 4 waves share a
 //    tile's k units at T = 1 (a single token leaves registers for two units in flight), 1 wave
-//    otherwise.
+//    otherwise.  From 12 tokens a wave streams two neighbouring tiles with one unit in flight,
+//    loading each activation fragment once for both (measured on 248320 x 5120 heads: 2-5%
+//    faster at T = 12, 5-14% at T = 16; 1-7% slower at T <= 8, where the fragment loads are
+//    cheaper than the halved number of units in flight per tile).
 //  - At least one tile per compute unit: 4 waves per workgroup, two units in flight up to T = 4
 //    and one above (from T = 12 the multi-token accumulators of a two-unit ring leave too few
 //    resident waves: 25-30% slower; at T = 2-4 the ring is 6-7% faster, T = 6-8 tie).  When
@@ -59,6 +63,10 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
         Plan p{route, 2, 1, 1, 0, 1};
         if (NT >= 2048) {
             p.waves = Tl == 1 ? 4 : 1;
+            if (Tl >= 12) {
+                p.tiles = 2;
+                p.depth = 1;
+            }
         } else if (NT >= cus) {
             p.waves = 4;
             p.depth = Tl <= 4 ? 2 : 1;
@@ -325,6 +333,9 @@ int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, vo
     if (reinterpret_cast<uintptr_t>(x_dev) % 16) return fail(QMAT_EINVAL, "qmat_run: x not 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_run: y not 4-byte aligned");
     if (p.route != kRouteValu && p.route != kRouteMfma) return fail(QMAT_EINVAL, "qmat_run: bad route");
+    if (p.tiles != 1 && p.tiles != 2) return fail(QMAT_EINVAL, "qmat_run: tiles must be 1 or 2");
+    if (p.tiles == 2 && (p.route != kRouteMfma || p.splits != 1 || p.tail_tiles != 0))
+        return fail(QMAT_EINVAL, "qmat_run: two tiles per wave need the MFMA route, splits == 1 and no trailing split");
     if (const int st = device_ok(h->device, "qmat_run")) return st;
     if (!(p.waves == 1 || p.waves == 2 || p.waves == 4 || p.waves == 8))
         return fail(QMAT_EINVAL, "qmat_run: waves must be 1, 2, 4 or 8");
@@ -363,7 +374,7 @@ int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, vo
         a.S = p.splits;
         a.NTt = p.tail_tiles;
         a.St = tail_splits;
-        const hipError_t e = launch_run(h->fmt, p.route, p.depth, a, p.waves, st);
+        const hipError_t e = launch_run(h->fmt, p.route, p.depth, a, p.waves, p.tiles, st);
         if (e != hipSuccess) return fail(QMAT_EHIP, "qmat_run: launch failed: %s", hipGetErrorString(e));
     }
     return ok();
@@ -392,6 +403,7 @@ int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int
         p.splits = splits;
         p.tail_tiles = 0;
         p.tail_splits = 1;
+        if (splits > 1) p.tiles = 1;
     }
     return run_plan(h, x_dev, y_dev, T, p, stream);
 }
@@ -407,7 +419,7 @@ int qmat_run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const qmat_p
     if (plan->route != QMAT_ROUTE_VALU && plan->route != QMAT_ROUTE_MFMA)
         return fail(QMAT_EINVAL, "qmat_run_plan: route must be QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA or QMAT_ROUTE_GEMM");
     const Plan p{plan->route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma, plan->depth, plan->waves, plan->splits,
-                 plan->tail_tiles, plan->tail_splits};
+                 plan->tail_tiles, plan->tail_splits, plan->tiles == 0 ? 1 : plan->tiles};
     return run_plan(h, x_dev, y_dev, T, p, stream);
 }
 
@@ -417,7 +429,7 @@ int qmat_get_plan(qmat_t h, int T, int route, qmat_plan *plan)
     if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_GEMM) return fail(QMAT_EINVAL, "qmat_get_plan: bad route %d", route);
     if (route == QMAT_ROUTE_GEMM || (route == QMAT_ROUTE_AUTO && T > kMaxT)) {
         if (T < 1 || T > kGemmMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kGemmMaxT);
-        *plan = qmat_plan{QMAT_ROUTE_GEMM, 1, 4, gemm_auto_splits(h->NT, h->NU, T, h->cus, h->ws_floats), 0, 1};
+        *plan = qmat_plan{QMAT_ROUTE_GEMM, 1, 4, gemm_auto_splits(h->NT, h->NU, T, h->cus, h->ws_floats), 0, 1, 1};
         return ok();
     }
     if (T < 1 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kMaxT);
@@ -429,6 +441,7 @@ int qmat_get_plan(qmat_t h, int T, int route, qmat_plan *plan)
     plan->splits = p.splits;
     plan->tail_tiles = p.tail_tiles;
     plan->tail_splits = p.tail_tiles > 0 ? p.tail_splits : 1;
+    plan->tiles = p.tiles;
     return ok();
 }
 

@@ -369,11 +369,13 @@ __global__ __launch_bounds__(512) void valu_kernel(RunArgs a)
 
 // ------------------------------------------------------------------ MFMA route
 
-template <int FMT, int KA, int NB, int XN>
-__device__ __forceinline__ void mfma_step(const Unit<NB, XN> &U, f32x4_t (&D)[4])
+// One 32-wide k step of a tile: the four 16-row slices' codes (blocks c) times the activation
+// fragment xa, accumulated into D.
+template <int FMT, int KA, int NB>
+__device__ __forceinline__ void mfma_step_w(const u32x4_t (&c)[NB], const u32x4_t &xa, f32x4_t (&D)[4])
 {
-    const uint32_t *W = reinterpret_cast<const uint32_t *>(U.c);
-    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, U.x[KA]);
+    const uint32_t *W = reinterpret_cast<const uint32_t *>(c);
+    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, xa);
 #define QMAT_MFMA_ROW(MM)                                                                       \
     {                                                                                           \
         uint32_t b[4];                                                                          \
@@ -383,6 +385,12 @@ __device__ __forceinline__ void mfma_step(const Unit<NB, XN> &U, f32x4_t (&D)[4]
     }
     QMAT_MFMA_ROW(0) QMAT_MFMA_ROW(1) QMAT_MFMA_ROW(2) QMAT_MFMA_ROW(3)
 #undef QMAT_MFMA_ROW
+}
+
+template <int FMT, int KA, int NB, int XN>
+__device__ __forceinline__ void mfma_step(const Unit<NB, XN> &U, f32x4_t (&D)[4])
+{
+    mfma_step_w<FMT, KA, NB>(U.c, U.x[KA], D);
 }
 
 // A operand: 16 tokens x 32 k (lane l: token l % 16, k octet l / 16); B operand: 32 k x 16 rows
@@ -470,6 +478,119 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
     });
 }
 
+// Two row tiles per wave, one activation fragment: for verify-sized T the activation loads
+// (16 tokens x 32 k per step, 1 KB per wave instruction from the L2) cost as much load issue
+// as a quarter to a half of the weight stream.  A wave that streams the same k unit of two
+// neighbouring tiles loads each fragment once for both.  Only for plans without k splits and
+// without a trailing-tile split: workgroup b owns tiles 2b and 2b + 1 (the second absent for
+// the last workgroup of an odd tile count; its loads then repeat the first tile and nothing is
+// stored for it).  Per tile the arithmetic, the wave split of its units and the reduction are
+// those of mfma_kernel, so both kernels give the same bits.
+template <int NB> struct PairUnit {
+    u32x4_t c[2][NB];
+    u32x4_t sc[2];
+    u32x4_t x[4];
+};
+
+template <int FMT, int D_>
+__global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
+{
+    constexpr int NB = Fmt<FMT>::NB, TR = 4;
+    extern __shared__ float red[];
+    const Slice s = make_slice(a);  // S == 1 and no trailing tiles: s.tile is the pair index
+    const int pair = s.tile;
+    const uint32_t lane = threadIdx.x & 63;
+    const int tok = lane & 15, oct = lane >> 4;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.x), (short)0, 2 * a.T * a.K, kRawBufferWord3);
+    const uint32_t xoff = tok < a.T ? 2u * (uint32_t)(tok * a.K) + 16u * oct : kPastEnd;
+    const int tile0 = 2 * pair, tile1 = 2 * pair + 1 < a.NT ? 2 * pair + 1 : 2 * pair;
+    f32x4_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[i][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    int ui0 = s.u0, ui1 = s.u1;
+    if constexpr (D_ == 2) {
+        ui0 = 0;
+        ui1 = s.sl < a.NU ? (a.NU - s.sl + s.nsl - 1) / s.nsl : 0;
+    }
+    PairUnit<NB> buf[D_];
+    pipeline<D_>(ui0, ui1, buf,
+        [&](PairUnit<NB> &r, int u) {
+            if constexpr (D_ == 2) u = s.sl + u * s.nsl;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int64_t tu = (int64_t)(i ? tile1 : tile0) * a.NU + u;
+                const char *cb = reinterpret_cast<const char *>(a.codes) + tu * (NB * kBlockBytes);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    r.c[i][j] = stream_load(reinterpret_cast<const u32x4_t *>(cb + j * kBlockBytes + 16u * lane));
+                if constexpr (FMT != 8) {
+                    const char *sb = reinterpret_cast<const char *>(a.scales) + tu * kScaleBlockBytes;
+                    r.sc[i] = stream_load(reinterpret_cast<const u32x4_t *>(sb + 16u * (lane & 15)));
+                }
+            }
+#pragma unroll
+            for (int ka = 0; ka < 4; ++ka)
+                r.x[ka] = load_x8_buf(a, xr, u * kUnitK + 32 * ka, xoff);
+        },
+        [&]() {},
+        [&](const PairUnit<NB> &U, int) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if constexpr (FMT == 8) {
+                    mfma_step_w<FMT, 0, NB>(U.c[i], U.x[0], acc[i]);
+                    mfma_step_w<FMT, 1, NB>(U.c[i], U.x[1], acc[i]);
+                    mfma_step_w<FMT, 2, NB>(U.c[i], U.x[2], acc[i]);
+                    mfma_step_w<FMT, 3, NB>(U.c[i], U.x[3], acc[i]);
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        f32x4_t P[4];
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) P[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                        if (g == 0) {
+                            mfma_step_w<FMT, 0, NB>(U.c[i], U.x[0], P);
+                            mfma_step_w<FMT, 1, NB>(U.c[i], U.x[1], P);
+                        } else {
+                            mfma_step_w<FMT, 2, NB>(U.c[i], U.x[2], P);
+                            mfma_step_w<FMT, 3, NB>(U.c[i], U.x[3], P);
+                        }
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const float sf = group_scale(U.sc[i], g, m);
+#pragma unroll
+                            for (int r = 0; r < TR; ++r) acc[i][m][r] = fmaf(sf, P[m][r], acc[i][m][r]);
+                        }
+                    }
+                }
+            }
+        });
+
+    const int t0 = 4 * oct, rr = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        Slice si = s;
+        si.tile = tile0 + i;
+        if (si.tile >= a.NT) break;  // uniform over the workgroup
+        f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
+        if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)si.tile * 16 + (lane & 15)];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < TR; ++r) acc[i][m][r] *= rs[m];
+        if (i > 0 && s.nw > 1) __syncthreads();  // the first tile's reduction is done with red
+        finish(a, si, red, [&](auto put) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < TR; ++r)
+                    if (t0 + r < a.T) put(t0 + r, 16 * m + rr, acc[i][m][r]);
+        });
+    }
+}
+
 // ------------------------------------------------------------------ dequant (checking path)
 
 template <int FMT, int KA, int MM>
@@ -532,8 +653,9 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a)
 
 // ------------------------------------------------------------------ launchers
 
-template <int FMT, int D> static const void *run_kernel_d(int route, int T)
+template <int FMT, int D> static const void *run_kernel_d(int route, int T, int tiles)
 {
+    if (tiles == 2) return route == kRouteMfma ? reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D>) : nullptr;
     if (route == kRouteMfma)
         return T == 1 ? reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 1>)
                       : reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 4>);
@@ -546,23 +668,23 @@ template <int FMT, int D> static const void *run_kernel_d(int route, int T)
     }
 }
 
-template <int FMT> static const void *run_kernel(int route, int T, int depth)
+template <int FMT> static const void *run_kernel(int route, int T, int depth, int tiles)
 {
     switch (depth) {
-    case 1: return run_kernel_d<FMT, 1>(route, T);
-    case 2: return run_kernel_d<FMT, 2>(route, T);
+    case 1: return run_kernel_d<FMT, 1>(route, T, tiles);
+    case 2: return run_kernel_d<FMT, 2>(route, T, tiles);
     default: return nullptr;
     }
 }
 
-static const void *run_kernel_for(int fmt, int route, int T, int depth)
+static const void *run_kernel_for(int fmt, int route, int T, int depth, int tiles)
 {
     switch (fmt) {
-    case 4: return run_kernel<4>(route, T, depth);
-    case 5: return run_kernel<5>(route, T, depth);
-    case 6: return run_kernel<6>(route, T, depth);
-    case 8: return run_kernel<8>(route, T, depth);
-    case 9: return run_kernel<9>(route, T, depth);
+    case 4: return run_kernel<4>(route, T, depth, tiles);
+    case 5: return run_kernel<5>(route, T, depth, tiles);
+    case 6: return run_kernel<6>(route, T, depth, tiles);
+    case 8: return run_kernel<8>(route, T, depth, tiles);
+    case 9: return run_kernel<9>(route, T, depth, tiles);
     default: return nullptr;
     }
 }
@@ -576,20 +698,21 @@ static size_t run_lds_bytes(int route, int waves, int T, int NU, int S)
 }
 
 
-hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, hipStream_t st)
+hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, int tiles, hipStream_t st)
 {
-    const void *k = run_kernel_for(fmt, route, a.T, depth);
+    if (tiles == 2 && (a.S != 1 || a.NTt != 0)) return hipErrorInvalidValue;
+    const void *k = run_kernel_for(fmt, route, a.T, depth, tiles);
     if (!k) return hipErrorInvalidValue;
     RunArgs arg = a;
     void *args[] = {&arg};
-    const int64_t grid = (int64_t)a.NTt * a.St + (int64_t)(a.NT - a.NTt) * a.S;
+    const int64_t grid = tiles == 2 ? (a.NT + 1) / 2 : (int64_t)a.NTt * a.St + (int64_t)(a.NT - a.NTt) * a.S;
     return hipLaunchKernel(k, dim3((unsigned)grid), dim3((unsigned)(64 * waves)), args,
                            run_lds_bytes(route, waves, a.T, a.NU, a.S), st);
 }
 
 int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int NU, int S)
 {
-    const void *k = run_kernel_for(fmt, route, T, depth);
+    const void *k = run_kernel_for(fmt, route, T, depth, 1);
     int n = 0;
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * waves, run_lds_bytes(route, waves, T, NU, S)) !=
                   hipSuccess)
