@@ -160,8 +160,9 @@ def plan_str(res, T):
     import weight_only_quant_amd as wq
     p = wq.qmat_get_plan(res.handles[0], T)
     tail = f" tail_tiles={p.tail_tiles} tail_splits={p.tail_splits}" if p.tail_tiles else ""
+    tiles = f" tiles={p.tiles}" if p.tiles > 1 else ""
     return (f"{'valu' if p.route == wq.QMAT_ROUTE_VALU else 'mfma'} depth={p.depth} waves={p.waves} "
-            f"splits={p.splits}{tail}")
+            f"splits={p.splits}{tail}{tiles}")
 
 
 EAGER_ONLY = False
