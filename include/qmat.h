@@ -175,7 +175,7 @@ typedef struct {
     int tail_splits; /* workgroups per trailing tile: >= 1 (not read when tail_tiles == 0) */
     int tiles;       /* row tiles per wave: 0 or 1 (one), or 2 (a wave streams the same k units
                         of two neighbouring tiles and loads each activation fragment once for
-                        both; QMAT_ROUTE_MFMA with splits == 1 and tail_tiles == 0 only) */
+                        both; QMAT_ROUTE_MFMA with tail_tiles == 0 only) */
 } qmat_plan;
 
 /* qmat_run with the automatic plan for (route, T) changed by the nonzero arguments, for tests

@@ -222,29 +222,30 @@ def test_random_shapes_and_plans(case):
 @pytest.mark.parametrize("T", [1, 2, 7, 12, 16])
 def test_run_pair_plans(fmt, T):
     # two row tiles per wave (one activation fragment for both): an odd tile count (the last
-    # workgroup has one tile), a ragged last tile and a half k unit; every wave count and both
-    # depths.  In tolerance, deterministic, and the same bits as one tile per wave with the same
-    # waves and depth (per tile the arithmetic and the reduction order are the same).
+    # pair has one tile), a ragged last tile and a half k unit; every wave count, both depths,
+    # with and without k splits.  In tolerance, deterministic, and the same bits as one tile per
+    # wave with the same waves, depth and splits (per tile the arithmetic and the reduction
+    # order are the same).
     M, K = 7 * 64 - 9, 1472   # 7 tiles, the last ragged; 12 k units, the last a half unit
     wl = _workload(fmt, M, K, T, 71 + fmt + T)
     qm = wq.QMat(fmt, wl.codes, wl.scales)
     xd = _x_dev(wl.x)
-    for depth in (1, 2):
-        for waves in (1, 2, 4, 8):
-            pair = wq.qmat_plan(wq.QMAT_ROUTE_MFMA, depth, waves, 1, 0, 1, 2)
-            single = wq.qmat_plan(wq.QMAT_ROUTE_MFMA, depth, waves, 1, 0, 1, 1)
-            label = f"pair fmt={fmt} T={T} plan={pair.as_tuple()}"
-            say(label)
-            y1 = torch.full((T, M), float("nan"), device="cuda")
-            y2 = torch.full((T, M), float("nan"), device="cuda")
-            y0 = torch.full((T, M), float("nan"), device="cuda")
-            wq.qmat_run_plan(qm.handle, xd, y1, pair, T=T)
-            wq.qmat_run_plan(qm.handle, xd, y2, pair, T=T)
-            wq.qmat_run_plan(qm.handle, xd, y0, single, T=T)
-            torch.cuda.synchronize()
-            assert torch.equal(y1, y2), label
-            assert torch.equal(y1, y0), label + " differs from one tile per wave"
-            _check_y(y1, wl, label)
+    for depth, waves, splits in [(d, w, 1) for d in (1, 2) for w in (1, 2, 4, 8)] + [
+            (1, 4, 3), (2, 8, 2), (1, 1, 5), (2, 2, 8)]:
+        pair = wq.qmat_plan(wq.QMAT_ROUTE_MFMA, depth, waves, splits, 0, 1, 2)
+        single = wq.qmat_plan(wq.QMAT_ROUTE_MFMA, depth, waves, splits, 0, 1, 1)
+        label = f"pair fmt={fmt} T={T} plan={pair.as_tuple()}"
+        say(label)
+        y1 = torch.full((T, M), float("nan"), device="cuda")
+        y2 = torch.full((T, M), float("nan"), device="cuda")
+        y0 = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run_plan(qm.handle, xd, y1, pair, T=T)
+        wq.qmat_run_plan(qm.handle, xd, y2, pair, T=T)
+        wq.qmat_run_plan(qm.handle, xd, y0, single, T=T)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), label
+        assert torch.equal(y1, y0), label + " differs from one tile per wave"
+        _check_y(y1, wl, label)
     qm.close()
 
 
@@ -285,9 +286,8 @@ def test_run_plan_rejects_bad_fields():
         with pytest.raises(wq.QmatError) as e:
             wq.qmat_run_plan(qm.handle, xd, y, wq.qmat_plan(*fields), T=1)
         assert e.value.status == wq.QMAT_EINVAL, fields
-    # tiles: 1 or 2; two tiles per wave only on the MFMA route without k or trailing splits
-    for fields in [(2, 1, 4, 1, 0, 1, 3), (2, 1, 4, 1, 0, 1, -1), (1, 1, 4, 1, 0, 1, 2), (2, 1, 4, 2, 0, 1, 2),
-                   (2, 1, 4, 1, 1, 2, 2)]:
+    # tiles: 1 or 2; two tiles per wave only on the MFMA route without a trailing split
+    for fields in [(2, 1, 4, 1, 0, 1, 3), (2, 1, 4, 1, 0, 1, -1), (1, 1, 4, 1, 0, 1, 2), (2, 1, 4, 1, 1, 2, 2)]:
         with pytest.raises(wq.QmatError) as e:
             wq.qmat_run_plan(qm.handle, xd, y, wq.qmat_plan(*fields), T=1)
         assert e.value.status == wq.QMAT_EINVAL, fields

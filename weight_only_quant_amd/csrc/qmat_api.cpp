@@ -334,8 +334,8 @@ int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, vo
     if (reinterpret_cast<uintptr_t>(y_dev) % 4) return fail(QMAT_EINVAL, "qmat_run: y not 4-byte aligned");
     if (p.route != kRouteValu && p.route != kRouteMfma) return fail(QMAT_EINVAL, "qmat_run: bad route");
     if (p.tiles != 1 && p.tiles != 2) return fail(QMAT_EINVAL, "qmat_run: tiles must be 1 or 2");
-    if (p.tiles == 2 && (p.route != kRouteMfma || p.splits != 1 || p.tail_tiles != 0))
-        return fail(QMAT_EINVAL, "qmat_run: two tiles per wave need the MFMA route, splits == 1 and no trailing split");
+    if (p.tiles == 2 && (p.route != kRouteMfma || p.tail_tiles != 0))
+        return fail(QMAT_EINVAL, "qmat_run: two tiles per wave need the MFMA route and no trailing split");
     if (const int st = device_ok(h->device, "qmat_run")) return st;
     if (!(p.waves == 1 || p.waves == 2 || p.waves == 4 || p.waves == 8))
         return fail(QMAT_EINVAL, "qmat_run: waves must be 1, 2, 4 or 8");
@@ -403,7 +403,6 @@ int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int
         p.splits = splits;
         p.tail_tiles = 0;
         p.tail_splits = 1;
-        if (splits > 1) p.tiles = 1;
     }
     return run_plan(h, x_dev, y_dev, T, p, stream);
 }

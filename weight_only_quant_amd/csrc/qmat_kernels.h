@@ -47,8 +47,8 @@ constexpr int kValuMaxT = 4;
 
 // depth: k units in flight per wave (1..kMaxDepth).
 constexpr int kMaxDepth = 2;
-// tiles: row tiles per wave, 1 or 2 (2: MFMA route, a.S == 1 and a.NTt == 0 only; the grid is
-// then ceil(NT / 2) workgroups).
+// tiles: row tiles per wave, 1 or 2 (2: MFMA route and a.NTt == 0 only; the grid is then
+// ceil(NT / 2) * S workgroups).
 hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, int tiles, hipStream_t stream);
 hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t stream);
 

@@ -481,11 +481,12 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
 // Two row tiles per wave, one activation fragment: for verify-sized T the activation loads
 // (16 tokens x 32 k per step, 1 KB per wave instruction from the L2) cost as much load issue
 // as a quarter to a half of the weight stream.  A wave that streams the same k unit of two
-// neighbouring tiles loads each fragment once for both.  Only for plans without k splits and
-// without a trailing-tile split: workgroup b owns tiles 2b and 2b + 1 (the second absent for
-// the last workgroup of an odd tile count; its loads then repeat the first tile and nothing is
-// stored for it).  Per tile the arithmetic, the wave split of its units and the reduction are
-// those of mfma_kernel, so both kernels give the same bits.
+// neighbouring tiles loads each fragment once for both.  Only for plans without a trailing-tile
+// split: the S workgroups of pair p own tiles 2p and 2p + 1 (the second absent for the last
+// pair of an odd tile count; its loads then repeat the first tile and nothing is stored for
+// it).  Per tile the arithmetic, the wave and k split of its units and the reduction (through
+// that tile's own workspace rows and arrival counter) are those of mfma_kernel, so both
+// kernels give the same bits.
 template <int NB> struct PairUnit {
     u32x4_t c[2][NB];
     u32x4_t sc[2];
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
 {
     constexpr int NB = Fmt<FMT>::NB, TR = 4;
     extern __shared__ float red[];
-    const Slice s = make_slice(a);  // S == 1 and no trailing tiles: s.tile is the pair index
+    const Slice s = make_slice(a);  // no trailing tiles: s.tile is the pair index
     const int pair = s.tile;
     const uint32_t lane = threadIdx.x & 63;
     const int tok = lane & 15, oct = lane >> 4;
@@ -573,6 +574,7 @@ __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
     for (int i = 0; i < 2; ++i) {
         Slice si = s;
         si.tile = tile0 + i;
+        si.wsrow = si.tile * kTileRows;
         if (si.tile >= a.NT) break;  // uniform over the workgroup
         f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
         if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)si.tile * 16 + (lane & 15)];
@@ -700,12 +702,12 @@ static size_t run_lds_bytes(int route, int waves, int T, int NU, int S)
 
 hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, int tiles, hipStream_t st)
 {
-    if (tiles == 2 && (a.S != 1 || a.NTt != 0)) return hipErrorInvalidValue;
+    if (tiles == 2 && a.NTt != 0) return hipErrorInvalidValue;
     const void *k = run_kernel_for(fmt, route, a.T, depth, tiles);
     if (!k) return hipErrorInvalidValue;
     RunArgs arg = a;
     void *args[] = {&arg};
-    const int64_t grid = tiles == 2 ? (a.NT + 1) / 2 : (int64_t)a.NTt * a.St + (int64_t)(a.NT - a.NTt) * a.S;
+    const int64_t grid = tiles == 2 ? (int64_t)(a.NT + 1) / 2 * a.S : (int64_t)a.NTt * a.St + (int64_t)(a.NT - a.NTt) * a.S;
     return hipLaunchKernel(k, dim3((unsigned)grid), dim3((unsigned)(64 * waves)), args,
                            run_lds_bytes(route, waves, a.T, a.NU, a.S), st);
 }
