@@ -204,3 +204,13 @@ def test_product_code_never_uses_the_oracle():
             if re.search(r"\bimport\s+oracle\b|\bfrom\s+oracle\b|\bqo_[a-z_0-9]+\s*\(|qmat_oracle", src):
                 offenders.append(f)
     assert not offenders, offenders
+
+
+def test_plan_struct_matches_header():
+    """The binding's qmat_plan has the header's fields, in order, all int."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct\s*\{([^}]*)\}\s*qmat_plan;", src).group(1)
+    fields = re.findall(r"\bint\s+([a-z_]+)\s*;", body)
+    assert fields == [name for name, _ in wq.qmat_plan._fields_]
+    assert all(t is ctypes.c_int for _, t in wq.qmat_plan._fields_)
+    assert ctypes.sizeof(wq.qmat_plan) == 4 * len(fields)
