@@ -249,7 +249,7 @@ def test_run_pair_plans(fmt, T):
     qm.close()
 
 
-@pytest.mark.parametrize("fmt,T", [(4, 16), (6, 12), (8, 16), (qi.Q8, 13)])
+@pytest.mark.parametrize("fmt,T", [(4, 16), (5, 10), (6, 12), (8, 16), (8, 9), (qi.Q8, 13)])
 def test_pair_plan_on_head_sized_matrix(fmt, T):
     # the automatic plan of a matrix of >= 2048 row tiles at verify-sized T streams two tiles
     # per wave; with an odd tile count and a ragged last tile it matches the oracle on sampled
@@ -260,6 +260,9 @@ def test_pair_plan_on_head_sized_matrix(fmt, T):
     p = wq.qmat_get_plan(qm.handle, T)
     say(f"head-sized fmt={fmt} T={T} auto plan {p.as_tuple()}")
     assert p.route == wq.QMAT_ROUTE_MFMA and p.tiles == 2 and p.splits == 1 and p.tail_tiles == 0
+    # two tiles per wave from T = 10 (T = 9 for the 8-bit formats), one below
+    first = 9 if fmt in (8, qi.Q8) else 10
+    assert [wq.qmat_get_plan(qm.handle, t).tiles for t in range(1, 17)] == [1] * (first - 1) + [2] * (17 - first)
     xd = _x_dev(wl.x)
     y = torch.full((T, M), float("nan"), device="cuda")
     y0 = torch.full((T, M), float("nan"), device="cuda")

@@ -33,10 +33,11 @@ struct Plan {
 // MFMA kernel.
 //  - Matrices of at least 2048 row tiles: one tile per workgroup, never split; 4 waves share a
 //    tile's k units at T = 1 (a single token leaves registers for two units in flight), 1 wave
-//    otherwise.  From 12 tokens a wave streams two neighbouring tiles with one unit in flight,
-//    loading each activation fragment once for both (measured on 248320 x 5120 heads: 2-5%
-//    faster at T = 12, 5-14% at T = 16; 1-7% slower at T <= 8, where the fragment loads are
-//    cheaper than the halved number of units in flight per tile).
+//    otherwise.  From 10 tokens (9 for the 8-bit formats) a wave streams two neighbouring
+//    tiles with one unit in flight, loading each activation fragment once for both (measured
+//    on 248320 x 5120 heads: 1-3% faster at T = 10-11, 2-5% at T = 12, 5-14% at T = 16, and for
+//    FP8 and Q8 2% at T = 9; up to 7% slower at small T, where the fragment loads are cheaper
+//    than the halved number of units in flight per tile).
 //  - At least one tile per compute unit: 4 waves per workgroup, two units in flight up to T = 4
 //    and one above (from T = 12 the multi-token accumulators of a two-unit ring leave too few
 //    resident waves: 25-30% slower; at T = 2-4 the ring is 6-7% faster, T = 6-8 tie).  When
@@ -63,7 +64,7 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
         Plan p{route, 2, 1, 1, 0, 1};
         if (NT >= 2048) {
             p.waves = Tl == 1 ? 4 : 1;
-            if (Tl >= 12) {
+            if (Tl >= (fmt == kFmtFp8 || fmt == kFmtQ8 ? 9 : 10)) {
                 p.tiles = 2;
                 p.depth = 1;
             }
