@@ -158,8 +158,8 @@ int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows);
 int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream);
 
 /* A launch shape of the product kernel.  The matrix is cut into NT = ceil(M/64) row tiles;
- * a workgroup of `waves` waves works on one tile and splits the tile's 128-wide k units among
- * its waves.  The leading NT - tail_tiles tiles are each shared by `splits` workgroups along K,
+ * a workgroup of `waves` waves works on one tile (or on two neighbouring tiles, see `tiles`)
+ * and splits the tile's 128-wide k units among its waves.  The leading NT - tail_tiles tiles are each shared by `splits` workgroups along K,
  * the trailing tail_tiles tiles by `tail_splits` workgroups (a way to spread a few leftover
  * tiles over the whole GPU when NT is not a multiple of the compute-unit count).  Tiles shared
  * by several workgroups are summed through the handle's workspace in a fixed order, so every
