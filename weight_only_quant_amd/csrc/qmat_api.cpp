@@ -490,7 +490,8 @@ void qmat_destroy(qmat_t h)
 
 struct qmat_logits {
     int64_t M;
-    int max_T, max_k, B, rpb;
+    int max_T, max_k, B;  // B: blocks per token at T = 1 (the partial buffers' size)
+    int64_t slots;  // epilogue workgroups resident on the whole GPU at once (0: unknown)
     float *part_f;
     int32_t *part_i;
     uint32_t *counter;
@@ -512,7 +513,6 @@ int qmat_logits_create(qmat_logits_t *e, int64_t M, int max_T, int max_k)
     h->max_T = max_T;
     h->max_k = max_k;
     h->B = logits_blocks(M);
-    h->rpb = (int)((M + h->B - 1) / h->B);
     h->part_f = nullptr;
     h->part_i = nullptr;
     h->counter = nullptr;
@@ -520,6 +520,9 @@ int qmat_logits_create(qmat_logits_t *e, int64_t M, int max_T, int max_k)
         delete h;
         return fail(QMAT_EHIP, "qmat_logits_create: hipGetDevice failed");
     }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess) cus = 0;
+    h->slots = (int64_t)cus * logits_blocks_per_cu();
     const size_t nf = (size_t)max_T * h->B * (2 + max_k), ni = (size_t)max_T * h->B * (max_k > 0 ? max_k : 1);
     if (hipMalloc(&h->part_f, nf * sizeof(float)) != hipSuccess ||
         hipMalloc(&h->part_i, ni * sizeof(int32_t)) != hipSuccess ||
@@ -566,8 +569,13 @@ int qmat_logits_run(qmat_logits_t e, const float *y_dev, int64_t ldy, int T, int
     a.part_f = e->part_f;
     a.part_i = e->part_i;
     a.counter = e->counter;
-    a.B = e->B;
-    a.rpb = e->rpb;
+    // B blocks per token, but no more than one round of resident workgroups over all T tokens:
+    // a second round would wait for the first, so fewer, longer blocks finish sooner (each
+    // streams its rows in several rounds of loads; the partial lists to merge get shorter too)
+    int B = e->B;
+    if (e->slots > 0 && (int64_t)B * T > e->slots) B = (int)(e->slots / T > 1 ? e->slots / T : 1);
+    a.B = B;
+    a.rpb = (int)((e->M + B - 1) / B);
     const hipError_t err = launch_logits(a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(QMAT_EHIP, "qmat_logits_run: launch failed: %s", hipGetErrorString(err));
     return ok();

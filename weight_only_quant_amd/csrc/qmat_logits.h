@@ -29,6 +29,9 @@ inline int logits_blocks(int64_t M)
     return (int)(b < 1 ? 1 : b > 512 ? 512 : b);
 }
 
+// Workgroups of the epilogue kernel one compute unit holds at once (0 if unknown).
+int logits_blocks_per_cu();
+
 hipError_t launch_logits(const LogitsArgs &a, hipStream_t stream);
 
 }  // namespace qmatk

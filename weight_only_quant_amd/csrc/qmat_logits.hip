@@ -395,6 +395,15 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
 
 }  // namespace
 
+int logits_blocks_per_cu()
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(&logits_kernel), kThreads, 0) !=
+        hipSuccess)
+        return 0;
+    return n;
+}
+
 hipError_t launch_logits(const LogitsArgs &a, hipStream_t st)
 {
     LogitsArgs arg = a;
