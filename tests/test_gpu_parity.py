@@ -656,6 +656,39 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
+def test_pair_plan_graph_replay_matches_eager():
+    # two tiles per wave with k splits: both tiles of a pair count in on their own arrival
+    # counters and reset them, so replays need no memset
+    import gc
+    gc.collect()
+    M, K, T = 7 * 64 - 9, 4352, 16
+    wl = _workload(6, M, K, T, 78)
+    qm = wq.QMat(6, wl.codes, wl.scales)
+    xd = _x_dev(wl.x)
+    plan = wq.qmat_plan(wq.QMAT_ROUTE_MFMA, 1, 4, 3, 0, 1, 2)
+    y_eager = torch.empty((T, M), device="cuda")
+    wq.qmat_run_plan(qm.handle, xd, y_eager, plan, T=T)
+    torch.cuda.synchronize()
+    _check_y(y_eager, wl, "pair graph eager")
+    y = torch.empty((T, M), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        wq.qmat_run_plan(qm.handle, xd, y, plan, T=T, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wq.qmat_run_plan(qm.handle, xd, y, plan, T=T, stream=torch.cuda.current_stream())
+    for i in range(4):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i}"
+        wq.qmat_run_plan(qm.handle, xd, y_eager, plan, T=T)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ full benchmark shapes
 
 def _sample_rows(M, n=1500, seed=0):
