@@ -4,12 +4,21 @@ A step is one qmat_run call (the whole product: stream packed codes and scales, 
 dot products, group scales, reductions, write y) on resident device buffers.  The headline
 workload is the Q4 fused MLP gate+up projection (two 17408 x 5120 matrices as one
 M=34816, K=5120 matrix) at T=1; the other benchmark shapes (Q6 vocab head, Q5 down
-projection with split-K, FP8 row-scaled head and projection, the small Q4 case) at each
-of their token counts are reported in "extra".
+projection with split-K, FP8 row-scaled head and projection, the 8-bit heads, the small Q4
+case) at each of their token counts are reported in "extra".
 
 Throughput is algorithmic bytes (packed codes + scales read once, x read, y written) per
 second.  Matrices smaller than 512 MB rotate over enough device copies to exceed 512 MB so
 the 256 MB Infinity Cache cannot serve them.  Inputs are seeded synthetic data.
+
+Timing protocol.  Every timed region follows a time-based warm-up on its own workload (the
+GPU runs that workload for a fixed wall time first, whatever --warmup says, so that clocks
+and caches are at steady state after host-side setup).  The headline line times exactly
+--steps launches captured in one HIP graph, once.  The other decode lines run in two rounds,
+the second in reverse order (every pair of lines is timed A-B-B-A), each round timing three
+replays of a graph of at least 50 launches; the reported time is the median over all
+replays, with the per-round medians beside it.  All decode lines run before the epilogue,
+prefill and read-probe lines.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -32,6 +41,11 @@ PRIMARY = ("q4_gate_up_34816x5120", 1)
 ROTATE_BYTES = 512 << 20
 PREFILL_T = (512, 2048)                      # prefill chunk sizes timed on the GEMM route
 PREFILL_SHAPES = ("q5_down_5120x17408", "fp8_proj_5120x5120")
+WARM_S = 0.25            # wall time each decode line runs before it is timed
+WARM_HEADLINE_S = 1.0    # the same for the headline line
+MIN_CALLS = 50           # launches per timed replay on the decode lines
+REPLAYS = 3              # timed replays per line and round
+ROUNDS = 2               # the second in reverse order
 
 
 def log(*a):
@@ -78,74 +92,50 @@ class Resident:
         self.copies = []
 
 
-def time_run(res, T, steps, warmup):
-    """Eager stream launches.  Returns (ms_per_step over the timed region, and the per-launch
-    kernel ms from HIP events bracketing each launch on the launch stream: mean, median, 10th
-    and 90th percentiles)."""
-    import torch
-    import weight_only_quant_amd as wq
-    stream = torch.cuda.current_stream()
-    x, y = res.x[:T], res.y[:T]
-    hs = res.handles
-    for i in range(warmup):
-        wq.qmat_run(hs[i % len(hs)], x, y, T=T, stream=stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        ev[i][0].record(stream)
-        wq.qmat_run(hs[i % len(hs)], x, y, T=T, stream=stream)
-        ev[i][1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total = start.elapsed_time(end)
-    per = [a.elapsed_time(b) for a, b in ev]
-    return (total / steps, float(np.mean(per)), float(np.median(per)), float(np.percentile(per, 10)),
-            float(np.percentile(per, 90)))
+class Timed:
+    """n launches of one decode workload captured in one HIP graph (rotating over the
+    resident copies), replayed on the current stream."""
 
+    def __init__(self, res, T, n):
+        import gc
+        import torch
+        import weight_only_quant_amd as wq
+        self.res, self.T, self.n = res, T, n
+        x, y = res.x[:T], res.y[:T]
+        hs = res.handles
+        gc.collect()
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            for i in range(n):
+                wq.qmat_run(hs[i % len(hs)], x, y, T=T)
+        torch.cuda.synchronize()
 
-def time_graph(res, T, steps, warmup):
-    """The same K steps captured once into a HIP graph and replayed: the way a decode step
-    is launched in an engine.  Returns ms per step over the timed replay."""
-    import gc
-    import torch
-    import weight_only_quant_amd as wq
-    x, y = res.x[:T], res.y[:T]
-    hs = res.handles
-    gc.collect()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(steps):
-            wq.qmat_run(hs[i % len(hs)], x, y, T=T)
-    for _ in range(max(1, warmup // steps)):
-        g.replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
-    del g
-    return ms
+    def warm(self, seconds):
+        """Replay until `seconds` of wall time have passed (at least twice)."""
+        import torch
+        t0, k = time.time(), 0
+        while k < 2 or time.time() - t0 < seconds:
+            self.g.replay()
+            k += 1
+            if k % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
 
+    def time_once(self):
+        """One replay bracketed by events on the replay stream: ms per launch."""
+        import torch
+        stream = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        self.g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / self.n
 
-def measured_traffic(workload):
-    """HBM bytes per launch for a workload from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
-    if not os.path.exists(path):
-        return None
-    try:
-        from weight_only_quant_amd.rocprof_summary import kernel_source_sha256
-        rec = json.load(open(path))
-        if rec.get("kernel_source_sha256") != kernel_source_sha256():
-            return None
-        return int(round(rec["traffic_bytes"]))
-    except Exception:
-        return None
+    def close(self):
+        del self.g
 
 
 def qmat_packed_size(name):
@@ -165,25 +155,42 @@ def plan_str(res, T):
             f"splits={p.splits}{tail}{tiles}")
 
 
-EAGER_ONLY = False
-
-
-def measure(res, T, steps, warmup):
-    ms_e, k_mean, k_med, k_p10, k_p90 = time_run(res, T, steps, warmup)
-    ms_g = ms_e if EAGER_ONLY else time_graph(res, T, steps, warmup)
+def line(res, T, us_list, per_round):
+    """A decode line from per-launch times (µs) of all timed replays."""
     wl = res.wl
     ab = alg_bytes(wl.fmt, wl.M, wl.K, T)
-    return {"us_per_call": round(ms_g * 1e3, 3), "eager_us_per_call": round(ms_e * 1e3, 3),
-            "kernel_us": round(k_mean * 1e3, 3), "kernel_us_median": round(k_med * 1e3, 3),
-            "kernel_us_p10": round(k_p10 * 1e3, 3), "kernel_us_p90": round(k_p90 * 1e3, 3),
-            "GBps": round(ab / (ms_g * 1e-3) / 1e9, 1), "kernel_GBps": round(ab / (k_mean * 1e-3) / 1e9, 1),
-            "pct_hbm_peak": round(100 * ab / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+    us = float(np.median(us_list))
+    return {"us_per_call": round(us, 3), "us_min": round(min(us_list), 3), "us_max": round(max(us_list), 3),
+            "us_round_medians": [round(v, 3) for v in per_round], "timed_replays": len(us_list),
+            "GBps": round(ab / us / 1e3, 1), "pct_hbm_peak": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 2),
             "bytes": ab, "plan": plan_str(res, T)}
 
 
-def measure_epilogue(res, T, k, steps, warmup):
+def measure_decode(lines, steps):
+    """Every (Resident, T) in `lines`, ROUNDS rounds alternating forward / reverse order; each
+    round warms the line for WARM_S and times REPLAYS replays of a graph of >= MIN_CALLS
+    launches."""
+    times = {i: [] for i in range(len(lines))}
+    rounds = {i: [] for i in range(len(lines))}
+    for r in range(ROUNDS):
+        order = range(len(lines)) if r % 2 == 0 else reversed(range(len(lines)))
+        for i in order:
+            res, T = lines[i]
+            # every rotation copy at least once per replay (the small matrix has thousands)
+            n = max(MIN_CALLS, steps, min(len(res.handles), 4096))
+            tm = Timed(res, T, n)
+            tm.warm(WARM_S)
+            us = [tm.time_once() * 1e3 for _ in range(REPLAYS)]
+            tm.close()
+            times[i] += us
+            rounds[i].append(float(np.median(us)))
+            log(f"[bench] round {r} {res.name} T={T}: {np.median(us):.3f} us/call")
+    return {i: line(lines[i][0], lines[i][1], times[i], rounds[i]) for i in range(len(lines))}
+
+
+def measure_epilogue(res, T, k, warm_s=WARM_S, n=MIN_CALLS):
     """The output-head epilogue (per-token log-sum-exp and top-k) on the logits the head product
-    left in res.y, graph-replayed; bytes are the logits read (T * M * 4)."""
+    left in res.y, graph-replayed after a time-based warm-up; bytes are the logits read."""
     import torch
     import weight_only_quant_amd as wq
     M = res.wl.M
@@ -192,31 +199,34 @@ def measure_epilogue(res, T, k, steps, warmup):
     lse = torch.empty(T, device="cuda")
     v = torch.empty((T, k), device="cuda")
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    for _ in range(warmup):
-        wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
+    wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(steps):
+        for _ in range(n):
             wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
-    for _ in range(2):
+    t0 = time.time()
+    while time.time() - t0 < warm_s:
         g.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / steps * 1e3
+        torch.cuda.synchronize()
+    us = []
+    for _ in range(REPLAYS):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) / n * 1e3)
     del g
     wq.qmat_logits_destroy(e)
     nb = T * M * 4
-    return {"us_per_call": round(us, 3), "GBps": round(nb / us / 1e3, 1), "bytes": nb, "k": k}
+    u = float(np.median(us))
+    return {"us_per_call": round(u, 3), "GBps": round(nb / u / 1e3, 1), "bytes": nb, "k": k}
 
 
-def measure_prefill(res, T, steps=20, warmup=3, reference=False):
+def measure_prefill(res, T, calls=20, warm_s=WARM_S, reference=False):
     """A prefill-sized product (the GEMM route) on the resident matrix with T synthetic bf16
-    activation rows; throughput in TFLOP/s (2 T M K per call)."""
+    activation rows, after a time-based warm-up; throughput in TFLOP/s (2 T M K per call)."""
     import torch
     import weight_only_quant_amd as wq
     wl = res.wl
@@ -225,16 +235,22 @@ def measure_prefill(res, T, steps=20, warmup=3, reference=False):
     x = torch.randn((T, wl.K), generator=g, device="cuda").to(torch.bfloat16)
     y = torch.empty((T, wl.M), device="cuda")
     hs = res.handles
-    for i in range(warmup):
-        wq.qmat_run(hs[i % len(hs)], x, y, T=T)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(steps):
-        wq.qmat_run(hs[i % len(hs)], x, y, T=T)
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / steps * 1e3
+
+    def timed(fn):
+        t0, i = time.time(), 0
+        while i < 3 or time.time() - t0 < warm_s:
+            fn(i)
+            i += 1
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(calls):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / calls * 1e3
+
+    us = timed(lambda i: wq.qmat_run(hs[i % len(hs)], x, y, T=T))
     tf = 2.0 * T * wl.M * wl.K / us / 1e6
     out = {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1), "pct_bf16_mfma_peak": round(100 * tf / 2500.0, 2),
            "route": "gemm"}
@@ -242,28 +258,20 @@ def measure_prefill(res, T, steps=20, warmup=3, reference=False):
         # context, not the product: the vendor bf16 GEMM (torch.matmul -> hipBLASLt) on an
         # unquantized bf16 weight of the same shape, the practical matrix-core rate on this GPU
         w = torch.randn((wl.M, wl.K), generator=g, device="cuda").to(torch.bfloat16)
-        for i in range(warmup):
-            torch.matmul(x, w.t())
-        torch.cuda.synchronize()
-        a.record()
-        for i in range(steps):
-            torch.matmul(x, w.t())
-        b.record()
-        torch.cuda.synchronize()
-        ref_us = a.elapsed_time(b) / steps * 1e3
+        ref_us = timed(lambda i: torch.matmul(x, w.t()))
         out["bf16_vendor_gemm_us"] = round(ref_us, 2)
         out["bf16_vendor_gemm_TFLOPs"] = round(2.0 * T * wl.M * wl.K / ref_us / 1e6, 1)
+        out["pct_of_vendor_bf16_gemm"] = round(100 * ref_us / us, 1)
         del w
     del x, y
     return out
 
 
-def cpu_baseline(res, T, target_s=12.0):
+def cpu_baseline(wl, T, target_s=12.0):
     """The CPU oracle (as it stands) on a bounded sample of the same workload: whole passes
     over all rows (or a row subset when one pass would exceed the budget), repeated until
     about target_s seconds of CPU work have run."""
     import oracle
-    wl = res.wl
     threads = min(os.cpu_count() or 1, 16)
     x = wl.x[:T]
     probe = np.arange(min(wl.M, 512))
@@ -286,16 +294,16 @@ def cpu_baseline(res, T, target_s=12.0):
                       f"(fp64 scalar C, {threads} threads)"}
 
 
-def read_ceilings(window_bytes):
+def read_ceilings(window_bytes, big_bytes):
     """Practical read-bandwidth ceilings from the read-stream probe (libqmat_probe.so, a plain
-    16-byte-per-lane nontemporal read; best of a few launch shapes): over a 1 GiB buffer, and
-    over windows of the headline matrix's size rotated through that buffer (so each read
-    streams from HBM, as the rotated weight copies do)."""
+    16-byte-per-lane nontemporal read; best of its launch shapes): over a buffer at least as
+    large as the largest benchmark matrix, and over windows of the headline matrix's size
+    rotated through 1 GiB (so each read streams from HBM, as the rotated weight copies do)."""
     from weight_only_quant_amd import probe
-    big, big_shapes = probe.best_read_gbs(1 << 30)
+    big, big_shapes = probe.best_read_gbs(big_bytes)
     w = window_bytes // 1024 * 1024
     win, _ = probe.best_read_gbs(1 << 30, window=w, reps=100)
-    return {"GBps_1GiB": big, "shapes_1GiB": big_shapes, "GBps_window": win, "window_bytes": w}
+    return {"GBps_big": big, "big_bytes": big_bytes, "shapes_big": big_shapes, "GBps_window": win, "window_bytes": w}
 
 
 def read_probe_window(window_bytes):
@@ -311,9 +319,9 @@ def cpu_context(target_s=1.0):
     import qmat_inputs as qi
     model = "unknown"
     try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
                 break
     except OSError:
         pass
@@ -332,22 +340,23 @@ def cpu_context(target_s=1.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=800)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="graph replays after the time-based warm-up (which always runs)")
     ap.add_argument("--primary-only", action="store_true", help="skip the other benchmark shapes")
     ap.add_argument("--only", default=None, help="comma-separated config names for the extra shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (known bytes) for scaling PMC byte counters")
     ap.add_argument("--eager-only", action="store_true",
-                    help="time eager stream launches only (no graph replay), e.g. under a counter profiler")
+                    help="time eager stream launches only (no graph replay), for counter profilers that "
+                         "serialize dispatches")
     args = ap.parse_args()
-    global EAGER_ONLY
-    EAGER_ONLY = args.eager_only
     if args.gpus != 1:
-        log("bench.py: the benchmark runs on one GPU only (the product shards by rows with no "
-            "collective; see the design notes); --gpus must be 1")
+        log("bench.py: this benchmark runs on one GPU only: the product shards by rows with no "
+            "collective, so a multi-GPU figure would be N independent copies of this one; --gpus must be 1")
         sys.exit(2)
 
     import torch
@@ -370,14 +379,33 @@ def main():
     name, T = PRIMARY
     res = Resident(name)
     wl = res.wl
-    m = measure(res, T, args.steps, args.warmup)
-    ab = m["bytes"]
-    ms = m["us_per_call"] * 1e-3
+    ab = alg_bytes(wl.fmt, wl.M, wl.K, T)
+    if args.eager_only:
+        hs = res.handles
+        for i in range(args.warmup):
+            wq.qmat_run(hs[i % len(hs)], res.x[:T], res.y[:T], T=T)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(args.steps):
+            wq.qmat_run(hs[i % len(hs)], res.x[:T], res.y[:T], T=T)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        extra_replays = []
+    else:
+        # exactly --steps launches in one graph: time-based warm-up, --warmup more replays,
+        # then one timed replay (the contract's timed region)
+        tm = Timed(res, T, args.steps)
+        tm.warm(WARM_HEADLINE_S)
+        for _ in range(args.warmup):
+            tm.g.replay()
+        ms = tm.time_once()
+        # more replays of the same graph, reported beside the line (not the headline value)
+        extra_replays = [round(tm.time_once() * 1e3, 3) for _ in range(5)]
+        tm.close()
     value = ab / (ms * 1e-3) / 1e9
-    # one launch per step: the average launch duration is the graph-replay time per step
-    # (kernel plus the inter-kernel gap); per-launch event brackets add their own flushes
-    achieved = value
-    log(f"[bench] {name} T={T}: {m}")
+    log(f"[bench] {name} T={T}: {ms * 1e3:.3f} us/call, {value:.1f} GB/s; more replays {extra_replays}")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -394,72 +422,79 @@ def main():
         "config": {"workload": f"{name}_T{T}", "format": "Q4 groupwise (64-weight groups, FP16 scales)",
                    "M": wl.M, "K": wl.K, "T": T, "x": "bf16", "y": "fp32", "global_batch": T,
                    "parallelism": "single-gpu", "rotation_copies": len(res.copies),
-                   "launch": "eager stream launches" if EAGER_ONLY else "K steps captured in one HIP graph and replayed",
-                   "plan": m["plan"]},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"{name}_T{T}"),
-                     "launch_us_mean": m["us_per_call"], "event_bracketed_launch_us_mean": m["kernel_us"],
-                     "event_bracketed_launch_us_median": m["kernel_us_median"], "bytes_per_launch": ab},
-        "us_per_call": m["us_per_call"],
-        "eager_us_per_call": m["eager_us_per_call"],
+                   "launch": "eager stream launches" if args.eager_only else
+                             "--steps launches captured in one HIP graph, one timed replay after a "
+                             f"{WARM_HEADLINE_S:.1f} s time-based warm-up",
+                   "plan": plan_str(res, T)},
+        # one launch per step: the average launch duration over the timed region is the time
+        # per step (kernel plus the dispatch gap between graph nodes)
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"{name}_T{T}"),
+                     "launch_us_mean": round(ms * 1e3, 3), "bytes_per_launch": ab,
+                     "more_replays_us": extra_replays},
+        "us_per_call": round(ms * 1e3, 3),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
     }
     extra = {}
-    if not args.no_cpu_baseline:
-        log("[bench] CPU oracle baseline ...")
-        out["cpu_baseline"] = cpu_baseline(res, T)
-        log(f"[bench] cpu_baseline {out['cpu_baseline']}")
-    # the same workload at its other token counts
-    for T2 in qi.CONFIGS[name][3]:
-        if T2 == T:
-            continue
-        extra[f"{name}_T{T2}"] = measure(res, T2, args.steps, args.warmup)
-        log(f"[bench] {name} T={T2}: {extra[f'{name}_T{T2}']}")
+    if args.eager_only:
+        res.close()
+        out["extra"] = extra
+        print(json.dumps(out), flush=True)
+        return
+
+    # every decode line (all resident at once), interleaved rounds
+    residents = {name: res}
+    names = [] if args.primary_only else [n for n in qi.CONFIGS if n != name]
+    if args.only:
+        names = [n for n in names if n in args.only.split(",")]
+    for n in names:
+        residents[n] = Resident(n)
+    lines = [(res, T2) for T2 in qi.CONFIGS[name][3] if T2 != T]
+    for n in names:
+        lines += [(residents[n], T2) for T2 in qi.CONFIGS[n][3]]
+    results = measure_decode(lines, args.steps)
+    for i, (r, T2) in enumerate(lines):
+        extra[f"{r.name}_T{T2}"] = results[i]
+        log(f"[bench] {r.name} T={T2}: {results[i]}")
+
+    # the output-head epilogue on the Q6 head's logits (the last product left them in y)
+    if "q6_head_248320x5120" in residents:
+        r = residents["q6_head_248320x5120"]
+        for T2 in qi.CONFIGS[r.name][3]:
+            wq.qmat_run(r.handles[0], r.x[:T2], r.y[:T2], T=T2)
+            key = f"head_epilogue_lse_top20_248320_T{T2}"
+            extra[key] = measure_epilogue(r, T2, 20)
+            log(f"[bench] {key}: {extra[key]}")
+
     # prefill-sized token counts (the GEMM route)
-    for T2 in PREFILL_T:
-        key = f"{name}_prefill_T{T2}"
-        extra[key] = measure_prefill(res, T2, reference=True)
-        log(f"[bench] {key}: {extra[key]}")
-    res.close()
+    if not args.no_prefill:
+        for n in [name] + [p for p in PREFILL_SHAPES if p in residents]:
+            for T3 in PREFILL_T:
+                key = f"{n}_prefill_T{T3}"
+                extra[key] = measure_prefill(residents[n], T3, reference=(n == name))
+                log(f"[bench] {key}: {extra[key]}")
+    for r in residents.values():
+        r.close()
+    residents.clear()
     del res
     torch.cuda.empty_cache()
-    if not args.primary_only:
-        names = [n for n in qi.CONFIGS if n != name]
-        if args.only:
-            names = [n for n in names if n in args.only.split(",")]
-        for n in names:
-            r = Resident(n)
-            for T2 in qi.CONFIGS[n][3]:
-                steps = args.steps if r.wl.M * r.wl.K < 1e9 else max(50, args.steps // 4)
-                extra[f"{n}_T{T2}"] = measure(r, T2, steps, args.warmup)
-                log(f"[bench] {n} T={T2}: {extra[f'{n}_T{T2}']}")
-                if n in PREFILL_SHAPES and T2 == qi.CONFIGS[n][3][0]:
-                    for T3 in PREFILL_T:
-                        key = f"{n}_prefill_T{T3}"
-                        extra[key] = measure_prefill(r, T3)
-                        log(f"[bench] {key}: {extra[key]}")
-                if n == "q6_head_248320x5120":
-                    key = f"head_epilogue_lse_top20_248320_T{T2}"
-                    extra[key] = measure_epilogue(r, T2, 20, args.steps, 20)
-                    log(f"[bench] {key}: {extra[key]}")
-            r.close()
-            del r
-            torch.cuda.empty_cache()
+
     if not args.no_ceiling:
-        c = read_ceilings(qmat_packed_size(name))
-        out["read_stream_ceiling_GBps"] = c["GBps_1GiB"]
+        big = max(1 << 30, max(qmat_packed_size(n) for n in qi.CONFIGS) + (256 << 20)) // (1 << 20) * (1 << 20)
+        c = read_ceilings(qmat_packed_size(name), big)
+        out["read_stream_ceiling_GBps"] = c["GBps_big"]
         out["read_stream"] = c
-        out["pct_of_read_ceiling"] = round(100 * value / c["GBps_1GiB"], 2)
+        out["pct_of_read_ceiling"] = round(100 * value / c["GBps_big"], 2)
         out["pct_of_same_size_read"] = round(100 * value / c["GBps_window"], 2)
         out["same_size_read_us"] = round(c["window_bytes"] / (c["GBps_window"] * 1e3), 3)
-        # every product line against the 1 GiB read, and the matrices that rotate (< 512 MB)
+        # every product line against the large read, and the matrices that rotate (< 512 MB)
         # also against a plain read of their own packed size (fixed launch, first-byte and drain
         # costs included), timed the same way
         windows = {name: c["GBps_window"]}
         for key, v in extra.items():
             if not ("GBps" in v and "bytes" in v and "k" not in v):
                 continue
-            v["pct_of_read_ceiling"] = round(100 * v["GBps"] / c["GBps_1GiB"], 2)
+            v["pct_of_read_ceiling"] = round(100 * v["GBps"] / c["GBps_big"], 2)
             wname = key.rsplit("_T", 1)[0]
             size = qmat_packed_size(wname) // 1024 * 1024 if wname in qi.CONFIGS else 0
             if not 0 < size < (512 << 20):
@@ -470,10 +505,29 @@ def main():
             v["pct_of_same_size_read"] = round(100 * v["same_size_read_us"] / v["us_per_call"], 2)
         log(f"[bench] read stream: {c}")
     if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline(wl, T)
+        log(f"[bench] cpu_baseline {out['cpu_baseline']}")
         out["cpu_context"] = cpu_context()
         log(f"[bench] cpu context {out['cpu_context']}")
     out["extra"] = extra
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch for a workload from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        from weight_only_quant_amd.rocprof_summary import kernel_source_sha256
+        rec = json.load(open(path))
+        if rec.get("kernel_source_sha256") != kernel_source_sha256():
+            return None
+        return int(round(rec["traffic_bytes"]))
+    except Exception:
+        return None
 
 
 if __name__ == "__main__":

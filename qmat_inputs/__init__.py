@@ -125,6 +125,9 @@ CONFIGS: Dict[str, tuple] = {
     "fp8_proj_5120x5120": (FP8, 5120, 5120, [1, 8, 16], 0.01),
     # the upstream artifact's 8-bit output head (the pages time its 8-token verify)
     "q8_head_248320x5120": (Q8, 248320, 5120, [1, 8], 0.0005),
+    # the 131,072-row proposal head kept in the upstream 8-bit encoding, whose rows stand for
+    # vocabulary ids through an index map
+    "q8_proposal_head_131072x5120": (Q8, 131072, 5120, [1, 8, 16], 0.0005),
 }
 
 
