@@ -116,10 +116,10 @@ struct qmat {
     int64_t M, K, NT, NU, Mpad;
     const uint8_t *codes;   // first code block of the handle's first tile (borrowed)
     const uint8_t *scales;  // its first scale block (borrowed)
-    float *ws;
+    float *ws;          // GEMM route: split-K partial sums (scratch)
     size_t ws_floats;
-    uint32_t *counters;
-    int64_t n_counters;
+    uint64_t *nodes;    // small-T routes: tree-node words of shared tiles (all zero between calls)
+    size_t node_words;
     int device;
     int cus;
     Plan plan[2][kMaxT + 1];  // [route - 1][tokens per launch]
@@ -199,9 +199,9 @@ int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *co
     h->codes = codes;
     h->scales = scales;
     h->ws = nullptr;
-    h->counters = nullptr;
+    h->nodes = nullptr;
     h->ws_floats = 0;
-    h->n_counters = 0;
+    h->node_words = 0;
     if (hipGetDevice(&h->device) != hipSuccess) {
         delete h;
         return fail(QMAT_EHIP, "%s: hipGetDevice failed", who);
@@ -210,19 +210,20 @@ int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *co
         delete h;
         return fail(QMAT_EHIP, "%s: cannot read the compute unit count", who);
     }
-    // launch plans for both routes and every tokens-per-launch; the workspace covers the
-    // largest split-K partial set among them, and at least 8 splits at T = 16 for matrices of
-    // up to 4096 rows (explicit launch shapes in tests and tuning)
-    size_t need_ws = 0;
+    // launch plans for both routes and every tokens-per-launch; the tree nodes cover the largest
+    // split among them, and at least 8 splits at T = 16 for matrices of up to 4096 rows (explicit
+    // launch shapes in tests and tuning)
+    size_t need_nodes = 0;
     for (int r = kRouteValu; r <= kRouteMfma; ++r)
         for (int T = 1; T <= kMaxT; ++T) {
             const int Tl = launch_tokens(r, T);
             const Plan p = make_plan(fmt, r, Tl, h->NT, h->NU, h->cus);
             h->plan[r - 1][T] = p;
-            const size_t f = run_workspace_floats(Tl, (int)h->NT, p.splits, p.tail_tiles, p.tail_splits);
-            if (f > need_ws) need_ws = f;
+            const size_t f = run_node_words(Tl, (int)h->NT, p.splits, p.tail_tiles, p.tail_splits);
+            if (f > need_nodes) need_nodes = f;
         }
-    if (h->Mpad <= 4096 && need_ws < (size_t)8 * kMaxT * h->Mpad) need_ws = (size_t)8 * kMaxT * h->Mpad;
+    if (h->Mpad <= 4096 && need_nodes < (size_t)7 * kMaxT * h->Mpad) need_nodes = (size_t)7 * kMaxT * h->Mpad;
+    size_t need_ws = 0;
     // the GEMM route's automatic k splits (each within the cap by construction); beyond
     // 2 workgroup waves of row blocks x token tiles no split pays
     for (int ntt = 1; gemm_row_blocks((int)h->NT) * (int64_t)ntt <= 4LL * h->cus; ++ntt) {
@@ -230,7 +231,6 @@ int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *co
         const size_t f = gemm_workspace_floats(T, (int)h->NT, gemm_auto_splits(h->NT, h->NU, T, h->cus));
         if (f > need_ws) need_ws = f;
     }
-    h->n_counters = h->NT;
     if (need_ws > 0) {
         h->ws_floats = need_ws;
         if (hipMalloc(&h->ws, h->ws_floats * sizeof(float)) != hipSuccess) {
@@ -238,18 +238,23 @@ int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *co
             delete h;
             return fail(QMAT_ENOMEM, "%s: workspace allocation failed", who);
         }
-        if (hipMalloc(&h->counters, (size_t)h->n_counters * sizeof(uint32_t)) != hipSuccess) {
+    }
+    if (need_nodes > 0) {
+        h->node_words = need_nodes;
+        if (hipMalloc(&h->nodes, h->node_words * sizeof(uint64_t)) != hipSuccess) {
             (void)hipGetLastError();
-            (void)hipFree(h->ws);
+            if (h->ws) (void)hipFree(h->ws);
             delete h;
-            return fail(QMAT_ENOMEM, "%s: counter allocation failed", who);
+            return fail(QMAT_ENOMEM, "%s: workspace allocation failed", who);
         }
-        if (hipMemset(h->counters, 0, (size_t)h->n_counters * sizeof(uint32_t)) != hipSuccess ||
+        // the tree nodes start empty; every call leaves them empty again
+        if (hipMemset(h->nodes, 0, h->node_words * sizeof(uint64_t)) != hipSuccess ||
             hipDeviceSynchronize() != hipSuccess) {
-            (void)hipFree(h->ws);
-            (void)hipFree(h->counters);
+            (void)hipGetLastError();
+            if (h->ws) (void)hipFree(h->ws);
+            (void)hipFree(h->nodes);
             delete h;
-            return fail(QMAT_EHIP, "%s: counter initialisation failed", who);
+            return fail(QMAT_EHIP, "%s: workspace initialisation failed", who);
         }
     }
     *handle = h;
@@ -308,7 +313,7 @@ int run_gemm(qmat_t h, const void *x_dev, float *y_dev, int T, int S, void *stre
         return fail(QMAT_ESIZE, "qmat_run: %d GEMM splits at T=%d exceed the workspace", S, T);
     RunArgs a{};
     a.ws = h->ws;
-    a.counters = h->counters;
+    a.nodes = nullptr;
     a.codes = h->codes;
     a.scales = h->scales;
     a.x = static_cast<const uint16_t *>(x_dev);
@@ -351,7 +356,7 @@ int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, vo
     const int64_t grid = (int64_t)p.tail_tiles * tail_splits + (h->NT - p.tail_tiles) * (int64_t)p.splits;
     if (grid > 0x7FFFFFFFLL) return fail(QMAT_ESIZE, "qmat_run: grid of %lld workgroups too large", (long long)grid);
     const int Tl = launch_tokens(p.route, T);
-    if (run_workspace_floats(Tl, (int)h->NT, p.splits, p.tail_tiles, tail_splits) > h->ws_floats)
+    if (run_node_words(Tl, (int)h->NT, p.splits, p.tail_tiles, tail_splits) > h->node_words)
         return fail(QMAT_ESIZE, "qmat_run: splits %d / tail %d x %d at %d tokens exceed the workspace", p.splits,
                     p.tail_tiles, tail_splits, Tl);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -364,8 +369,8 @@ int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, vo
         a.scales = scales;
         a.x = x + (int64_t)t0 * h->K;
         a.y = y_dev + (int64_t)t0 * h->M;
-        a.ws = h->ws;
-        a.counters = h->counters;
+        a.ws = nullptr;
+        a.nodes = h->nodes;
         a.ldy = h->M;
         a.M = (int)h->M;
         a.K = (int)h->K;
@@ -472,14 +477,14 @@ int qmat_dequant(qmat_t h, float *w_dev, void *stream)
 size_t qmat_workspace_bytes(qmat_t h)
 {
     if (!h) return 0;
-    return h->ws_floats * sizeof(float) + (h->counters ? (size_t)h->n_counters * sizeof(uint32_t) : 0);
+    return h->ws_floats * sizeof(float) + h->node_words * sizeof(uint64_t);
 }
 
 void qmat_destroy(qmat_t h)
 {
     if (!h) return;
     if (h->ws) (void)hipFree(h->ws);
-    if (h->counters) (void)hipFree(h->counters);
+    if (h->nodes) (void)hipFree(h->nodes);
     delete h;
 }
 

@@ -7,12 +7,13 @@
 
 namespace qmatk {
 
-// Workspace floats one launch needs (0 when no tile is shared by several workgroups).
-inline size_t run_workspace_floats(int T, int NT, int S, int NTt, int St)
+// 64-bit tree-node words one launch needs to sum the partial tiles of tiles shared by several
+// workgroups (S - 1 nodes per element of a tile shared S ways; 0 when no tile is shared).
+inline size_t run_node_words(int T, int NT, int S, int NTt, int St)
 {
     size_t f = 0;
-    if (S > 1) f += (size_t)S * T * (size_t)(NT - NTt) * 64;
-    if (NTt > 0 && St > 1) f += (size_t)St * T * (size_t)NTt * 64;
+    if (S > 1) f += (size_t)(S - 1) * T * (size_t)(NT - NTt) * 64;
+    if (NTt > 0 && St > 1) f += (size_t)(St - 1) * T * (size_t)NTt * 64;
     return f;
 }
 
@@ -25,9 +26,10 @@ struct RunArgs {
     const uint8_t *scales;  // packed scale blocks
     const uint16_t *x;      // bf16 [T][K]
     float *y;               // fp32 [T][ldy]
-    float *ws;              // split-K partials: leading tiles [S][T][(NT-NTt)*64] when S > 1,
-                            // then trailing tiles [St][T][NTt*64] when St > 1
-    uint32_t *counters;     // one arrival counter per tile (S > 1 only), zero between launches
+    float *ws;              // GEMM route: split-K partials (scratch)
+    uint64_t *nodes;        // small-T routes: tree-node words of the shared tiles, all zero between
+                            // calls: leading tiles [S-1][T][(NT-NTt)*64] when S > 1, then
+                            // trailing tiles [St-1][T][NTt*64] when St > 1
     int64_t ldy;            // row stride of y in elements (M)
     int M, K, T, NT, NU, S;
     int NTt, St;            // trailing tiles and their k splits (NTt == 0: every tile uses S)

@@ -21,9 +21,9 @@
 // No offset-binary tricks: a row with sparse or zero codes has no cancellation error.
 //
 // Work split: a wave owns one 64-row tile and a contiguous range of 128-wide k units.  NW waves
-// of a workgroup split a tile's units and reduce through LDS; S workgroups split further and the
-// last-arriving one adds the S partials from the workspace in a fixed order (deterministic, no
-// atomics on data, no memset: the arrival counter is reset by the last block).
+// of a workgroup split a tile's units and reduce through LDS; S workgroups split further and
+// their partial tiles meet over a fixed binary tree of atomic exchanges (see finish):
+// deterministic, and no memset (every tree word is empty again when a call ends).
 #include <hip/hip_runtime.h>
 
 #include "qmat_device.h"
@@ -39,8 +39,8 @@ namespace qmatk {
 struct Slice {
     int tile, sp, S, w, nw, u0, u1;
     int sl, nsl;
-    int wsrow, wsld;  // the tile's first row and the row count of its workspace region
-    int64_t wsoff;    // start of that region in the workspace (floats)
+    int wsrow, wsld;  // the tile's first row and the row count of its tree-node region
+    int64_t wsoff;    // start of that region among the tree-node words
 };
 
 // Workgroup -> (tile, split, splits of that tile).  The trailing NTt tiles come first in the grid
@@ -59,7 +59,7 @@ __device__ __forceinline__ Slice make_slice(const RunArgs &a)
         s.S = a.St;
         s.wsrow = tt * kTileRows;
         s.wsld = a.NTt * kTileRows;
-        s.wsoff = a.S > 1 ? (int64_t)a.S * a.T * nlead * kTileRows : 0;
+        s.wsoff = a.S > 1 ? (int64_t)(a.S - 1) * a.T * nlead * kTileRows : 0;
     } else {
         const int c = b - ntail;
         s.tile = c / a.S;
@@ -98,6 +98,17 @@ __device__ __forceinline__ float ordered_sum(int S, Load load)
 // Combine the waves' and workgroups' partial tiles and write y.  Every wave passes its values
 // through put(t, row_in_tile, v) calls made identically by all waves (same (t, row) sets).
 // red: dynamic LDS of nw * T * 64 floats (unused when nw == 1 and S == 1).
+//
+// Tiles shared by S > 1 workgroups are summed over a fixed binary tree of the S splits (pairs
+// (0,1), (2,3), ... at the first level; a split without a partner moves up unchanged).  Two
+// partial sums meet in one 64-bit word of the tile's tree nodes: each side swaps in {1, bits of
+// its value} with one agent-scope atomic exchange.  Exchanges of one location are totally
+// ordered, so exactly one side gets back the empty word {0, 0} and is done; the other gets its
+// partner's value, adds it (fp32 addition is commutative, so the sum has the same bits
+// whichever side arrives second), clears the word for the next call and carries the sum to the
+// next level.  Whoever completes the root writes y.  Every element meets independently: no
+// counters, barriers or fences, one memory round trip per tree level, and the same bits on
+// every run of the same plan.
 template <typename ForEach>
 __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *red, ForEach for_each)
 {
@@ -108,11 +119,11 @@ __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *
         });
         return;
     }
+    // the waves' partial tiles through LDS (also with one wave when the tile is shared: the tree
+    // below walks the tile's elements by thread, not by the lanes that computed them)
     const int n = a.T * kTileRows;
-    if (s.nw > 1) {
-        for_each([&](int t, int r, float v) { red[s.w * n + t * kTileRows + r] = v; });
-        __syncthreads();
-    }
+    for_each([&](int t, int r, float v) { red[s.w * n + t * kTileRows + r] = v; });
+    __syncthreads();
     const int nthr = blockDim.x;
     if (s.S == 1) {
         for (int e = threadIdx.x; e < n; e += nthr) {
@@ -123,51 +134,33 @@ __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *
         }
         return;
     }
-    // S > 1.  The workgroup's partial tile goes to the workspace through returning agent-scope
-    // atomic exchanges: each is performed at the device coherence point before its old value
-    // comes back, and every thread consumes its old values before the barrier, so all of the
-    // tile's partials are in place before thread 0 bumps the arrival counter.  The last of the
-    // S workgroups to arrive reads the S partials with agent-scope atomic loads and adds them
-    // in split order (deterministic).  No cache-wide fences, no memset: the last block resets
-    // the counter for the next call.
-    float *wsr = a.ws + s.wsoff + s.wsrow;
-    float *wsp = wsr + (int64_t)s.sp * a.T * s.wsld;
-    uint32_t sink = 0;
-    auto publish = [&](int t, int r, float v) {
-        uint32_t *p = reinterpret_cast<uint32_t *>(wsp + (int64_t)t * s.wsld + r);
-        sink |= __hip_atomic_exchange(p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    if (s.nw > 1) {
-        for (int e = threadIdx.x; e < n; e += nthr) {
-            float v = red[e];
-            for (int w = 1; w < s.nw; ++w) v += red[w * n + e];
-            const int t = e / kTileRows, r = e - t * kTileRows;
-            publish(t, r, v);
-        }
-    } else {
-        for_each(publish);
-    }
-    asm volatile("" ::"v"(sink));
-    __syncthreads();
-    __shared__ int last;
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[s.tile], 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        last = (prev == (uint32_t)(s.S - 1));
-    }
-    __syncthreads();
-    if (!last) return;
+    // the tile's node words: one level slot [node][t][row of the region] per tree node
+    uint64_t *nodes = a.nodes + s.wsoff;
+    const int64_t nstride = (int64_t)a.T * s.wsld;
     for (int e = threadIdx.x; e < n; e += nthr) {
         const int t = e / kTileRows, r = e - t * kTileRows;
-        if (row0 + r >= a.M) continue;
-        uint32_t *p = reinterpret_cast<uint32_t *>(wsr + (int64_t)t * s.wsld + r);
-        a.y[(int64_t)t * a.ldy + row0 + r] = ordered_sum(s.S, [&](int sp) {
-            return __builtin_bit_cast(float, __hip_atomic_load(p + (int64_t)sp * a.T * s.wsld, __ATOMIC_RELAXED,
-                                                               __HIP_MEMORY_SCOPE_AGENT));
-        });
+        if (row0 + r >= a.M) continue;  // padding rows: skipped by every split alike
+        float v = red[e];
+        for (int w = 1; w < s.nw; ++w) v += red[w * n + e];
+        const int64_t wd = (int64_t)t * s.wsld + s.wsrow + r;
+        int p = s.sp, m = s.S;
+        int64_t base = 0;
+        bool done = false;
+        while (m > 1) {
+            if ((p ^ 1) < m) {
+                uint64_t *slot = nodes + (base + (p >> 1)) * nstride + wd;
+                const uint64_t old = __hip_atomic_exchange(slot, (1ull << 32) | __builtin_bit_cast(uint32_t, v),
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((old >> 32) == 0) { done = true; break; }
+                v = __builtin_bit_cast(float, (uint32_t)old) + v;
+                __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            base += m >> 1;
+            p >>= 1;
+            m = (m + 1) >> 1;
+        }
+        if (!done) a.y[(int64_t)t * a.ldy + row0 + r] = v;
     }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&a.counters[s.tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ unit loads
@@ -691,12 +684,11 @@ static const void *run_kernel_for(int fmt, int route, int T, int depth, int tile
     }
 }
 
-static size_t run_lds_bytes(int route, int waves, int T, int NU, int S)
+// dynamic LDS of the small-T kernels: the waves' partial tiles, when a workgroup has several
+// waves or its tile is shared with other workgroups
+static size_t run_lds_bytes(int waves, int T, bool shared)
 {
-    (void)route;
-    (void)NU;
-    (void)S;
-    return waves > 1 ? (size_t)waves * T * kTileRows * sizeof(float) : 0;
+    return waves > 1 || shared ? (size_t)waves * T * kTileRows * sizeof(float) : 0;
 }
 
 
@@ -708,15 +700,16 @@ hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves
     RunArgs arg = a;
     void *args[] = {&arg};
     const int64_t grid = tiles == 2 ? (int64_t)(a.NT + 1) / 2 * a.S : (int64_t)a.NTt * a.St + (int64_t)(a.NT - a.NTt) * a.S;
-    return hipLaunchKernel(k, dim3((unsigned)grid), dim3((unsigned)(64 * waves)), args,
-                           run_lds_bytes(route, waves, a.T, a.NU, a.S), st);
+    const bool shared = a.S > 1 || (a.NTt > 0 && a.St > 1);
+    return hipLaunchKernel(k, dim3((unsigned)grid), dim3((unsigned)(64 * waves)), args, run_lds_bytes(waves, a.T, shared),
+                           st);
 }
 
 int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int NU, int S)
 {
     const void *k = run_kernel_for(fmt, route, T, depth, 1);
     int n = 0;
-    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * waves, run_lds_bytes(route, waves, T, NU, S)) !=
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * waves, run_lds_bytes(waves, T, S > 1)) !=
                   hipSuccess)
         return 0;
     return n;
