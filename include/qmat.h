@@ -48,7 +48,9 @@ extern "C" {
 typedef enum {
     QMAT_OK = 0,
     QMAT_EINVAL = 1, /* bad format, null pointer, bad handle, bad route */
-    QMAT_ESHAPE = 2, /* M < 1, K < 64, K % 64 != 0, T outside [0, 16] */
+    QMAT_ESHAPE = 2, /* M < 1, K < 64, K % 64 != 0; T < 0, or T above the route's limit (16 on
+                        the small-T routes, 4194240 on the GEMM route that qmat_run takes for
+                        T > 16) */
     QMAT_ERANGE = 3, /* code outside the format's range, NaN FP8 byte, non-finite scale */
     QMAT_ESIZE = 4,  /* a buffer is smaller than required, or a launch shape exceeds the workspace */
     QMAT_EHIP = 5,   /* a HIP runtime call or kernel launch failed */
@@ -84,6 +86,12 @@ typedef struct qmat *qmat_t;
 size_t qmat_packed_bytes(int fmt, int64_t M, int64_t K);
 
 /* Pack a matrix into the layout above.  Host only; pure; thread-safe.
+ * What is stored is exactly the information of the formats' definitions: the b-bit two's
+ * complement codes and one FP16 scale per 64-weight group along K ("Qwen3.8-27B for NInfer on
+ * the RTX 3090", "What is different from the upstream artifact"), or the E4M3 bytes and one
+ * scale per row of the row-scaled FP8 tensors ("Qwen3.8-27B NVFP4 for NInfer", "Artifact"); the
+ * engine on those pages likewise re-encodes tensors once, at load ("Qwen3.8-27B for NInfer on
+ * the RTX 3090", "Measurements": the embedding transcoded to 4 bits at load).
  *   codes:  groupwise: int8 [M][K], each in [-2^(b-1), 2^(b-1)-1] (b = 4, 5, 6, or 8 for Q8);
  *           FP8: uint8 [M][K] E4M3 bytes (0x7F / 0xFF, the NaNs, are rejected).
  *   scales: groupwise: uint16 [M][K/64] binary16 bit patterns, finite, any sign;
@@ -125,12 +133,16 @@ typedef enum {
 int qmat_quantize(int fmt, int64_t M, int64_t K, const float *w, const float *importance, int encoder,
                   void *codes_out, void *scales_out);
 
-/* Create a handle over a packed matrix already in device memory.
+/* Create a handle over a packed matrix already in device memory: the weight operand of the
+ * decode and verify products whose speed the pages measure ("Qwen3.8-27B for NInfer on the
+ * RTX 3090", "Measurements": the 6-bit output head under an 8-token verify).
  *   packed_dev: device pointer to qmat_pack's output (bytes == qmat_packed_bytes, 16-byte
  *               aligned).  Borrowed: it must outlive the handle and is never written.
- * The handle owns a split-K workspace (device) that it allocates here: small-T partial sums,
- * and for matrices of fewer than 1024 rows per CU up to 32 MB for the GEMM route's k splits.  Calls that share one handle must therefore be ordered (one stream, or
- * synchronized streams).
+ * The handle owns a device workspace that it allocates and zero-fills here: the tree words
+ * that sum the partial results of row tiles whose K range is split across workgroups (every
+ * call leaves them zero again), and, for matrices of fewer than 1024 rows per CU, up to 32 MB
+ * for the GEMM route's k splits.  Calls that share one handle must therefore be ordered (one
+ * stream, or synchronized streams).
  * Errors: QMAT_EINVAL, QMAT_ESHAPE, QMAT_ESIZE (bytes mismatch), QMAT_ENOMEM, QMAT_EHIP. */
 int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packed_dev, size_t bytes);
 
@@ -145,8 +157,14 @@ int qmat_create(qmat_t *handle, int fmt, int64_t M, int64_t K, const void *packe
  * Errors: QMAT_EINVAL (null pointers), QMAT_ESHAPE (row range), QMAT_ENOMEM, QMAT_EHIP. */
 int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows);
 
-/* y = x . W^T.  x: device bf16 [T][K] (16-byte aligned); y: device fp32 [T][M], fully
- * overwritten.  T == 0 is a no-op.  Decode and verify sizes (T <= 16) take the small-T routes;
+/* y = x . W^T, with W as the format defines it (w = fp32(scale) * code per 64-weight group,
+ * "Qwen3.8-27B for NInfer on the RTX 3090", "What is different from the upstream artifact";
+ * w = fl32(r * e4m3) per row, "Qwen3.8-27B NVFP4 for NInfer", "Artifact") applied to T tokens:
+ * T = 1 is decode, T <= 16 a speculative verify of up to 15 drafts (the NVFP4 card's "Artifact"
+ * section; the RTX 3090 card's "Measurements" times the head's 8-token verify).  y is computed
+ * with fp32 accumulation of exact bf16 products; it agrees with the exact sum to within
+ * 1e-4 * sum_j |w_ij x_tj| + 1e-6 per element.
+ * x: device bf16 [T][K] (16-byte aligned); y: device fp32 [T][M], fully overwritten.  T == 0 is a no-op.  Decode and verify sizes (T <= 16) take the small-T routes;
  * prefill sizes (17 <= T <= 4194240) the GEMM route, where each unpacked weight feeds the
  * matrix cores for 64 tokens (the pages' prefill, where the groupwise route is capped by the
  * 4-bit -> bf16 decoding: "Qwen3.6-35B-A3B NVFP4" / "Qwen3.8-27B EXL3" speed notes).  When a
@@ -159,12 +177,13 @@ int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream
 
 /* A launch shape of the product kernel.  The matrix is cut into NT = ceil(M/64) row tiles;
  * a workgroup of `waves` waves works on one tile (or on two neighbouring tiles, see `tiles`)
- * and splits the tile's 128-wide k units among its waves.  The leading NT - tail_tiles tiles are each shared by `splits` workgroups along K,
- * the trailing tail_tiles tiles by `tail_splits` workgroups (a way to spread a few leftover
- * tiles over the whole GPU when NT is not a multiple of the compute-unit count).  Tiles shared
- * by several workgroups are summed through the handle's workspace in a fixed order, so every
- * plan gives the same y for the same inputs run after run (different plans may differ in the
- * last bits: the summation order differs). */
+ * and splits the tile's 128-wide k units among its waves.  The leading NT - tail_tiles tiles
+ * are each shared by `splits` workgroups along K, the trailing tail_tiles tiles by
+ * `tail_splits` workgroups (a way to spread a few leftover tiles over the whole GPU when NT is
+ * not a multiple of the compute-unit count).  Tiles shared by several workgroups are summed
+ * over a fixed binary tree of the splits in the handle's workspace, so every plan gives the
+ * same y for the same inputs run after run (different plans may differ in the last bits: the
+ * summation order differs). */
 typedef struct {
     int route;       /* QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA, or QMAT_ROUTE_GEMM (then only splits is
                         read: the k splits of every 64-token x 256-row tile, 1..16) */
@@ -203,12 +222,21 @@ int qmat_run_plan(qmat_t handle, const void *x_dev, float *y_dev, int T, const q
  * small-T routes, outside [1, 4194240] on the GEMM route). */
 int qmat_get_plan(qmat_t handle, int T, int route, qmat_plan *plan);
 
-/* Expand the packed matrix to fp32 w [M][K] (device), bit-exact: groupwise
- * fp32(scale) * code, FP8 fl32(r * e4m3).  For checking; not a fast path. */
+/* Expand the packed matrix to fp32 w [M][K] (device), bit-exact: groupwise fp32(scale) * code
+ * ("Qwen3.8-27B for NInfer on the RTX 3090", "What is different from the upstream artifact"),
+ * FP8 fl32(r * e4m3) ("Qwen3.8-27B NVFP4 for NInfer", "Artifact").  Asynchronous on stream, no
+ * allocation.  w must be 16-byte aligned and hold M * K floats.  For checking; not a fast path.
+ * Errors: QMAT_EINVAL (null handle or w, misaligned w, another device current), QMAT_EHIP. */
 int qmat_dequant(qmat_t handle, float *w_dev, void *stream);
 
-/* Bytes of device workspace the handle holds (0 if none). */
-size_t qmat_workspace_bytes(qmat_t handle);
+/* Device workspace of a handle, in bytes.
+ *   T >= 1: what qmat_run with T tokens uses of it under the automatic plan: the tree words
+ *           that sum a row tile's partial results when K is split across workgroups (small T),
+ *           or the GEMM route's split-K partial sums (T > 16); 0 when that plan splits nothing.
+ *   T == 0: everything the handle holds (allocated by qmat_create / qmat_create_view for every
+ *           T and every launch shape qmat_run_ex / qmat_run_plan accept).
+ * Returns 0 for a NULL handle or T outside [0, 4194240].  Host only; no device calls. */
+size_t qmat_workspace_bytes(qmat_t handle, int T);
 
 /* Release the handle and its workspace (not the packed matrix).  NULL is ignored. */
 void qmat_destroy(qmat_t handle);

@@ -136,7 +136,8 @@ def test_run_and_dequant_reject_null_handle():
     assert L.qmat_run(None, 16, 16, 1, None) == wq.QMAT_EINVAL
     assert L.qmat_run_ex(None, 16, 16, 1, 0, 0, 0, 0, None) == wq.QMAT_EINVAL
     assert L.qmat_dequant(None, 16, None) == wq.QMAT_EINVAL
-    assert L.qmat_workspace_bytes(None) == 0
+    assert L.qmat_workspace_bytes(None, 0) == 0
+    assert L.qmat_workspace_bytes(None, 1) == 0
     L.qmat_destroy(None)
 
 

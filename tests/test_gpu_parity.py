@@ -4,7 +4,7 @@
   - qmat_run must satisfy |y - y_ref| <= 1e-4 * sum_j |w_ij x_tj| + 1e-6 everywhere, and match
     bit for bit on inputs where every partial sum is exact in fp32.
 Small shapes span several 64-row tiles with a ragged last tile and odd group counts; the full
-benchmark shapes are checked on sampled rows in the launch configuration the benchmark uses.
+benchmark shapes are checked on every row in the launch configuration the benchmark uses.
 """
 import os
 import sys
@@ -551,6 +551,58 @@ def test_zero_and_sparse_codes(fmt):
         _check_y(y, qi.Workload("s", fmt, M, K, T, codes, wl.scales, wl.x), f"sparse {route}")
 
 
+# FP8 row scales the API accepts (any finite fp32) that the seeded workloads never produce:
+# negative, +0, -0, subnormal, the smallest normal and large magnitudes
+FP8_EDGE_ROW_SCALES = np.array([-0.0123, 0.0, -0.0, 1.0e-40, -3.0e-42, 2.0 ** -126, -1.0e30, 7.5e29,
+                                -1.0, 1.0, 2.0 ** -149, -(2.0 ** -149)], dtype=np.float32)
+
+
+@pytest.mark.parametrize("route", ["valu", "mfma"])
+def test_fp8_edge_row_scales_product(route):
+    M, K = 200, 640
+    for T in (1, 8, 16):
+        wl = _workload(8, M, K, T, 40 + T)
+        scales = wl.scales.copy()
+        scales[: len(FP8_EDGE_ROW_SCALES)] = FP8_EDGE_ROW_SCALES
+        scales[64: 64 + len(FP8_EDGE_ROW_SCALES)] = FP8_EDGE_ROW_SCALES[::-1]
+        scales[-len(FP8_EDGE_ROW_SCALES):] = FP8_EDGE_ROW_SCALES
+        say(f"fp8 edge row scales {route} T={T}")
+        qm = wq.QMat(8, wl.codes, scales)
+        y = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run_ex(qm.handle, _x_dev(wl.x), y, T, route=ROUTES[route])
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        assert np.all(got[:, 1] == 0) and np.all(got[:, 2] == 0)  # zero row scales give zero
+        _check_y(y, qi.Workload("e", 8, M, K, T, wl.codes, scales, wl.x), f"fp8 edge scales {route} T={T}")
+        qm.close()
+
+
+# FP16 group scales: +-0, the smallest subnormal, the largest subnormal, the smallest normal,
+# +-65504 and ordinary negative values, spread over every group position of some rows
+HALF_EDGE_SCALES = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x83FF, 0x0400, 0x8400, 0x7BFF,
+                             0xFBFF, 0xBC00, 0x3C00, 0xA266], dtype=np.uint16)
+
+
+@pytest.mark.parametrize("route", ["valu", "mfma"])
+@pytest.mark.parametrize("fmt", [4, 5, 6, qi.Q8])
+def test_groupwise_edge_scales_product(route, fmt):
+    M, K = 150, 1536
+    G = K // 64
+    for T in (1, 8):
+        wl = _workload(fmt, M, K, T, 60 + fmt + T)
+        scales = wl.scales.copy()
+        n = len(HALF_EDGE_SCALES)
+        for i in range(0, M, 3):
+            scales[i] = HALF_EDGE_SCALES[(np.arange(G) + i) % n]
+        say(f"groupwise edge scales {route} fmt={fmt} T={T}")
+        qm = wq.QMat(fmt, wl.codes, scales)
+        y = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run_ex(qm.handle, _x_dev(wl.x), y, T, route=ROUTES[route])
+        torch.cuda.synchronize()
+        _check_y(y, qi.Workload("e", fmt, M, K, T, wl.codes, scales, wl.x), f"edge scales {route} fmt={fmt} T={T}")
+        qm.close()
+
+
 @pytest.mark.parametrize("fmt,T", [(4, 16), (8, 1), (qi.Q8, 5), (6, 3)])
 def test_largest_k(fmt, T):
     # K at the largest size the library accepts (2^20: 8192 k units per tile) with a ragged row
@@ -719,15 +771,14 @@ def test_full_size_prefill_sampled_rows(name, T):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", list(qi.CONFIGS))
-def test_full_size_sampled_rows(name):
-    """Each benchmark shape at every listed T, automatic launch plan (the one the benchmark
-    times): the product on ~1600 sampled rows (first and last tile included) and the
-    dequantization on ~300 sampled rows against the oracle."""
+def test_full_size_every_row(name):
+    """Each benchmark shape at every listed T on the automatic launch plan (the one the benchmark
+    times): every output element of the product against the oracle (fp64 over all rows), and
+    the dequantization on ~300 sampled rows bit for bit."""
     _, _, _, Ts, _ = qi.CONFIGS[name]
     say(f"full {name}: generating")
     wl = qi.config(name)
     qm = wq.QMat(wl.fmt, wl.codes, wl.scales)
-    rows = _sample_rows(wl.M)
     for T in Ts:
         say(f"full {name} T={T}")
         xd = _x_dev(wl.x[:T])
@@ -736,8 +787,9 @@ def test_full_size_sampled_rows(name):
         torch.cuda.synchronize()
         assert not torch.isnan(y).any()
         sub = qi.Workload(wl.name, wl.fmt, wl.M, wl.K, T, wl.codes, wl.scales, wl.x[:T])
-        worst = _check_y(y, sub, f"{name} T={T}", rows=rows)
-        say(f"  worst ratio {worst:.3g}")
+        worst = _check_y(y, sub, f"{name} T={T}")
+        say(f"  worst ratio {worst:.3g} over all {wl.M} rows")
+        del y
     say(f"full {name}: dequant")
     drows = _sample_rows(wl.M, n=200, seed=1)
     w = qm.dequant()

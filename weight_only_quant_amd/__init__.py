@@ -37,7 +37,7 @@ SIGNATURES = {
     "qmat_dequant": (_int, [_vp, _vp, _vp]),
     "qmat_run_plan": (_int, [_vp, _vp, _vp, _int, _vp, _vp]),
     "qmat_get_plan": (_int, [_vp, _int, _int, _vp]),
-    "qmat_workspace_bytes": (_sz, [_vp]),
+    "qmat_workspace_bytes": (_sz, [_vp, _int]),
     "qmat_destroy": (None, [_vp]),
     "qmat_last_error": (ctypes.c_char_p, []),
     "qmat_logits_create": (_int, [ctypes.POINTER(_vp), _i64, _int, _int]),
@@ -186,8 +186,9 @@ def qmat_run_plan(handle: int, x, y, plan: qmat_plan, T: Optional[int] = None, s
     _check(lib().qmat_run_plan(handle, x.data_ptr(), y.data_ptr(), T, ctypes.byref(plan), _stream_handle(stream)))
 
 
-def qmat_workspace_bytes(handle: int) -> int:
-    return int(lib().qmat_workspace_bytes(handle))
+def qmat_workspace_bytes(handle: int, T: int = 0) -> int:
+    """Device workspace bytes the automatic plan uses at T tokens (T = 0: all the handle holds)."""
+    return int(lib().qmat_workspace_bytes(handle, T))
 
 
 def qmat_destroy(handle: Optional[int]) -> None:

@@ -474,10 +474,18 @@ int qmat_dequant(qmat_t h, float *w_dev, void *stream)
     return ok();
 }
 
-size_t qmat_workspace_bytes(qmat_t h)
+size_t qmat_workspace_bytes(qmat_t h, int T)
 {
-    if (!h) return 0;
-    return h->ws_floats * sizeof(float) + h->node_words * sizeof(uint64_t);
+    if (!h || T < 0 || T > kGemmMaxT) return 0;
+    if (T == 0) return h->ws_floats * sizeof(float) + h->node_words * sizeof(uint64_t);
+    if (T > kMaxT) {  // the GEMM route with its automatic k splits
+        const int S = gemm_auto_splits(h->NT, h->NU, T, h->cus, h->ws_floats);
+        return S > 1 ? gemm_workspace_floats(T, (int)h->NT, S) * sizeof(float) : 0;
+    }
+    const int r = auto_route(h->fmt, T);
+    const Plan &p = h->plan[r - 1][T];
+    return run_node_words(launch_tokens(r, T), (int)h->NT, p.splits, p.tail_tiles, p.tail_tiles > 0 ? p.tail_splits : 1) *
+           sizeof(uint64_t);
 }
 
 void qmat_destroy(qmat_t h)
