@@ -175,6 +175,24 @@ int qmat_create_view(qmat_t *view, qmat_t parent, int64_t row0, int64_t rows);
  * QMAT_EHIP (launch failure). */
 int qmat_run(qmat_t handle, const void *x_dev, float *y_dev, int T, void *stream);
 
+/* qmat_run for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same product, the same automatic
+ * plan and the same kernels as qmat_create + qmat_run, without a handle and without any
+ * allocation.  The library plans the launch on the host and keeps what the kernels need beyond
+ * x, y and the packed matrix in one static device array per GPU (32 MiB, held by each GPU the
+ * library runs on until the process ends): 8 MiB of tree words that sum a row tile's partial
+ * results when K is split across workgroups (zero from the moment the code loads, and left
+ * zero by every call), and 24 MiB for the GEMM route's split-K partial sums (T > 16; its
+ * automatic splits are limited to what fits).  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (different streams without synchronization, or several host
+ * threads at once) race and give wrong results; calls ordered on one stream are safe.
+ *   fmt, M, K, packed_dev, bytes: as for qmat_create (the packed matrix is only read);
+ *   x_dev, y_dev, T, stream: as for qmat_run.
+ * Errors: as qmat_create and qmat_run, plus QMAT_ESIZE when the launch plan would need more
+ * scratch than the array holds, QMAT_EINVAL on a device index of 64 or more. */
+int qmat_run_static(int fmt, int64_t M, int64_t K, const void *packed_dev, size_t bytes,
+                    const void *x_dev, float *y_dev, int T, void *stream);
+
 /* A launch shape of the product kernel.  The matrix is cut into NT = ceil(M/64) row tiles;
  * a workgroup of `waves` waves works on one tile (or on two neighbouring tiles, see `tiles`)
  * and splits the tile's 128-wide k units among its waves.  The leading NT - tail_tiles tiles

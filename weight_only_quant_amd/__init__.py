@@ -33,6 +33,7 @@ SIGNATURES = {
     "qmat_create": (_int, [ctypes.POINTER(_vp), _int, _i64, _i64, _vp, _sz]),
     "qmat_create_view": (_int, [ctypes.POINTER(_vp), _vp, _i64, _i64]),
     "qmat_run": (_int, [_vp, _vp, _vp, _int, _vp]),
+    "qmat_run_static": (_int, [_int, _i64, _i64, _vp, _sz, _vp, _vp, _int, _vp]),
     "qmat_run_ex": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]),
     "qmat_dequant": (_int, [_vp, _vp, _vp]),
     "qmat_run_plan": (_int, [_vp, _vp, _vp, _int, _vp, _vp]),
@@ -150,6 +151,14 @@ def qmat_run(handle: int, x, y, T: Optional[int] = None, stream=None) -> None:
     """x: bf16 device [T,K]; y: fp32 device [T,M]."""
     T = x.shape[0] if T is None else T
     _check(lib().qmat_run(handle, x.data_ptr(), y.data_ptr(), T, _stream_handle(stream)))
+
+
+def qmat_run_static(fmt: int, M: int, K: int, packed_dev, x, y, T: Optional[int] = None, stream=None) -> None:
+    """qmat_run without a handle or any allocation: packed_dev is a torch uint8 device tensor
+    holding qmat_pack's output; x bf16 device [T,K]; y fp32 device [T,M]."""
+    T = x.shape[0] if T is None else T
+    _check(lib().qmat_run_static(fmt, M, K, packed_dev.data_ptr(), packed_dev.numel(), x.data_ptr(), y.data_ptr(), T,
+                                 _stream_handle(stream)))
 
 
 def qmat_run_ex(handle: int, x, y, T: Optional[int] = None, route: int = QMAT_ROUTE_AUTO,

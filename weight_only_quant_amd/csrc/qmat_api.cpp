@@ -3,6 +3,7 @@
 // host helpers are in qmat_pack.cpp and qmat_host.cpp (no HIP there).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/qmat.h"
@@ -486,6 +487,102 @@ size_t qmat_workspace_bytes(qmat_t h, int T)
     const Plan &p = h->plan[r - 1][T];
     return run_node_words(launch_tokens(r, T), (int)h->NT, p.splits, p.tail_tiles, p.tail_tiles > 0 ? p.tail_splits : 1) *
            sizeof(uint64_t);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free entry point
+
+namespace {
+
+// The scratch of qmat_run_static: one array per GPU (each device holds its own copy, at its own
+// address, until the process ends), shared by every such call on that GPU.
+//   words [0, kStaticNodeWords): the tree words that sum shared row tiles (small T).  Static
+//       storage starts zeroed when the code object is loaded, and every call leaves the words
+//       it used zero again.
+//   words [kStaticNodeWords, kStaticWords): the GEMM route's split-K partial sums (fp32 scratch).
+constexpr size_t kStaticNodeWords = (size_t)1 << 20;   // 8 MiB: every automatic small-T plan on
+                                                       // a 256-CU GPU needs at most 512 Ki words
+constexpr size_t kStaticGemmFloats = (size_t)6 << 20;  // 24 MiB
+constexpr size_t kStaticWords = kStaticNodeWords + kStaticGemmFloats / 2;
+static __device__ __align__(256) uint64_t scratch[kStaticWords];
+
+constexpr int kStaticMaxDevices = 64;
+std::mutex g_static_mu;
+uint64_t *g_static_ptr[kStaticMaxDevices];  // device address of scratch on each device
+int g_static_cus[kStaticMaxDevices];
+
+// The device address of the current device's scratch and its compute-unit count, looked up once
+// per device.  The array's name is only a host-side stand-in: kernels get this address.
+int static_scratch(int dev, uint64_t **ptr, int *cus)
+{
+    if (dev < 0 || dev >= kStaticMaxDevices)
+        return fail(QMAT_EINVAL, "qmat_run_static: device %d beyond the %d devices supported", dev, kStaticMaxDevices);
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (!g_static_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(QMAT_EHIP, "qmat_run_static: cannot locate the scratch array on device %d", dev);
+        }
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            return fail(QMAT_EHIP, "qmat_run_static: cannot read the compute unit count of device %d", dev);
+        g_static_cus[dev] = n;
+        g_static_ptr[dev] = static_cast<uint64_t *>(p);
+    }
+    *ptr = g_static_ptr[dev];
+    *cus = g_static_cus[dev];
+    return QMAT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmat_run_static(int fmt, int64_t M, int64_t K, const void *packed_dev, size_t bytes, const void *x_dev,
+                    float *y_dev, int T, void *stream)
+{
+    if (!format_ok(fmt)) return fail(QMAT_EINVAL, "qmat_run_static: unknown format %d", fmt);
+    if (!shape_ok(M, K))
+        return fail(QMAT_ESHAPE, "qmat_run_static: bad shape M=%lld K=%lld", (long long)M, (long long)K);
+    if (T < 0 || T > kGemmMaxT) return fail(QMAT_ESHAPE, "qmat_run_static: T=%d outside [0,%d]", T, kGemmMaxT);
+    if (!packed_dev) return fail(QMAT_EINVAL, "qmat_run_static: null packed pointer");
+    if (reinterpret_cast<uintptr_t>(packed_dev) % 16)
+        return fail(QMAT_EINVAL, "qmat_run_static: packed pointer not 16-byte aligned");
+    const size_t need = qmat_packed_bytes(fmt, M, K);
+    if (bytes != need) return fail(QMAT_ESIZE, "qmat_run_static: bytes %zu != packed size %zu", bytes, need);
+    if (T == 0) return ok();
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(QMAT_EHIP, "qmat_run_static: hipGetDevice failed");
+    uint64_t *scr = nullptr;
+    int cus = 0;
+    if (const int st = static_scratch(dev, &scr, &cus)) return st;
+    // a handle on the stack over the caller's packed matrix and the scratch: nothing allocated
+    qmat h;
+    h.fmt = fmt;
+    h.M = M;
+    h.K = K;
+    h.NT = num_tiles(M);
+    h.NU = num_units(K);
+    h.Mpad = h.NT * kTileRows;
+    h.codes = static_cast<const uint8_t *>(packed_dev);
+    h.scales = h.codes + code_bytes(fmt, M, K);
+    h.nodes = scr;
+    h.node_words = kStaticNodeWords;
+    h.ws = reinterpret_cast<float *>(scr + kStaticNodeWords);
+    h.ws_floats = kStaticGemmFloats;
+    h.device = dev;
+    h.cus = cus;
+    if (T > kMaxT) return run_gemm(&h, x_dev, y_dev, T, 0, stream);
+    const int r = auto_route(fmt, T);
+    const int Tl = launch_tokens(r, T);
+    const Plan p = make_plan(fmt, r, Tl, h.NT, h.NU, cus);
+    const size_t words = run_node_words(Tl, (int)h.NT, p.splits, p.tail_tiles, p.tail_tiles > 0 ? p.tail_splits : 1);
+    if (words > kStaticNodeWords)
+        return fail(QMAT_ESIZE, "qmat_run_static: the plan for M=%lld at T=%d needs %zu scratch words, above the %zu "
+                    "the library reserves", (long long)M, T, words, kStaticNodeWords);
+    return run_plan(&h, x_dev, y_dev, T, p, stream);
 }
 
 void qmat_destroy(qmat_t h)
