@@ -188,9 +188,11 @@ def measure_decode(lines, steps):
     return {i: line(lines[i][0], lines[i][1], times[i], rounds[i]) for i in range(len(lines))}
 
 
-def measure_epilogue(res, T, k, warm_s=WARM_S, n=MIN_CALLS):
+def measure_epilogue(res, T, k, warm_s=WARM_S, n=MIN_CALLS, with_product=False):
     """The output-head epilogue (per-token log-sum-exp and top-k) on the logits the head product
-    left in res.y, graph-replayed after a time-based warm-up; bytes are the logits read."""
+    left in res.y, graph-replayed after a time-based warm-up; bytes are the logits read.  With
+    with_product, the head product and the epilogue in one call (qmat_run_logits, logits kept in
+    the epilogue's own buffer); bytes are then the packed matrix and the logits written and read."""
     import torch
     import weight_only_quant_amd as wq
     M = res.wl.M
@@ -199,12 +201,20 @@ def measure_epilogue(res, T, k, warm_s=WARM_S, n=MIN_CALLS):
     lse = torch.empty(T, device="cuda")
     v = torch.empty((T, k), device="cuda")
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
+
+    def call(i):
+        if with_product:
+            h = res.handles[i % len(res.handles)]
+            wq.qmat_run_logits(h, e, res.x[:T], k, lse=lse, top_vals=v, top_ids=ids)
+        else:
+            wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
+
+    call(0)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(n):
-            wq.qmat_logits_run(e, y, k, lse=lse, top_vals=v, top_ids=ids)
+        for i in range(n):
+            call(i)
     t0 = time.time()
     while time.time() - t0 < warm_s:
         g.replay()
@@ -219,7 +229,7 @@ def measure_epilogue(res, T, k, warm_s=WARM_S, n=MIN_CALLS):
         us.append(a.elapsed_time(b) / n * 1e3)
     del g
     wq.qmat_logits_destroy(e)
-    nb = T * M * 4
+    nb = T * M * 4 + (res.copies[0].numel() + T * res.wl.K * 2 + T * M * 4 if with_product else 0)
     u = float(np.median(us))
     return {"us_per_call": round(u, 3), "GBps": round(nb / u / 1e3, 1), "bytes": nb, "k": k}
 
@@ -464,6 +474,10 @@ def main():
             wq.qmat_run(r.handles[0], r.x[:T2], r.y[:T2], T=T2)
             key = f"head_epilogue_lse_top20_248320_T{T2}"
             extra[key] = measure_epilogue(r, T2, 20)
+            log(f"[bench] {key}: {extra[key]}")
+        for T2 in qi.CONFIGS[r.name][3]:
+            key = f"head_product_and_epilogue_lse_top20_248320x5120_T{T2}"
+            extra[key] = measure_epilogue(r, T2, 20, with_product=True)
             log(f"[bench] {key}: {extra[key]}")
 
     # prefill-sized token counts (the GEMM route)

@@ -273,8 +273,10 @@ void qmat_destroy(qmat_t handle);
 typedef struct qmat_logits *qmat_logits_t;
 
 /* An epilogue handle for M rows, up to max_T tokens (1..16) and top-k up to max_k (0..64).  It
- * owns a small device workspace (per token and block: two floats and max_k (value, row) pairs),
- * allocated and zeroed here; calls sharing a handle must be ordered.
+ * owns a device workspace, allocated here: per token and row block (up to 512 blocks of about
+ * 4096 rows) a (max, sum) state and max_k (value, row) pairs, and max_T * M floats of logits for
+ * qmat_run_logits called without y.  Nothing in it needs resetting between calls; calls sharing
+ * a handle must be ordered.
  * Errors: QMAT_EINVAL (null pointer), QMAT_ESHAPE (M outside [1, 2^30], max_T, max_k),
  * QMAT_ENOMEM, QMAT_EHIP. */
 int qmat_logits_create(qmat_logits_t *handle, int64_t M, int max_T, int max_k);
@@ -290,6 +292,20 @@ int qmat_logits_create(qmat_logits_t *handle, int64_t M, int max_T, int max_k);
  * QMAT_EHIP (launch). */
 int qmat_logits_run(qmat_logits_t handle, const float *y_dev, int64_t ldy, int T, int k,
                     const int32_t *index_dev, float *lse_dev, float *top_vals_dev,
+                    int32_t *top_ids_dev, void *stream);
+
+/* The product and the epilogue in one call, on one stream: y = x . W^T exactly as qmat_run
+ * computes it, then per token the log-sum-exp and the top k of y exactly as qmat_logits_run
+ * computes them.  With y NULL the logits go to the handle's own buffer and are not returned.
+ *   handle:  the product matrix; epilogue: created for the same M (max_T, max_k as needed).
+ *   x_dev, T, stream: as for qmat_run (T <= the epilogue's max_T);  y_dev: as for qmat_run, or
+ *   NULL;  k, index_dev, lse_dev, top_vals_dev, top_ids_dev: as for qmat_logits_run.
+ * Asynchronous, no allocation, graph-capturable.  Calls sharing an epilogue handle must be
+ * ordered.
+ * Errors: QMAT_EINVAL (null handle, x or top-k outputs), QMAT_ESHAPE (M differs, T, k), and
+ * those of qmat_run. */
+int qmat_run_logits(qmat_t handle, qmat_logits_t epilogue, const void *x_dev, float *y_dev, int T,
+                    int k, const int32_t *index_dev, float *lse_dev, float *top_vals_dev,
                     int32_t *top_ids_dev, void *stream);
 
 /* Release the handle and its workspace.  NULL is ignored. */

@@ -178,3 +178,172 @@ def test_epilogue_argument_errors():
         with pytest.raises(wq.QmatError) as err:
             wq.qmat_logits_create(*args)
         assert err.value.status == wq.QMAT_ESHAPE, args
+
+
+# ------------------------------------------------------------------ product and epilogue in one call
+
+def _head(fmt, M, K, T, seed, exact=False):
+    if exact:
+        # every product and partial sum exact in fp32 (small integer activations, power-of-two
+        # scales, integer-valued E4M3 bytes): the logits equal the oracle's float64 ones, with
+        # many equal values among the largest
+        rng = np.random.default_rng(seed)
+        x = torch.from_numpy(rng.integers(-4, 5, (T, K)).astype(np.float32)).to(torch.bfloat16)
+        x_bits = x.view(torch.int16).numpy().view(np.uint16)
+        if fmt == 8:
+            ints = rng.integers(-16, 17, (M, K)).astype(np.float32)
+            codes = torch.from_numpy(ints).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            scales = (2.0 ** rng.integers(-6, 3, M)).astype(np.float32)
+        else:
+            b = qi.code_bits(fmt)
+            codes = rng.integers(-(1 << (b - 1)), 1 << (b - 1), (M, K)).astype(np.int8)
+            sg = np.where(rng.random((M, K // 64)) < 0.5, -1.0, 1.0)
+            scales = (sg * 2.0 ** rng.integers(-2, 2, (M, K // 64))).astype(np.float16).view(np.uint16)
+        return qi.Workload("exact", fmt, M, K, T, codes, scales, x_bits)
+    if fmt == 8:
+        return qi.fp8_rows("h", M, K, T, 0.01, seed)
+    return qi.groupwise("h", fmt, M, K, T, 0.005, seed)
+
+
+def _both(qm, e, xd, T, k, index=None, with_y=True):
+    y = torch.full((T, qm.M), float("nan"), device="cuda") if with_y else None
+    lse = torch.full((T,), float("nan"), device="cuda")
+    vals = torch.full((T, max(k, 1)), float("nan"), device="cuda")
+    ids = torch.full((T, max(k, 1)), -7, dtype=torch.int32, device="cuda")
+    wq.qmat_run_logits(qm.handle, e, xd[:T], k, y=y, lse=lse, top_vals=vals, top_ids=ids, index=index, T=T)
+    torch.cuda.synchronize()
+    return y, lse.cpu().numpy(), vals.cpu().numpy()[:, :k], ids.cpu().numpy()[:, :k]
+
+
+# head-shaped matrices (many row tiles, no split of K), ragged last tiles included
+HEAD_SHAPES = [(6, 131072 + 37, 640), (8, 131072, 512), (qi.Q8, 140000, 384), (4, 2049 * 64 - 63, 256)]
+
+
+@pytest.mark.parametrize("fmt,M,K", HEAD_SHAPES)
+def test_run_logits_matches_product_then_pass(fmt, M, K):
+    """qmat_run_logits on a head-shaped matrix: y bit for bit qmat_run's; top-k identical to the
+    separate epilogue call on that y and to the oracle's sort of it; lse within the fp32
+    evaluation bound of the oracle's float64 log-sum-exp of that y; the same outputs without y."""
+    wl = _head(fmt, M, K, 16, 30 + fmt)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    xd = torch.from_numpy(wl.x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    e = wq.qmat_logits_create(M, 16, 64)
+    rng = np.random.default_rng(M)
+    index = rng.permutation(2 * M)[:M].astype(np.int32) if fmt == qi.Q8 else None
+    idx = None if index is None else torch.from_numpy(index).cuda()
+    for T, k in [(1, 20), (2, 1), (3, 0), (8, 20), (10, 64), (16, 7)]:
+        say(f"run_logits fmt={fmt} M={M} T={T} k={k}")
+        y, lse, vals, ids = _both(qm, e, xd, T, k, idx)
+        y_run = qm.run(xd[:T])
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_run.view(torch.int32))
+        yg = y.cpu().numpy()
+        ref = oracle.logsumexp(yg)
+        assert np.all(np.abs(lse.astype(np.float64) - ref) <= _lse_tol(ref)), (lse, ref)
+        if k:
+            rv, ri = oracle.topk(yg, k, None if index is None else index.astype(np.int64))
+            assert np.array_equal(vals.astype(np.float64), rv), (vals, rv)
+            assert np.array_equal(ids.astype(np.int64), ri), (ids, ri)
+            lse2, vals2, ids2 = _run(e, yg, k, index=index)
+            assert np.array_equal(vals, vals2) and np.array_equal(ids, ids2)
+        _, lse3, vals3, ids3 = _both(qm, e, xd, T, k, idx, with_y=False)
+        assert np.array_equal(lse3.view(np.int32), lse.view(np.int32))
+        assert np.array_equal(vals3, vals) and np.array_equal(ids3, ids)
+    wq.qmat_logits_destroy(e)
+    qm.close()
+
+
+@pytest.mark.parametrize("fmt", [6, 8])
+def test_run_logits_bit_exact_on_exact_inputs(fmt):
+    """Exact-arithmetic inputs (logits with many equal values, also across row blocks): the
+    top-k equals the oracle's sort of its float64 logits, ties ordered by row."""
+    M, K = 131072 + 64 * 3, 256
+    for T, k in [(1, 64), (8, 20), (16, 5)]:
+        wl = _head(fmt, M, K, T, 50 + T, exact=True)
+        qm = wq.QMat(fmt, wl.codes, wl.scales)
+        xd = torch.from_numpy(wl.x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+        e = wq.qmat_logits_create(M, T, k)
+        say(f"run_logits exact fmt={fmt} T={T} k={k}")
+        _, lse, vals, ids = _both(qm, e, xd, T, k, with_y=False)
+        y_ref, _ = oracle.gemv(fmt, wl.codes, wl.scales, wl.x)
+        rv, ri = oracle.topk(y_ref, k)
+        assert np.array_equal(vals.astype(np.float64), rv) and np.array_equal(ids.astype(np.int64), ri)
+        ref = oracle.logsumexp(y_ref)
+        assert np.all(np.abs(lse.astype(np.float64) - ref) <= _lse_tol(ref))
+        wq.qmat_logits_destroy(e)
+        qm.close()
+
+
+def test_run_logits_end_to_end_and_graph_replay():
+    """The Q6 head shape at T = 8: the outputs against the oracle's float64 logits (as in the
+    separate-pass end-to-end test), repeated calls identical, and graph replays of the product
+    and both epilogue kernels identical to the eager result."""
+    import gc
+    gc.collect()
+    M, K, T, k = 248320, 512, 8, 20
+    wl = qi.groupwise("h", 6, M, K, T, 0.005, 77)
+    qm = wq.QMat(6, wl.codes, wl.scales)
+    xd = torch.from_numpy(wl.x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    e = wq.qmat_logits_create(M, T, k)
+    y, lse, vals, ids = _both(qm, e, xd, T, k)
+    y_ref, A = oracle.gemv(6, wl.codes, wl.scales, wl.x)
+    tol = oracle.REL_TOL * A + oracle.ABS_TOL
+    lse_ref = oracle.logsumexp(y_ref)
+    assert np.all(np.abs(lse.astype(np.float64) - lse_ref) <= tol.max(axis=1) + _lse_tol(lse_ref))
+    yg = y.cpu().numpy()
+    for t in range(T):
+        assert len(set(ids[t].tolist())) == k
+        assert np.array_equal(vals[t], yg[t, ids[t]])
+        assert np.all(np.abs(vals[t] - y_ref[t, ids[t]]) <= tol[t, ids[t]])
+        rest = np.setdiff1d(np.arange(M), ids[t])
+        assert y_ref[t, rest].max() <= y_ref[t, ids[t]].min() + 2 * tol[t].max()
+    for i in range(2):
+        _, lse2, vals2, ids2 = _both(qm, e, xd, T, k, with_y=False)
+        assert np.array_equal(lse2.view(np.int32), lse.view(np.int32)) and np.array_equal(vals2, vals)
+        assert np.array_equal(ids2, ids)
+    lse_d = torch.empty(T, device="cuda")
+    v_d = torch.empty((T, k), device="cuda")
+    i_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wq.qmat_run_logits(qm.handle, e, xd, k, lse=lse_d, top_vals=v_d, top_ids=i_d)
+    for i in range(4):
+        lse_d.fill_(float("nan"))
+        i_d.fill_(-5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(lse_d.cpu().numpy().view(np.int32), lse.view(np.int32)), i
+        assert np.array_equal(v_d.cpu().numpy(), vals) and np.array_equal(i_d.cpu().numpy(), ids), i
+        _both(qm, e, xd, T, k, with_y=False)  # eager work between replays
+    del g
+    wq.qmat_logits_destroy(e)
+    qm.close()
+
+
+def test_run_logits_on_a_split_plan_and_errors():
+    """A matrix whose plan splits K (the exchange-tree reduction runs first), with or without y;
+    and the argument checks."""
+    M, K, T, k = 5000, 4352, 4, 16
+    wl = qi.groupwise("s", 5, M, K, T, 0.01, 88)
+    qm = wq.QMat(5, wl.codes, wl.scales)
+    assert wq.qmat_get_plan(qm.handle, T).splits > 1
+    xd = torch.from_numpy(wl.x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    e = wq.qmat_logits_create(M, T, k)
+    y, lse, vals, ids = _both(qm, e, xd, T, k)
+    yg = y.cpu().numpy()
+    rv, ri = oracle.topk(yg, k)
+    assert np.array_equal(vals.astype(np.float64), rv) and np.array_equal(ids.astype(np.int64), ri)
+    _, lse2, vals2, ids2 = _both(qm, e, xd, T, k, with_y=False)
+    assert np.array_equal(vals2, vals) and np.array_equal(ids2, ids)
+    L = wq.lib()
+    e2 = wq.qmat_logits_create(M + 1, T, k)
+    assert L.qmat_run_logits(qm.handle, e2, xd.data_ptr(), None, T, k, None, None, vals2.ctypes.data, None,
+                             None) == wq.QMAT_ESHAPE
+    assert L.qmat_run_logits(qm.handle, e, xd.data_ptr(), None, T, k + 1, None, None, None, None,
+                             None) == wq.QMAT_ESHAPE
+    assert L.qmat_run_logits(qm.handle, e, xd.data_ptr(), None, T, k, None, None, None, None, None) == wq.QMAT_EINVAL
+    assert L.qmat_run_logits(None, e, xd.data_ptr(), None, T, k, None, None, None, None, None) == wq.QMAT_EINVAL
+    assert L.qmat_run_logits(qm.handle, e, xd.data_ptr(), None, 0, k, None, None, None, None, None) == wq.QMAT_OK
+    wq.qmat_logits_destroy(e2)
+    wq.qmat_logits_destroy(e)
+    qm.close()

@@ -44,6 +44,7 @@ SIGNATURES = {
     "qmat_logits_create": (_int, [ctypes.POINTER(_vp), _i64, _int, _int]),
     "qmat_logits_run": (_int, [_vp, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp]),
     "qmat_logits_destroy": (None, [_vp]),
+    "qmat_run_logits": (_int, [_vp, _vp, _vp, _vp, _int, _int, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -219,6 +220,17 @@ def qmat_logits_run(handle: int, y, k: int, lse=None, top_vals=None, top_ids=Non
     T = y.shape[0] if T is None else T
     ptr = lambda a: None if a is None else a.data_ptr()
     _check(lib().qmat_logits_run(handle, y.data_ptr(), y.stride(0), T, k, ptr(index), ptr(lse), ptr(top_vals),
+                                 ptr(top_ids), _stream_handle(stream)))
+
+
+def qmat_run_logits(handle: int, epilogue: int, x, k: int, y=None, lse=None, top_vals=None, top_ids=None,
+                    index=None, T: Optional[int] = None, stream=None) -> None:
+    """Product, then epilogue, in one call: x bf16
+    device [T, K]; y fp32 device [T, M] or None; lse fp32 [T]; top_vals fp32 [T, k]; top_ids int32
+    [T, k]; index int32 [M] or None."""
+    T = x.shape[0] if T is None else T
+    ptr = lambda a: None if a is None else a.data_ptr()
+    _check(lib().qmat_run_logits(handle, epilogue, x.data_ptr(), ptr(y), T, k, ptr(index), ptr(lse), ptr(top_vals),
                                  ptr(top_ids), _stream_handle(stream)))
 
 

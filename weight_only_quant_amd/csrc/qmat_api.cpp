@@ -365,7 +365,7 @@ int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, vo
     const uint8_t *codes = h->codes;
     const uint8_t *scales = h->scales;
     for (int t0 = 0; t0 < T; t0 += Tl) {
-        RunArgs a;
+        RunArgs a{};
         a.codes = codes;
         a.scales = scales;
         a.x = x + (int64_t)t0 * h->K;
@@ -600,11 +600,12 @@ void qmat_destroy(qmat_t h)
 
 struct qmat_logits {
     int64_t M;
-    int max_T, max_k, B;  // B: blocks per token at T = 1 (the partial buffers' size)
-    int64_t slots;  // epilogue workgroups resident on the whole GPU at once (0: unknown)
-    float *part_f;
-    int32_t *part_i;
-    uint32_t *counter;
+    int max_T, max_k;
+    int B;                // row blocks per token
+    float2 *part_lse;     // [max_T][B] block states
+    uint64_t *part_list;  // [max_T][B][max(max_k, 1)] block lists
+    uint64_t *part_kth;   // [max_T][B] blocks' k-th keys
+    float *ybuf;          // [max_T][M] logits for qmat_run_logits without y
     int device;
 };
 
@@ -622,33 +623,25 @@ int qmat_logits_create(qmat_logits_t *e, int64_t M, int max_T, int max_k)
     h->M = M;
     h->max_T = max_T;
     h->max_k = max_k;
-    h->B = logits_blocks(M);
-    h->part_f = nullptr;
-    h->part_i = nullptr;
-    h->counter = nullptr;
+    h->part_lse = nullptr;
+    h->part_list = nullptr;
+    h->part_kth = nullptr;
+    h->ybuf = nullptr;
     if (hipGetDevice(&h->device) != hipSuccess) {
         delete h;
         return fail(QMAT_EHIP, "qmat_logits_create: hipGetDevice failed");
     }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess) cus = 0;
-    h->slots = (int64_t)cus * logits_blocks_per_cu();
-    const size_t nf = (size_t)max_T * h->B * (2 + max_k), ni = (size_t)max_T * h->B * (max_k > 0 ? max_k : 1);
-    if (hipMalloc(&h->part_f, nf * sizeof(float)) != hipSuccess ||
-        hipMalloc(&h->part_i, ni * sizeof(int32_t)) != hipSuccess ||
-        hipMalloc(&h->counter, (size_t)max_T * sizeof(uint32_t)) != hipSuccess) {
+    h->B = logits_blocks(M);
+    const size_t nt = (size_t)max_T;
+    if (hipMalloc(&h->part_lse, nt * h->B * sizeof(float2)) != hipSuccess ||
+        hipMalloc(&h->part_list, nt * h->B * (max_k > 0 ? max_k : 1) * sizeof(uint64_t)) != hipSuccess ||
+        hipMalloc(&h->part_kth, nt * h->B * sizeof(uint64_t)) != hipSuccess ||
+        hipMalloc(&h->ybuf, nt * M * sizeof(float)) != hipSuccess) {
         (void)hipGetLastError();
-        if (h->part_f) (void)hipFree(h->part_f);
-        if (h->part_i) (void)hipFree(h->part_i);
+        for (void *p : {(void *)h->part_lse, (void *)h->part_list, (void *)h->part_kth, (void *)h->ybuf})
+            if (p) (void)hipFree(p);
         delete h;
         return fail(QMAT_ENOMEM, "qmat_logits_create: workspace allocation failed");
-    }
-    if (hipMemset(h->counter, 0, (size_t)max_T * sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-        (void)hipFree(h->part_f);
-        (void)hipFree(h->part_i);
-        (void)hipFree(h->counter);
-        delete h;
-        return fail(QMAT_EHIP, "qmat_logits_create: counter initialisation failed");
     }
     *e = h;
     return ok();
@@ -676,16 +669,11 @@ int qmat_logits_run(qmat_logits_t e, const float *y_dev, int64_t ldy, int T, int
     a.lse = lse_dev;
     a.vals = top_vals_dev;
     a.ids = top_ids_dev;
-    a.part_f = e->part_f;
-    a.part_i = e->part_i;
-    a.counter = e->counter;
-    // B blocks per token, but no more than one round of resident workgroups over all T tokens:
-    // a second round would wait for the first, so fewer, longer blocks finish sooner (each
-    // streams its rows in several rounds of loads; the partial lists to merge get shorter too)
-    int B = e->B;
-    if (e->slots > 0 && (int64_t)B * T > e->slots) B = (int)(e->slots / T > 1 ? e->slots / T : 1);
-    a.B = B;
-    a.rpb = (int)((e->M + B - 1) / B);
+    a.part_lse = e->part_lse;
+    a.part_list = e->part_list;
+    a.part_kth = e->part_kth;
+    a.B = e->B;
+    a.rpb = (int)((e->M + a.B - 1) / a.B);
     const hipError_t err = launch_logits(a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(QMAT_EHIP, "qmat_logits_run: launch failed: %s", hipGetErrorString(err));
     return ok();
@@ -694,10 +682,28 @@ int qmat_logits_run(qmat_logits_t e, const float *y_dev, int64_t ldy, int T, int
 void qmat_logits_destroy(qmat_logits_t e)
 {
     if (!e) return;
-    (void)hipFree(e->part_f);
-    (void)hipFree(e->part_i);
-    (void)hipFree(e->counter);
+    for (void *p : {(void *)e->part_lse, (void *)e->part_list, (void *)e->part_kth, (void *)e->ybuf})
+        if (p) (void)hipFree(p);
     delete e;
+}
+
+int qmat_run_logits(qmat_t h, qmat_logits_t e, const void *x_dev, float *y_dev, int T, int k, const int32_t *index_dev,
+                    float *lse_dev, float *top_vals_dev, int32_t *top_ids_dev, void *stream)
+{
+    if (!h || !e) return fail(QMAT_EINVAL, "qmat_run_logits: null handle");
+    if (e->M != h->M)
+        return fail(QMAT_ESHAPE, "qmat_run_logits: epilogue handle for M=%lld, matrix has M=%lld", (long long)e->M,
+                    (long long)h->M);
+    if (T < 0 || T > e->max_T) return fail(QMAT_ESHAPE, "qmat_run_logits: T=%d outside [0,%d]", T, e->max_T);
+    if (k < 0 || k > e->max_k) return fail(QMAT_ESHAPE, "qmat_run_logits: k=%d outside [0,%d]", k, e->max_k);
+    if (T == 0) return ok();
+    if (!x_dev) return fail(QMAT_EINVAL, "qmat_run_logits: null x");
+    if (k > 0 && (!top_vals_dev || !top_ids_dev)) return fail(QMAT_EINVAL, "qmat_run_logits: null top-k output");
+    if (const int st = device_ok(e->device, "qmat_run_logits")) return st;
+    float *y = y_dev ? y_dev : e->ybuf;
+    if (const int st = qmat_run(h, x_dev, y, T, stream)) return st;
+    if (k == 0 && !lse_dev) return ok();
+    return qmat_logits_run(e, y, h->M, T, k, index_dev, lse_dev, top_vals_dev, top_ids_dev, stream);
 }
 
 }  // extern "C"

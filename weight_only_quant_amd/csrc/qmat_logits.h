@@ -1,4 +1,4 @@
-// Launch interface of the output-head epilogue kernel (qmat_logits.hip).  Internal: the public
+// Launch interface of the output-head epilogue kernels (qmat_logits.hip).  Internal: the public
 // contract is qmat_logits_* in include/qmat.h.
 #pragma once
 
@@ -6,6 +6,8 @@
 #include <stdint.h>
 
 namespace qmatk {
+
+constexpr int kMaxBlocks = 512;  // row blocks per token at most
 
 struct LogitsArgs {
     const float *y;         // fp32 logits, row t at y + t * ldy, M entries
@@ -15,23 +17,34 @@ struct LogitsArgs {
     float *lse;             // [T] or null
     float *vals;            // [T][k]
     int32_t *ids;           // [T][k]
-    float *part_f;          // per (token, block): max, sum, k best values   [T][B][2 + k]
-    int32_t *part_i;        // per (token, block): rows of the k best        [T][B][k]
-    uint32_t *counter;      // per token arrival counter, zero between launches
-    int B, rpb;             // blocks per token, rows per block
+    float2 *part_lse;       // per (token, block): (max, sum of exp(y - max))   [T][B]
+    uint64_t *part_list;    // per (token, block): the k best keys, best first  [T][B][k]
+    uint64_t *part_kth;     // per (token, block): the k-th best key (0: none)  [T][B]
+    int B, rpb;             // blocks per token (<= kMaxBlocks), rows per block (B * rpb >= M)
 };
 
-// Blocks per token for M rows (each block of 16 waves streams about 4096 rows: one round of
-// four 64-row loads per wave).
+// Blocks per token for M rows: one round of 8 rows per lane of a 256-thread block (2048 rows) per
+// block, at most kMaxBlocks.  A block costs about the same with fewer rows (a round takes 8
+// slots per lane), and every block adds a list to the merge, so no more blocks than the rows
+// fill, whatever T is.
 inline int logits_blocks(int64_t M)
 {
-    int64_t b = (M + 4095) / 4096;
-    return (int)(b < 1 ? 1 : b > 512 ? 512 : b);
+    const int64_t b = (M + 2047) / 2048;
+    return (int)(b < 1 ? 1 : b > kMaxBlocks ? kMaxBlocks : b);
 }
 
-// Workgroups of the epilogue kernel one compute unit holds at once (0 if unknown).
-int logits_blocks_per_cu();
-
+// Both kernels of the epilogue: the blocks' partials, then their merge, one block per token.
 hipError_t launch_logits(const LogitsArgs &a, hipStream_t stream);
+
+struct MergeArgs {
+    const float2 *lse_part;  // [T][G]
+    const uint64_t *kth;     // [T][G]
+    const uint64_t *list;    // [T][G][k]
+    int G, k;
+    const int32_t *index;    // row -> id map [M], or null
+    float *lse;              // [T] or null
+    float *vals;             // [T][k]
+    int32_t *ids;            // [T][k]
+};
 
 }  // namespace qmatk

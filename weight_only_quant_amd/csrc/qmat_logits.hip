@@ -1,5 +1,5 @@
-// gfx950 kernel for the output-head epilogue: per token, the log-sum-exp of the fp32 logits and
-// their k largest values with row ids, in one pass over y.
+// gfx950 kernels for the output-head epilogue: per token, the log-sum-exp of the fp32 logits and
+// their k largest values with row ids.
 //
 // The pages describe both steps next to the head product: the fork merges a "single-pass
 // logsumexp" (giveen/ninfer-ext README, upstream pull requests merged ahead of upstream), and
@@ -8,19 +8,29 @@
 // "Qwen3.8-27B EXL3", the indexed proposal head).  Here the epilogue is format-independent: it
 // reads the logits any qmat product wrote, and maps rows through an optional index.
 //
-// Work split: grid (B, T); block b of token t streams rows [b*rpb, (b+1)*rpb) with 16 waves.
-// Each lane keeps an online (max, sum of exp(y - max)); each wave keeps its 64 best (value, row)
-// pairs sorted across its lanes (lane i holds the i-th best).  Each lane first orders its four
-// rows of a round; the round then enters the list as four 64-pair chunks (every lane's best, then
-// every lane's second, ...), each costing one compare against the current k-th best and a wave
-// vote, and only when some lane beats it a bitonic sort (DPP / swizzle / half-swap lane
-// exchanges) and merge.  Comparisons are branch-free selects.  The block's 16 lists merge in a
-// fixed pairwise tree; the block publishes (max, sum, k best) to the workspace, and the last
-// block of the token to arrive (arrival counter, reset by that block) merges the B partials
-// the same way, with the log-sum-exp states combined in double in a fixed order:
-// deterministic output, no memset between calls.
+// Order: a (value, row) pair is one 64-bit key, the value's bits made unsigned-monotone above
+// the row's complement, so "better" (larger value, equal values by smaller row) is one unsigned
+// compare and every step of a sort is one compare and two selects.  -0 ranks as +0 (it is
+// returned as +0); key 0 is an empty slot and ranks below every pair, -inf included.
 //
-// Order: value descending, equal values by ascending row.  Empty slots are (-inf, INT_MAX).
+// Kernel 1, grid (B, T), 4 waves: block b of token t streams rows [b*rpb, (b+1)*rpb) in rounds
+// of 8 rows per lane, the next round's loads in flight while one round is processed.  Each lane
+// keeps an online (max, sum of exp(y - max)).  For the top k the block keeps its k best keys in
+// wave 0 (sorted across the lanes, lane i the i-th best) and a threshold theta, the k-th of them:
+// a round's keys below theta cannot reach the top k, and usually none or a few are above it, so
+// they are collected in LDS and one sort and merge takes them.  The first round seeds theta
+// with the k-th best of the block's lane maxima (k distinct rows reach it): sorting the lane
+// maxima costs one sort per wave and a merge of the four, and it leaves about k candidates
+// where an empty list would take every key of the round.  Rounds with more than 64 candidates
+// (many equal values, adversarial orders) take them in every wave and merge the waves' lists.
+// The block writes (max, sum), its k best keys and its k-th key.
+//
+// Kernel 2, one block per token: the largest k-th key over the blocks, tau, is reached by k
+// rows, so every key of the token's top k is at or above it, and only keys at or above tau can
+// contribute; every block's list is loaded in one round of loads, the keys at or above tau
+// (usually about k) are collected and sorted once.  The block states combine in double in a
+// fixed order.  The candidate set is exact and the order total, so the output is deterministic:
+// no atomics on global memory, nothing to reset between calls.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -31,25 +41,35 @@ namespace qmatk {
 
 namespace {
 
-constexpr int kRowEmpty = 0x7FFFFFFF;
+// ---------------------------------------------------------------------------- keys
 
-// (v1, r1) ranks before (v2, r2).  Bitwise, not short-circuit, operators: the comparisons
-// stay lane masks and selects instead of becoming divergent branches.
-__device__ __forceinline__ bool better(float v1, int r1, float v2, int r2)
+__device__ __forceinline__ uint64_t make_key(float v, int row)
 {
-    return (v1 > v2) | ((v1 == v2) & (r1 < r2));
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    u = u == 0x80000000u ? 0u : u;
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)row;
 }
 
-// value of lane ^ S, by the cheapest cross-lane route for each distance: DPP within a quad
-// (1, 2) or a row of 16 (8), LDS-unit swizzle within 32 lanes (4, 16), and the gfx950 swap of
-// the wave's halves (32).  None of these goes through the LDS crossbar's address path.
+__device__ __forceinline__ float key_value(uint64_t key)
+{
+    const uint32_t o = (uint32_t)(key >> 32);
+    return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ int key_row(uint64_t key) { return (int)~(uint32_t)key; }
+
+// ---------------------------------------------------------------------------- lane exchanges
+
+// value of lane ^ S: DPP within a quad (1, 2) or a row of 16 (8), the LDS unit's swizzle within
+// 32 lanes (4, 16: no VALU issue slot), and the gfx950 swap of the wave's halves (32)
 template <int S> __device__ __forceinline__ int lane_xor(int v)
 {
-    if constexpr (S == 1) return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
-    else if constexpr (S == 2) return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-    else if constexpr (S == 4) return __builtin_amdgcn_ds_swizzle(v, 0x101F);                  // xor 4 in 32
-    else if constexpr (S == 8) return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false); // row_ror 8
-    else if constexpr (S == 16) return __builtin_amdgcn_ds_swizzle(v, 0x401F);                 // xor 16 in 32
+    if constexpr (S == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);   // quad_perm 1,0,3,2
+    else if constexpr (S == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+    else if constexpr (S == 4) return __builtin_amdgcn_ds_swizzle(v, 0x101F);             // xor 4 in 32
+    else if constexpr (S == 8) return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true); // row_ror 8
+    else if constexpr (S == 16) return __builtin_amdgcn_ds_swizzle(v, 0x401F);            // xor 16 in 32
     else {
         static_assert(S == 32, "lane distance");
         const auto p = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
@@ -62,102 +82,121 @@ template <int S> __device__ __forceinline__ float lane_xor(float v)
     return __builtin_bit_cast(float, lane_xor<S>(__builtin_bit_cast(int, v)));
 }
 
-// one compare-exchange step between lanes `lane` and `lane ^ S`; keep_better selects which of
-// the two this lane keeps
-template <int S> __device__ __forceinline__ void cmpx(float &v, int &r, bool keep_better)
+template <int S> __device__ __forceinline__ uint64_t lane_xor(uint64_t v)
 {
-    const float pv = lane_xor<S>(v);
-    const int pr = lane_xor<S>(r);
-    // rows are distinct except empty slots, which are identical, so "mine is better" is
-    // "partner is not better" (swapping two identical empty slots changes nothing)
-    const bool take = keep_better == better(pv, pr, v, r);
-    v = take ? pv : v;
-    r = take ? pr : r;
+    const uint32_t lo = (uint32_t)lane_xor<S>((int)(uint32_t)v), hi = (uint32_t)lane_xor<S>((int)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// bitonic sort of the wave's 64 (v, r) pairs, worst first (lane 63 holds the best: the order
-// a sorted list merges against without reversing it)
-template <int SIZE, int S> __device__ __forceinline__ void sort_stage(float &v, int &r, int lane)
-{
-    if constexpr (S > 0) {
-        cmpx<S>(v, r, ((lane & S) == 0) != ((lane & SIZE) == 0));
-        sort_stage<SIZE, S / 2>(v, r, lane);
-    }
-}
-
-template <int SIZE = 2> __device__ __forceinline__ void wave_sort(float &v, int &r, int lane)
-{
-    if constexpr (SIZE <= 64) {
-        sort_stage<SIZE, SIZE / 2>(v, r, lane);
-        wave_sort<SIZE * 2>(v, r, lane);
-    }
-}
-
-// bitonic clean of a bitonic 64-sequence into best-first order
-template <int S = 32> __device__ __forceinline__ void wave_clean(float &v, int &r, int lane)
-{
-    if constexpr (S > 0) {
-        cmpx<S>(v, r, (lane & S) == 0);
-        wave_clean<S / 2>(v, r, lane);
-    }
-}
-
-// L (sorted, best first) := the 64 best of L and Q, with Q sorted worst first: lane by lane
-// the better of the two is the upper half of a bitonic sequence, which one clean sorts.
-__device__ __forceinline__ void wave_merge(float &lv, int &lr, float qv, int qr, int lane)
-{
-    const bool qb = better(qv, qr, lv, lr);
-    lv = qb ? qv : lv;
-    lr = qb ? qr : lr;
-    wave_clean(lv, lr, lane);
-}
-
-// Merge the wave's 64 (v, r) pairs, one per lane, into the sorted list.  Only pairs that beat
-// the current k-th best can end in the top k: when none does (one compare and a wave vote), the
-// chunk costs nothing more; otherwise it is sorted worst first (unless SORTED: then it already
-// is) and merged.  (Inserting a few
-// candidates one at a time measured slower than the sort: each insertion is a chain of
-// vector-to-scalar round trips.)
-template <bool SORTED>
-__device__ __forceinline__ void wave_take(float &lv, int &lr, float v, int r, int k, int lane)
-{
-    const float tv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), k - 1));
-    const int tr = __builtin_amdgcn_readlane(lr, k - 1);
-    if (!__ballot(better(v, r, tv, tr))) return;
-    if constexpr (!SORTED) wave_sort(v, r, lane);
-    wave_merge(lv, lr, v, r, lane);
-}
-
-// sort one lane's pairs a, b into best-first order
-__device__ __forceinline__ void lane_cswap(float &va, int &ra, float &vb, int &rb)
-{
-    const bool sw = better(vb, rb, va, ra);
-    const float tv = va;
-    const int tr = ra;
-    va = sw ? vb : va;
-    ra = sw ? rb : ra;
-    vb = sw ? tv : vb;
-    rb = sw ? tr : rb;
-}
-
-// The log-sum-exp state (max, sum of exp(v - max)) of the whole wave from the lanes' states:
-// the wave max, one exponential per lane to rescale its sum, then a sum over the lanes, all
-// through the lane exchanges above.  Every lane ends with the max; lane 0's sum is the one
-// used (its order of additions is the same every run).
 template <int S> __device__ __forceinline__ double lane_xor(double v)
 {
     const int lo = lane_xor<S>(__double2loint(v)), hi = lane_xor<S>(__double2hiint(v));
     return __hiloint2double(hi, lo);
 }
 
+__device__ __forceinline__ uint64_t readlane(uint64_t v, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// ---------------------------------------------------------------------------- wave sort / merge
+
+// one compare-exchange between lanes `lane` and `lane ^ S`; keep_better says which one this lane
+// keeps (keys are distinct except empty slots, which are equal, so either choice is right then)
+template <int S> __device__ __forceinline__ void cmpx(uint64_t &key, bool keep_better)
+{
+    const uint64_t p = lane_xor<S>(key);
+    key = keep_better == (p > key) ? p : key;
+}
+
+template <int SIZE, int S> __device__ __forceinline__ void sort_stage(uint64_t &key, int lane)
+{
+    if constexpr (S > 0) {
+        cmpx<S>(key, ((lane & S) == 0) != ((lane & SIZE) == 0));
+        sort_stage<SIZE, S / 2>(key, lane);
+    }
+}
+
+// bitonic sort of the wave's 64 keys, worst first (lane 63 holds the best: the order a sorted
+// list merges against without reversing it)
+template <int SIZE = 2, int LAST = 64> __device__ __forceinline__ void wave_sort(uint64_t &key, int lane)
+{
+    if constexpr (SIZE <= LAST) {
+        sort_stage<SIZE, SIZE / 2>(key, lane);
+        wave_sort<SIZE * 2, LAST>(key, lane);
+    }
+}
+
+// bitonic clean of a bitonic 64-sequence into best-first order
+template <int S = 32> __device__ __forceinline__ void wave_clean(uint64_t &key, int lane)
+{
+    if constexpr (S > 0) {
+        cmpx<S>(key, (lane & S) == 0);
+        wave_clean<S / 2>(key, lane);
+    }
+}
+
+// the same sort best first: the stages up to 32 leave a bitonic 64-sequence, cleaned downwards
+__device__ __forceinline__ void wave_sort_best_first(uint64_t &key, int lane)
+{
+    wave_sort<2, 32>(key, lane);
+    wave_clean(key, lane);
+}
+
+// L (sorted, best first) := the 64 best of L and Q, with Q sorted worst first: lane by lane the
+// better of the two is the upper half of a bitonic sequence, which one clean sorts
+__device__ __forceinline__ void wave_merge(uint64_t &list, uint64_t q, int lane)
+{
+    list = q > list ? q : list;
+    wave_clean(list, lane);
+}
+
+// Take the wave's 64 keys (one per lane, 0 = none) into the sorted list, keeping its k best:
+// when no key beats the list's k-th (one compare and a wave vote) nothing more is done,
+// otherwise the keys are sorted and merged.
+__device__ __forceinline__ void wave_take(uint64_t &list, uint64_t key, int k, int lane)
+{
+    if (!__ballot(key > readlane(list, k - 1))) return;
+    wave_sort(key, lane);
+    wave_merge(list, key, lane);
+}
+
+// ---------------------------------------------------------------------------- exp
+
+// e^x for x <= 0 (or -inf): 2^(x log2 e) with x log2 e carried in two parts, the hardware 2^h of
+// the rounded part times the first-order term of the rest, within a few ulp.  x is clamped at
+// -200 (e^-200 and below flush to zero, which no sum of terms up to 1 can tell apart; -inf
+// would make the residual NaN).
+__device__ __forceinline__ float exp_nonpos(float x)
+{
+    constexpr float kL = 1.44269502f;         // log2 e rounded to float
+    constexpr float kLlo = 1.92596299e-8f;    // log2 e - kL
+    constexpr float kLn2 = 0.693147182f;
+    x = fmaxf(x, -200.f);
+    const float h = x * kL;
+    const float l = fmaf(x, kL, -h) + x * kLlo;
+    const float e = __builtin_amdgcn_exp2f(h);
+    return fmaf(e, l * kLn2, e);
+}
+
+// ---------------------------------------------------------------------------- reductions
+
+template <int S, typename F> __device__ __forceinline__ F max_step(F v)
+{
+    const F o = lane_xor<S>(v);
+    return o > v ? o : v;
+}
+
 template <typename F> __device__ __forceinline__ F wave_max(F v)
 {
-    v = fmax(v, lane_xor<1>(v));
-    v = fmax(v, lane_xor<2>(v));
-    v = fmax(v, lane_xor<4>(v));
-    v = fmax(v, lane_xor<8>(v));
-    v = fmax(v, lane_xor<16>(v));
-    return fmax(v, lane_xor<32>(v));
+    v = max_step<1>(v);
+    v = max_step<2>(v);
+    v = max_step<4>(v);
+    v = max_step<8>(v);
+    v = max_step<16>(v);
+    return max_step<32>(v);
 }
 
 template <typename F> __device__ __forceinline__ F wave_sum(F v)
@@ -170,6 +209,9 @@ template <typename F> __device__ __forceinline__ F wave_sum(F v)
     return v + lane_xor<32>(v);
 }
 
+// The log-sum-exp state (max, sum of exp(v - max)) of the whole wave from the lanes' states: the
+// wave max, one exponential per lane to rescale its sum, then a sum over the lanes, in a fixed
+// order.  Every lane ends with the wave's state.
 template <typename F> __device__ __forceinline__ void wave_lse(F &m, F &s)
 {
     const F mx = wave_max(m);
@@ -177,239 +219,368 @@ template <typename F> __device__ __forceinline__ void wave_lse(F &m, F &s)
     m = mx;
 }
 
-__device__ __forceinline__ float ld_agent(const float *p)
-{
-    return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT));
-}
+// ---------------------------------------------------------------------------- rank selection
 
-__device__ __forceinline__ int ld_agent(const int32_t *p)
+// The number of keys in s[0..n) above `key` (LDS broadcast reads, two keys each, eight in flight:
+// the compares are independent, unlike the steps of a sort).
+__device__ __forceinline__ int rank_in(const uint64_t *s, int n, uint64_t key)
 {
-    return (int)__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint32_t publish(float *p, float v)
-{
-    return __hip_atomic_exchange(reinterpret_cast<uint32_t *>(p), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint32_t publish(int32_t *p, int v)
-{
-    return __hip_atomic_exchange(reinterpret_cast<uint32_t *>(p), (uint32_t)v, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-}
-
-constexpr int kWaves = 16;        // waves per block
-constexpr int kThreads = 64 * kWaves;
-constexpr int kStageWords = 8192;  // LDS words staging block partials in the final merge (32 KB)
-constexpr int kBurst = 16;         // loads each thread issues before using the first
-
-// (m, s) := combination of two online log-sum-exp states, in double
-__device__ __forceinline__ void lse_combine_d(double &m, double &s, double pm, double ps)
-{
-    if (pm == -INFINITY) return;
-    if (m == -INFINITY) {
-        m = pm;
-        s = ps;
-        return;
+    const ulonglong2 *p = reinterpret_cast<const ulonglong2 *>(s);
+    int r = 0;
+#pragma unroll 8
+    for (int i = 0; i < n / 2; ++i) {
+        const ulonglong2 q = p[i];
+        r += (int)(q.x > key) + (int)(q.y > key);
     }
-    const double mx = fmax(m, pm);
-    s = s * exp(m - mx) + ps * exp(pm - mx);
-    m = mx;
+    if (n & 1) r += (int)(s[n - 1] > key);
+    return r;
 }
 
-
-// The sorted lists of the block's 16 waves (in s_v / s_r) merge pairwise in a fixed tree
-// (wave w takes wave w + step); wave 0 ends with the block's list in (lv, lr).
-__device__ __forceinline__ void block_tree_merge(float (*s_v)[64], int (*s_r)[64], float &lv, int &lr, int w,
-                                                 int lane)
+// Each thread appends its keys at or above th (and non-zero) to s_cand at offset `at0` +
+// its place from one atomic on s_count: one LDS atomic per thread that has any.
+template <int N>
+__device__ __forceinline__ void append_at_or_above(const uint64_t (&key)[N], uint64_t th, uint64_t *s_cand, int cap,
+                                                   int *s_count, int at0)
 {
-    for (int step = kWaves / 2; step > 0; step >>= 1) {
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) cnt += (int)(key[j] != 0 && key[j] >= th);
+    if (cnt == 0) return;
+    int at = at0 + atomicAdd(s_count, cnt);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        if (key[j] != 0 && key[j] >= th) {
+            if (at < cap) s_cand[at] = key[j];
+            ++at;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- kernel 1
+
+constexpr int kWaves = 4;                    // waves per block
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPerLane = 8;                  // rows per lane per round
+constexpr int kRound = kPerLane * kThreads;  // rows per round
+constexpr int kCand = kThreads;              // candidates ranked at once: one per thread
+
+// The sorted lists of the block's waves (in s_list and in registers, best first) merge pairwise
+// in a fixed tree (wave w takes wave w + step, read worst first); wave 0 ends with the block's.
+template <int NW>
+__device__ __forceinline__ void block_tree_merge(uint64_t (*s_list)[64], uint64_t &list, int w, int lane)
+{
+    for (int step = NW / 2; step > 0; step >>= 1) {
         __syncthreads();
         if (w < step) {
-            wave_merge(lv, lr, s_v[w + step][63 - lane], s_r[w + step][63 - lane], lane);
-            s_v[w][lane] = lv;
-            s_r[w][lane] = lr;
+            wave_merge(list, s_list[w + step][63 - lane], lane);
+            s_list[w][lane] = list;
         }
     }
 }
 
 __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
 {
-    __shared__ float s_v[kWaves][64];
-    __shared__ int s_r[kWaves][64];
+    __shared__ __align__(16) uint64_t s_cand[kCand];
+    __shared__ uint64_t s_top[64];
+    __shared__ __align__(16) uint64_t s_lm[kWaves][64];
+    __shared__ uint64_t s_thw[kWaves];
     __shared__ float s_m[kWaves], s_s[kWaves];
-    __shared__ int32_t s_stage[kStageWords];
-    __shared__ int s_last;
-
+    __shared__ int s_count[3];  // round r counts in s_count[r % 3]
+    __shared__ int s_ntop;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int b = blockIdx.x, t = blockIdx.y;
-    const int k = a.k, kc = a.k;
+    const int k = a.k;
     const float *yt = a.y + (int64_t)t * a.ldy;
     const int r0 = b * a.rpb;
     const int r1 = r0 + a.rpb < a.M ? r0 + a.rpb : a.M;
+    if (threadIdx.x == 0) s_count[0] = 0;
 
-    // ---- stream the block's rows: 4 chunks of 64 rows per wave in flight,
-    //      rows r0 + 64 * (kWaves * (4i + j) + w) + lane
-    float lv = -INFINITY, m = -INFINITY, s = 0.f;
-    int lr = kRowEmpty;
-    for (int base = r0; base < r1; base += 4 * kThreads) {
-        float v[4];
-        int row[4];
+    float m = -INFINITY, s = 0.f;
+    int ntop = 0;        // entries in s_top, the block's best keys so far (best first)
+    uint64_t theta = 0;  // the k-th of them (0 while there are fewer)
+    int rr = 0;  // round index mod 3
+    float nv[kPerLane];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            row[j] = base + kThreads * j + 64 * w + lane;
-            v[j] = row[j] < r1 ? yt[row[j]] : -INFINITY;
-        }
+    for (int j = 0; j < kPerLane; ++j) {
+        const int row = r0 + kThreads * j + threadIdx.x;
+        nv[j] = row < r1 ? yt[row] : -INFINITY;
+    }
+    for (int base = r0; base < r1; base += kRound) {
+        float v[kPerLane];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (row[j] < r1) {
-                if (v[j] > m) {
-                    s = s * expf(m - v[j]) + 1.f;
-                    m = v[j];
-                } else {
-                    s += expf(v[j] - m);
-                }
-            } else {
-                row[j] = kRowEmpty;
+        for (int j = 0; j < kPerLane; ++j) v[j] = nv[j];
+        if (base + kRound < r1) {
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) {
+                const int row = base + kRound + kThreads * j + threadIdx.x;
+                nv[j] = row < r1 ? yt[row] : -INFINITY;
             }
         }
-        if (k > 0) {
-            // each lane orders its four rows first: chunk j then holds every lane's j-th best, so
-            // once the lane maxima are in the list the later chunks rarely have a candidate
-            lane_cswap(v[0], row[0], v[1], row[1]);
-            lane_cswap(v[2], row[2], v[3], row[3]);
-            lane_cswap(v[0], row[0], v[2], row[2]);
-            lane_cswap(v[1], row[1], v[3], row[3]);
-            lane_cswap(v[1], row[1], v[2], row[2]);
+        // online log-sum-exp: rows past the end load as -inf and add exp(-inf) = 0
+        float mr = v[0];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wave_take<false>(lv, lr, v[j], row[j], k, lane);
+        for (int j = 1; j < kPerLane; ++j) mr = fmaxf(mr, v[j]);
+        if (mr > -INFINITY) {
+            const float mn = fmaxf(m, mr);
+            float acc = m == -INFINITY ? 0.f : s * exp_nonpos(m - mn);
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) acc += exp_nonpos(v[j] - mn);
+            m = mn;
+            s = acc;
         }
+        if (k == 0) continue;
+        uint64_t key[kPerLane];
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int row = base + kThreads * j + threadIdx.x;
+            key[j] = row < r1 ? make_key(v[j], row) : 0ull;
+        }
+        if (base == r0) {
+            // theta := the largest over the waves of the k-th best lane maximum of the wave
+            uint64_t mx = key[0];
+#pragma unroll
+            for (int j = 1; j < kPerLane; ++j) mx = key[j] > mx ? key[j] : mx;
+            s_lm[w][lane] = mx;
+            if (lane == 0) s_thw[w] = 0;
+            __syncthreads();
+            if (rank_in(s_lm[w], 64, mx) == k - 1) s_thw[w] = mx;  // empty lane maxima tie at 0
+            __syncthreads();
+            theta = s_thw[0];
+#pragma unroll
+            for (int i = 1; i < kWaves; ++i) theta = s_thw[i] > theta ? s_thw[i] : theta;
+        }
+        // candidates: the list so far, then this round's keys at or above theta.  The next
+        // round's counter is cleared before this round's barrier: its last readers (two rounds
+        // ago) are past the previous barrier, and the next round counts after this one.
+        const int rn = rr == 2 ? 0 : rr + 1;
+        if (threadIdx.x == 0) s_count[rn] = 0;
+        if (threadIdx.x < ntop) s_cand[threadIdx.x] = s_top[threadIdx.x];
+        append_at_or_above(key, theta, s_cand, kCand, &s_count[rr], ntop);
+        __syncthreads();
+        const int C = ntop + s_count[rr];
+        rr = rn;
+        if (C == ntop) continue;  // nothing new; s_cand and s_top were only read
+        if (C <= kCand) {
+            if (threadIdx.x < C) {
+                const uint64_t c = s_cand[threadIdx.x];
+                const int r = rank_in(s_cand, C, c);
+                if (r < k) s_top[r] = c;
+            }
+            ntop = C < k ? C : k;
+        } else {
+            // rare: every wave takes its keys at or above theta (wave 0 the list too) by sorts,
+            // and the waves' lists merge
+            uint64_t wl = 0;
+            if (w == 0) wave_take(wl, lane < ntop ? s_top[lane] : 0ull, k, lane);
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) wave_take(wl, key[j] >= theta ? key[j] : 0ull, k, lane);
+            __syncthreads();  // every reader of s_top is done
+            s_lm[w][lane] = wl;
+            block_tree_merge<kWaves>(s_lm, wl, w, lane);
+            if (w == 0) {
+                if (lane < k) s_top[lane] = wl;
+                const int nz = __popcll(__ballot(lane < k && wl != 0));
+                if (lane == 0) s_ntop = nz;
+            }
+            __syncthreads();
+            ntop = s_ntop;
+        }
+        __syncthreads();
+        theta = ntop == k ? s_top[k - 1] : 0ull;
     }
+
+    // block partial: (max, sum) of the 4 waves, the k best keys and the k-th
     wave_lse(m, s);
-    s_v[w][lane] = lv;
-    s_r[w][lane] = lr;
     if (lane == 0) {
         s_m[w] = m;
         s_s[w] = s;
     }
-    if (k > 0) block_tree_merge(s_v, s_r, lv, lr, w, lane);
     __syncthreads();
-
-    // ---- block partial (wave 0): publish (max, sum, k best) with returning exchanges
-    float *pf = a.part_f + ((int64_t)t * a.B + b) * (2 + kc);
-    int32_t *pi = a.part_i + ((int64_t)t * a.B + b) * kc;
-    uint32_t sink = 0;
     if (w == 0) {
-        // the 16 wave states: lanes 0..15 hold them, lane 0 ends with the block's state
-        m = lane < kWaves ? s_m[lane] : -INFINITY;
-        s = lane < kWaves ? s_s[lane] : 0.f;
-        wave_lse(m, s);
-        if (lane < kc) {
-            sink |= publish(pf + 2 + lane, lv);
-            sink |= publish(pi + lane, lr);
-        }
-        if (lane == 0) {
-            sink |= publish(pf, m);
-            sink |= publish(pf + 1, s);
+        float mm = lane < kWaves ? s_m[lane] : -INFINITY, ss = lane < kWaves ? s_s[lane] : 0.f;
+        wave_lse(mm, ss);
+        const int64_t tb = (int64_t)t * a.B + b;
+        if (lane == 0) a.part_lse[tb] = make_float2(mm, ss);
+        if (k > 0) {
+            if (lane < k) a.part_list[tb * k + lane] = lane < ntop ? s_top[lane] : 0ull;
+            if (lane == 0) a.part_kth[tb] = ntop == k ? s_top[k - 1] : 0ull;
         }
     }
-    asm volatile("" ::"v"(sink));
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&a.counter[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == (uint32_t)(a.B - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
+}
 
-    // ---- last block of token t: merge the B partials.  They are staged through LDS in chunks
-    //      of cb blocks; each thread issues kBurst independent loads before using the first.
-    const float *tf = a.part_f + (int64_t)t * a.B * (2 + kc);
-    const int32_t *ti = a.part_i + (int64_t)t * a.B * kc;
-    const int stride_f = 2 + kc, per = 2 + 2 * kc;
-    const int cb = kStageWords / per < a.B ? kStageWords / per : a.B;
-    float *st_f = reinterpret_cast<float *>(s_stage);
-    int32_t *st_i = s_stage + cb * stride_f;
-    double tm = -INFINITY, ts = 0.0;  // wave 0 lane l: blocks l, l + 64, ... in order
-    lv = -INFINITY;
-    lr = kRowEmpty;
-    for (int c0 = 0; c0 < a.B; c0 += cb) {
-        const int n = a.B - c0 < cb ? a.B - c0 : cb;
-        const int nf = n * stride_f, ni = n * kc;
-        __syncthreads();  // the previous chunk's readers are done
-        for (int e0 = threadIdx.x; e0 < nf; e0 += kBurst * kThreads) {
-            float v[kBurst];
+// ---------------------------------------------------------------------------- kernel 2
+
+constexpr int kMWaves = 4;
+constexpr int kMThreads = 64 * kMWaves;
+constexpr int kMPer = 16;                               // list entries per thread per round of loads
+constexpr int kMPerBlock = kMaxBlocks / kMThreads;      // blocks (states, heads) per thread at most
+constexpr int kMCand = 1024;                            // candidates ranked at once
+
+__global__ __launch_bounds__(kMThreads) void logits_merge_kernel(MergeArgs a)
+{
+    __shared__ __align__(16) uint64_t s_cand[kMCand];
+    __shared__ __align__(16) uint64_t s_h[kMaxBlocks];   // the lists' best keys
+    __shared__ __align__(16) uint64_t s_hc[kMaxBlocks];  // those among the k best of their group of 64
+    __shared__ uint64_t s_list[kMWaves][64];
+    __shared__ float s_mx[kMWaves];
+    __shared__ double s_sum[kMWaves];
+    __shared__ uint64_t s_kth[kMWaves];
+    __shared__ uint64_t s_th;
+    __shared__ int s_count, s_hcount;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = blockIdx.x;
+    const int k = a.k, G = a.G;
+    const int n = G * k;
+    const int i0 = threadIdx.x;
+    if (i0 == 0) {
+        s_count = 0;
+        s_hcount = 0;
+        s_th = 0;
+    }
+
+    // every load at once: the block states, k-th keys and best keys (thread i0 takes blocks
+    // i0, i0 + 256), and the first kMPer entries of the lists per thread
+    float2 p[kMPerBlock];
+    uint64_t kth = 0, head[kMPerBlock];
+    const uint64_t *lists = a.list + (int64_t)t * n;
 #pragma unroll
-            for (int i = 0; i < kBurst; ++i) {
-                const int e = e0 + kThreads * i;
-                v[i] = e < nf ? ld_agent(tf + (int64_t)c0 * stride_f + e) : 0.f;
+    for (int q = 0; q < kMPerBlock; ++q) {
+        const int i = i0 + kMThreads * q;
+        p[q] = i < G ? a.lse_part[(int64_t)t * G + i] : make_float2(-INFINITY, 0.f);
+        const uint64_t kq = k > 0 && i < G ? a.kth[(int64_t)t * G + i] : 0ull;
+        kth = kq > kth ? kq : kth;
+        head[q] = k > 0 && i < G ? lists[(int64_t)i * k] : 0ull;
+    }
+    uint64_t e[kMPer];
+#pragma unroll
+    for (int j = 0; j < kMPer; ++j) {
+        const int idx = i0 + kMThreads * j;
+        e[j] = idx < n ? lists[idx] : 0ull;
+    }
+
+    // log-sum-exp: the largest block max, then the blocks' sums rescaled to it (fp32 exponent of
+    // a difference, summed in double in a fixed order)
+    float mt = p[0].x;
+#pragma unroll
+    for (int q = 1; q < kMPerBlock; ++q) mt = fmaxf(mt, p[q].x);
+    mt = wave_max(mt);
+    kth = wave_max(kth);
+    if (lane == 0) {
+        s_mx[w] = mt;
+        s_kth[w] = kth;
+    }
+#pragma unroll
+    for (int q = 0; q < kMPerBlock; ++q)
+        if (i0 + kMThreads * q < G) s_h[i0 + kMThreads * q] = head[q];
+    __syncthreads();
+    float mstar = s_mx[0];
+    uint64_t tau = s_kth[0];
+#pragma unroll
+    for (int i = 1; i < kMWaves; ++i) {
+        mstar = fmaxf(mstar, s_mx[i]);
+        tau = s_kth[i] > tau ? s_kth[i] : tau;
+    }
+    double term = 0.0;
+#pragma unroll
+    for (int q = 0; q < kMPerBlock; ++q)
+        term += p[q].x == -INFINITY ? 0.0 : (double)p[q].y * (double)expf(p[q].x - mstar);
+    const double sw = wave_sum(term);
+    if (lane == 0) s_sum[w] = sw;
+
+    if (k > 0) {
+        // tau: the larger of two keys that k distinct rows reach, the largest k-th entry of a
+        // list and the k-th best of the lists' best keys (tight when the lists are many); the
+        // latter from the best keys that are among the k best of their group of 64
+#pragma unroll
+        for (int q = 0; q < kMPerBlock; ++q) {
+            const int i = i0 + kMThreads * q;
+            if (i < G && head[q] != 0) {
+                const int g0 = i & ~63, gn = G - g0 < 64 ? G - g0 : 64;
+                if (rank_in(s_h + g0, gn, head[q]) < k) s_hc[atomicAdd(&s_hcount, 1)] = head[q];
             }
-#pragma unroll
-            for (int i = 0; i < kBurst; ++i)
-                if (e0 + kThreads * i < nf) st_f[e0 + kThreads * i] = v[i];
-        }
-        for (int e0 = threadIdx.x; e0 < ni; e0 += kBurst * kThreads) {
-            int v[kBurst];
-#pragma unroll
-            for (int i = 0; i < kBurst; ++i) {
-                const int e = e0 + kThreads * i;
-                v[i] = e < ni ? ld_agent(ti + (int64_t)c0 * kc + e) : 0;
-            }
-#pragma unroll
-            for (int i = 0; i < kBurst; ++i)
-                if (e0 + kThreads * i < ni) st_i[e0 + kThreads * i] = v[i];
         }
         __syncthreads();
-        if (w == 0)
-            for (int e = lane; e < n; e += 64)
-                lse_combine_d(tm, ts, (double)st_f[e * stride_f], (double)st_f[e * stride_f + 1]);
-        // top-k: wave w takes the block lists w, w + 16, ... of the chunk (lane i reads entry i)
-        if (k > 0)
-            for (int e = w; e < n; e += kWaves) {
-                // the block's list, read worst first (empty slots, then entry kc - 1 ... 0)
-                const int q = 63 - lane;
-                const float cv = q < kc ? st_f[e * stride_f + 2 + q] : -INFINITY;
-                const int cr = q < kc ? st_i[e * kc + q] : kRowEmpty;
-                wave_take<true>(lv, lr, cv, cr, k, lane);
+        const int Ch = s_hcount;
+        for (int c = i0; c < Ch; c += kMThreads)
+            if (rank_in(s_hc, Ch, s_hc[c]) == k - 1) s_th = s_hc[c];
+        __syncthreads();
+        tau = s_th > tau ? s_th : tau;
+        // candidates: the entries at or above tau
+        append_at_or_above(e, tau, s_cand, kMCand, &s_count, 0);
+        for (int c0 = kMThreads * kMPer; c0 < n; c0 += kMThreads * kMPer) {
+#pragma unroll
+            for (int j = 0; j < kMPer; ++j) {
+                const int idx = c0 + i0 + kMThreads * j;
+                e[j] = idx < n ? lists[idx] : 0ull;
             }
-    }
-    if (k > 0) {
-        __syncthreads();  // the stage is free; s_v / s_r take the wave lists
-        s_v[w][lane] = lv;
-        s_r[w][lane] = lr;
-        block_tree_merge(s_v, s_r, lv, lr, w, lane);
-    }
-    if (w == 0) {
-        if (lane < kc) {
-            a.vals[(int64_t)t * kc + lane] = lv;
-            a.ids[(int64_t)t * kc + lane] = lr == kRowEmpty ? -1 : (a.index ? a.index[lr] : lr);
+            append_at_or_above(e, tau, s_cand, kMCand, &s_count, 0);
         }
-        // the 64 lane states (in double), lane 0 ends with the token's
-        wave_lse(tm, ts);
-        if (lane == 0 && a.lse) a.lse[t] = (float)(tm + log(ts));
-        if (lane == 0) __hip_atomic_store(&a.counter[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int C = s_count;
+        float *vals = a.vals + (int64_t)t * k;
+        int32_t *ids = a.ids + (int64_t)t * k;
+        if (C <= kMCand) {
+            for (int c = i0; c < C; c += kMThreads) {
+                const uint64_t key = s_cand[c];
+                const int r = rank_in(s_cand, C, key);
+                if (r < k) {
+                    vals[r] = key_value(key);
+                    ids[r] = a.index ? a.index[key_row(key)] : key_row(key);
+                }
+            }
+            if (i0 >= C && i0 < k) {
+                vals[i0] = -INFINITY;
+                ids[i0] = -1;
+            }
+        } else {
+            // rare: every wave takes its threads' candidates by sorts, read again
+            uint64_t list = 0;
+#pragma unroll 1
+            for (int idx = i0; idx - lane < n; idx += kMThreads) {
+                const uint64_t c = idx < n ? lists[idx] : 0ull;
+                wave_take(list, c >= tau ? c : 0ull, k, lane);
+            }
+            s_list[w][lane] = list;
+            block_tree_merge<kMWaves>(s_list, list, w, lane);
+            if (w == 0 && lane < k) {
+                vals[lane] = list ? key_value(list) : -INFINITY;
+                ids[lane] = list ? (a.index ? a.index[key_row(list)] : key_row(list)) : -1;
+            }
+        }
+    }
+    __syncthreads();
+    if (w == 0 && a.lse) {
+        double ss = lane < kMWaves ? s_sum[lane] : 0.0;
+        ss = wave_sum(ss);
+        if (lane == 0) a.lse[t] = (float)((double)mstar + log(ss));
     }
 }
 
 }  // namespace
 
-int logits_blocks_per_cu()
-{
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(&logits_kernel), kThreads, 0) !=
-        hipSuccess)
-        return 0;
-    return n;
-}
-
 hipError_t launch_logits(const LogitsArgs &a, hipStream_t st)
 {
+    if (a.B < 1 || a.B > kMaxBlocks || a.T < 1 || a.k < 0 || a.k > 64 || a.M < 1 || a.rpb < 1 ||
+        (int64_t)a.B * a.rpb < a.M)
+        return hipErrorInvalidValue;
     LogitsArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&logits_kernel), dim3((unsigned)a.B, (unsigned)a.T),
-                           dim3(kThreads), args, 0, st);
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&logits_kernel), dim3((unsigned)a.B, (unsigned)a.T),
+                                   dim3(kThreads), args, 0, st);
+    if (e != hipSuccess) return e;
+    MergeArgs m;
+    m.lse_part = a.part_lse;
+    m.kth = a.part_kth;
+    m.list = a.part_list;
+    m.G = a.B;
+    m.k = a.k;
+    m.index = a.index;
+    m.lse = a.lse;
+    m.vals = a.vals;
+    m.ids = a.ids;
+    void *margs[] = {&m};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&logits_merge_kernel), dim3((unsigned)a.T),
+                           dim3(kMThreads), margs, 0, st);
 }
 
 }  // namespace qmatk
