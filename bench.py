@@ -40,6 +40,7 @@ HBM_PEAK_GBS = 8000.0
 PRIMARY = ("q4_gate_up_34816x5120", 1)
 ROTATE_BYTES = 512 << 20
 PREFILL_T = (512, 2048)                      # prefill chunk sizes timed on the GEMM route
+PROBE_WARM_S = 0.3  # wall time each read-probe shape replays before it is timed (best of 3 replays)
 PREFILL_SHAPES = ("q5_down_5120x17408", "fp8_proj_5120x5120")
 WARM_S = 0.25            # wall time each decode line runs before it is timed
 WARM_HEADLINE_S = 1.0    # the same for the headline line
@@ -310,16 +311,16 @@ def read_ceilings(window_bytes, big_bytes):
     large as the largest benchmark matrix, and over windows of the headline matrix's size
     rotated through 1 GiB (so each read streams from HBM, as the rotated weight copies do)."""
     from weight_only_quant_amd import probe
-    big, big_shapes = probe.best_read_gbs(big_bytes)
+    big, big_shapes = probe.best_read_gbs(big_bytes, warm_s=PROBE_WARM_S, replays=3)
     w = window_bytes // 1024 * 1024
-    win, _ = probe.best_read_gbs(1 << 30, window=w, reps=100)
+    win, _ = probe.best_read_gbs(1 << 30, window=w, reps=100, warm_s=PROBE_WARM_S, replays=3)
     return {"GBps_big": big, "big_bytes": big_bytes, "shapes_big": big_shapes, "GBps_window": win, "window_bytes": w}
 
 
 def read_probe_window(window_bytes):
     """Best plain-read rate (GB/s) over windows of window_bytes rotated through 1 GiB."""
     from weight_only_quant_amd import probe
-    return probe.best_read_gbs(1 << 30, window=window_bytes, reps=100)
+    return probe.best_read_gbs(1 << 30, window=window_bytes, reps=100, warm_s=PROBE_WARM_S, replays=3)
 
 
 def cpu_context(target_s=1.0):

@@ -5,8 +5,9 @@
  *
  * The kernel reads a device buffer once, in 1 KB chunks (one 16-byte nontemporal load per
  * lane of a 64-lane wave), each wave keeping `unroll` loads in flight, and folds what it read
- * into one 32-bit word per lane so the loads cannot be dropped.  Waves take either
- * consecutive runs of chunks or every grid_waves-th chunk, and the workgroup size and an LDS
+ * into one 32-bit word per lane so the loads cannot be dropped.  Waves take consecutive runs of
+ * chunks, or every grid_waves-th chunk, or workgroups take runs that their waves interleave
+ * (the order of a product workgroup streaming a tile), and the workgroup size and an LDS
  * reservation set how many waves a compute unit runs at once.  The best launch shape over a
  * small sweep on a buffer much larger than the last-level caches is the practical ceiling of
  * a streaming kernel on this GPU.
@@ -33,7 +34,9 @@ int64_t qmat_probe_read_out_words(int64_t nbytes, int per_wave, int waves_per_bl
  *   per_wave:        with grid_waves == 0, each wave reads per_wave consecutive 1 KB chunks
  *                    (1 .. 65536) and the grid covers the buffer.
  *   grid_waves:      if > 0 (at most 2^24), that many waves instead, wave w reading chunks
- *                    w, w + grid_waves, w + 2 grid_waves, ... (per_wave is not read).
+ *                    w, w + grid_waves, w + 2 grid_waves, ... (per_wave is not read);
+ *                    if -1, each workgroup reads per_wave consecutive chunks, its waves
+ *                    taking every waves_per_block-th chunk of the run in turn.
  *   unroll:          loads in flight per wave: 1, 2, 4, 8 or 16.
  *   waves_per_block: waves per workgroup, 1 .. 8.
  *   lds_bytes:       dynamic LDS per workgroup, 0 .. 65536: unused memory whose only effect is

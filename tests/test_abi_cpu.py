@@ -159,8 +159,11 @@ def test_probe_library_exports_its_header_and_validates():
     assert W(1024 * 9, 2, 4, 0) == 2 * 256      # 5 waves: two
     assert W(1024 * 9, 2, 1, 0) == 5 * 64       # one-wave workgroups
     assert W(1024 * 9, 0, 8, 100) == 13 * 512   # grid-stride: 100 waves in 8-wave workgroups
+    assert W(1024 * 9, 4, 4, -1) == 3 * 256     # workgroup runs of 4 chunks: 3 workgroups
+    assert W(1024 * 9, 9, 2, -1) == 128         # one run
     for args in [(0, 1, 4, 0), (1000, 1, 4, 0), (1024, 0, 4, 0), (1024, 65537, 4, 0), (-1024, 1, 4, 0),
-                 (1024, 1, 0, 0), (1024, 1, 9, 0), (1024, 1, 4, -1), (1024, 1, 4, (1 << 24) + 1)]:
+                 (1024, 1, 0, 0), (1024, 1, 9, 0), (1024, 1, 4, -2), (1024, 0, 4, -1),
+                 (1024, 1, 4, (1 << 24) + 1)]:
         assert W(*args) == 0, args
     # host-side validation returns before any GPU call
     R = L.qmat_probe_read

@@ -12,7 +12,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("nbytes", [1024, 5 * 1024, 1 << 20, (1 << 20) + 7 * 1024])
 @pytest.mark.parametrize("shape", [(1, 0, 1, 4, 0), (3, 0, 2, 1, 0), (16, 0, 4, 8, 0), (64, 0, 16, 1, 40960),
-                                   (7, 0, 8, 2, 0), (0, 5, 4, 8, 0), (0, 2048, 4, 8, 0), (0, 3, 16, 1, 20480)])
+                                   (7, 0, 8, 2, 0), (0, 5, 4, 8, 0), (0, 2048, 4, 8, 0), (0, 3, 16, 1, 20480),
+                                   (1, -1, 1, 1, 0), (3, -1, 2, 4, 0), (5, -1, 16, 2, 0), (240, -1, 8, 4, 65536)])
 def test_probe_reads_every_byte_once(nbytes, shape):
     print(f"probe nbytes={nbytes} shape={shape}", flush=True)
     rng = np.random.default_rng(nbytes + 131 * shape[0] + 7 * shape[1] + shape[2])

@@ -212,7 +212,7 @@ int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *co
         return fail(QMAT_EHIP, "%s: cannot read the compute unit count", who);
     }
     // launch plans for both routes and every tokens-per-launch; the tree nodes cover the largest
-    // split among them, and at least 8 splits at T = 16 for matrices of up to 4096 rows (explicit
+    // split among them, and at least 8 splits at T = 16 for matrices of up to 16384 rows (explicit
     // launch shapes in tests and tuning)
     size_t need_nodes = 0;
     for (int r = kRouteValu; r <= kRouteMfma; ++r)
@@ -223,7 +223,7 @@ int make_handle(qmat_t *handle, int fmt, int64_t M, int64_t K, const uint8_t *co
             const size_t f = run_node_words(Tl, (int)h->NT, p.splits, p.tail_tiles, p.tail_splits);
             if (f > need_nodes) need_nodes = f;
         }
-    if (h->Mpad <= 4096 && need_nodes < (size_t)7 * kMaxT * h->Mpad) need_nodes = (size_t)7 * kMaxT * h->Mpad;
+    if (h->Mpad <= 16384 && need_nodes < (size_t)7 * kMaxT * h->Mpad) need_nodes = (size_t)7 * kMaxT * h->Mpad;
     size_t need_ws = 0;
     // the GEMM route's automatic k splits (each within the cap by construction); beyond
     // 2 workgroup waves of row blocks x token tiles no split pays

@@ -17,9 +17,14 @@ SIGNATURES = {
 # Launch shapes swept for the ceiling: (per_wave, grid_waves, unroll, waves_per_block, lds_bytes).
 # Contiguous runs with one-wave workgroups held to four per compute unit by their LDS
 # reservation, and grid-stride reads by 8 waves per compute unit, were the fastest in a wider
-# sweep on MI355X (1 GiB: 7.0-7.1 TB/s); the others are common shapes for comparison.
+# sweep on MI355X (1 GiB: 7.0-7.1 TB/s); grid_waves -1 takes workgroup runs of per_wave chunks
+# that the workgroup's waves interleave, as a head workgroup streams its 240-330 KB tile (one
+# or two such workgroups per compute unit, or as many as fit); the others are common shapes for
+# comparison.
 SHAPES = ((256, 0, 8, 1, 40960), (64, 0, 8, 1, 40960), (64, 0, 4, 1, 20480), (256, 0, 16, 1, 0),
-          (64, 0, 16, 1, 0), (0, 2048, 4, 8, 0), (0, 2048, 8, 8, 0), (0, 2048, 4, 4, 0), (32, 0, 2, 4, 0))
+          (64, 0, 16, 1, 0), (0, 2048, 4, 8, 0), (0, 2048, 8, 8, 0), (0, 2048, 4, 4, 0), (32, 0, 2, 4, 0),
+          (240, -1, 4, 4, 65536), (240, -1, 8, 4, 65536), (240, -1, 8, 4, 0), (240, -1, 16, 4, 0),
+          (320, -1, 8, 4, 65536), (480, -1, 8, 8, 65536), (120, -1, 8, 4, 0), (240, -1, 8, 4, 40960))
 _lib = None
 
 
@@ -40,7 +45,7 @@ def lib():
 
 def shape_name(shape) -> str:
     pw, gw, unr, wpb, lds = shape
-    order = f"stride{gw}" if gw else f"run{pw}"
+    order = f"stride{gw}" if gw > 0 else f"block{pw}" if gw == -1 else f"run{pw}"
     return f"{order}_u{unr}_w{wpb}_lds{lds // 1024}k"
 
 
@@ -60,11 +65,16 @@ def read(buf, nbytes: int, shape, out, stream=None) -> None:
         raise RuntimeError(f"qmat_probe_read({nbytes}, {shape}) failed with status {st}")
 
 
-def best_read_gbs(nbytes: int = 1 << 30, window: Optional[int] = None, reps: int = 10, shapes=SHAPES):
+def best_read_gbs(nbytes: int = 1 << 30, window: Optional[int] = None, reps: int = 10, shapes=SHAPES,
+                  warm_s: float = 0.0, replays: int = 1):
     """Best read bandwidth (GB/s) over the launch shapes on a fresh buffer of nbytes, each timed
-    as `reps` launches captured in a HIP graph and replayed.  With window set, each launch reads
-    the next window-sized slice of the buffer (rotating through it, so a window smaller than the
-    caches still streams from HBM).  Returns (GB/s, {shape name: GB/s})."""
+    as `reps` launches captured in a HIP graph and replayed (the best of `replays` timed
+    replays, after replaying for warm_s seconds of wall time, so the GPU is at its steady
+    clock as in the product lines).  With window set, each launch reads the next window-sized
+    slice of the buffer (rotating through it, so a window smaller than the caches still streams
+    from HBM).  Returns (GB/s, {shape name: GB/s})."""
+    import time
+
     import torch
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
     w = nbytes if window is None else window
@@ -80,14 +90,21 @@ def best_read_gbs(nbytes: int = 1 << 30, window: Optional[int] = None, reps: int
         with torch.cuda.graph(g):
             for i in range(reps):
                 read(views[i % nwin], w, shape, out, stream=torch.cuda.current_stream())
+        t0 = time.time()
         g.replay()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        res[shape_name(shape)] = round(w * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+        while time.time() - t0 < warm_s:
+            g.replay()
+            torch.cuda.synchronize()
+        best = 0.0
+        for _ in range(max(1, replays)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            best = max(best, w * reps / (a.elapsed_time(b) * 1e-3) / 1e9)
+        res[shape_name(shape)] = round(best, 1)
         del g, out
     del buf, views
     torch.cuda.empty_cache()
