@@ -147,9 +147,9 @@ def qmat_packed_size(name):
     return wq.qmat_packed_bytes(c[0], c[1], c[2])
 
 
-def plan_str(res, T):
+def plan_str(res, T, route=0):
     import weight_only_quant_amd as wq
-    p = wq.qmat_get_plan(res.handles[0], T)
+    p = wq.qmat_get_plan(res.handles[0], T, route)
     tail = f" tail_tiles={p.tail_tiles} tail_splits={p.tail_splits}" if p.tail_tiles else ""
     tiles = f" tiles={p.tiles}" if p.tiles > 1 else ""
     return (f"{'valu' if p.route == wq.QMAT_ROUTE_VALU else 'mfma'} depth={p.depth} waves={p.waves} "
@@ -364,6 +364,11 @@ def main():
     ap.add_argument("--eager-only", action="store_true",
                     help="time eager stream launches only (no graph replay), for counter profilers that "
                          "serialize dispatches")
+    ap.add_argument("--profile-lines", default=None,
+                    help="only run these decode lines (name:T,...), --warmup then --steps eager launches "
+                         "each, for counter profilers")
+    ap.add_argument("--route", choices=("auto", "valu", "mfma"), default="auto",
+                    help="small-T route of the --profile-lines launches")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py: this benchmark runs on one GPU only: the product shards by rows with no "
@@ -386,6 +391,20 @@ def main():
         __graft_entry__.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wq.lib()
+    if args.profile_lines:
+        route = {"auto": wq.QMAT_ROUTE_AUTO, "valu": wq.QMAT_ROUTE_VALU, "mfma": wq.QMAT_ROUTE_MFMA}[args.route]
+        for item in args.profile_lines.split(","):
+            pname, pT = item.split(":")
+            pT = int(pT)
+            r = Resident(pname)
+            hs = r.handles
+            for i in range(args.warmup + args.steps):
+                wq.qmat_run_ex(hs[i % len(hs)], r.x[:pT], r.y[:pT], T=pT, route=route)
+            torch.cuda.synchronize()
+            log(f"[bench] profiled {pname} T={pT} route={args.route}: {args.warmup} + {args.steps} launches, "
+                f"plan {plan_str(r, pT, route)}")
+            r.close()
+        return
 
     name, T = PRIMARY
     res = Resident(name)

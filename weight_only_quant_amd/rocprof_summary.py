@@ -7,7 +7,8 @@
     python -m weight_only_quant_amd.rocprof_summary counters <counter_collection.csv> --names A,B,...
         [--kernels <substring>,...] [--out summary.md]
 
-trace:   per (kernel, grid size) dispatch count and mean/median/min duration.
+trace:   per (kernel, grid size) dispatch count, mean/median/min duration and the median
+         start-to-start period of back-to-back dispatches (graph replays: gap included).
 counters: per (kernel, grid) dispatch count and the mean per dispatch of each named counter
          (rocprofv3 --pmc output, one row per dispatch and counter).
 traffic: HBM bytes per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE (KiB per
@@ -59,16 +60,29 @@ def _short(name: str) -> str:
 
 
 def trace_summary(path: str):
+    """Per (kernel, grid, workgroup): dispatch count, mean / median / min duration, and the
+    median start-to-start period of back-to-back dispatches of that kernel (consecutive in the
+    trace with nothing in between: the time per launch of a graph replay, dispatch gap included,
+    the figure an event-timed replay measures)."""
     rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     d = collections.defaultdict(list)
+    period = collections.defaultdict(list)
+    prev = None
     for r in rows:
         grid = r.get("Grid_Size_X") or r.get("Grid_Size")
-        d[(_short(r["Kernel_Name"]), grid, r.get("Workgroup_Size_X") or r.get("Workgroup_Size"))].append(
-            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        key = (_short(r["Kernel_Name"]), grid, r.get("Workgroup_Size_X") or r.get("Workgroup_Size"))
+        start = int(r["Start_Timestamp"])
+        d[key].append(int(r["End_Timestamp"]) - start)
+        if prev is not None and prev[0] == key:
+            period[key].append(start - prev[1])
+        prev = (key, start)
     out = []
     for (k, g, wg), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        pv = period.get((k, g, wg))
         out.append({"kernel": k, "grid": int(g), "workgroup": int(wg), "calls": len(v),
-                    "mean_us": sum(v) / len(v) / 1e3, "median_us": statistics.median(v) / 1e3, "min_us": min(v) / 1e3})
+                    "mean_us": sum(v) / len(v) / 1e3, "median_us": statistics.median(v) / 1e3, "min_us": min(v) / 1e3,
+                    "period_us": statistics.median(pv) / 1e3 if pv else None})
     return out
 
 
@@ -121,10 +135,12 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "trace":
         rows = trace_summary(args.csv)
-        lines = ["| kernel | grid | workgroup | calls | mean us | median us | min us |", "|---|---|---|---|---|---|---|"]
+        lines = ["| kernel | grid | workgroup | calls | mean us | median us | min us | period us |",
+                 "|---|---|---|---|---|---|---|---|"]
         for r in rows:
+            per = f"{r['period_us']:.2f}" if r["period_us"] is not None else ""
             lines.append(f"| {r['kernel']} | {r['grid']} | {r['workgroup']} | {r['calls']} | {r['mean_us']:.2f} | "
-                         f"{r['median_us']:.2f} | {r['min_us']:.2f} |")
+                         f"{r['median_us']:.2f} | {r['min_us']:.2f} | {per} |")
         text = "\n".join(lines) + "\n"
         if args.command:
             text = f"Command: `{args.command}`\n\n" + text
