@@ -14,7 +14,9 @@ the 256 MB Infinity Cache cannot serve them.  Inputs are seeded synthetic data.
 Timing protocol.  Every timed region follows a time-based warm-up on its own workload (the
 GPU runs that workload for a fixed wall time first, whatever --warmup says, so that clocks
 and caches are at steady state after host-side setup).  The headline line times exactly
---steps launches captured in one HIP graph, once.  The other decode lines run in two rounds,
+--steps launches captured in one HIP graph, once (value and ms_per_step, the launch of the
+graph included); its roofline divides the bytes by the kernel's marginal time per launch, from
+a graph of twice the launches timed against it.  The other decode lines run in two rounds,
 the second in reverse order (every pair of lines is timed A-B-B-A), each round timing three
 replays of a graph of at least 50 launches; the reported time is the median over all
 replays, with the per-round medians beside it.  All decode lines run before the epilogue,
@@ -423,6 +425,7 @@ def main():
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / args.steps
         extra_replays = []
+        launch_us = ms * 1e3
     else:
         # exactly --steps launches in one graph: time-based warm-up, --warmup more replays,
         # then one timed replay (the contract's timed region)
@@ -434,6 +437,14 @@ def main():
         # more replays of the same graph, reported beside the line (not the headline value)
         extra_replays = [round(tm.time_once() * 1e3, 3) for _ in range(5)]
         tm.close()
+        # the kernel's own time per launch: a graph of twice the launches against this one
+        # (medians of 6 replays each), which cancels the one-off cost of launching a graph
+        t1 = float(np.median([ms * 1e3] + extra_replays)) * args.steps
+        tm2 = Timed(res, T, 2 * args.steps)
+        tm2.warm(WARM_S)
+        t2 = float(np.median([tm2.time_once() * 1e3 for _ in range(6)])) * 2 * args.steps
+        tm2.close()
+        launch_us = (t2 - t1) / args.steps
     value = ab / (ms * 1e-3) / 1e9
     log(f"[bench] {name} T={T}: {ms * 1e3:.3f} us/call, {value:.1f} GB/s; more replays {extra_replays}")
     out = {
@@ -456,12 +467,18 @@ def main():
                              "--steps launches captured in one HIP graph, one timed replay after a "
                              f"{WARM_HEADLINE_S:.1f} s time-based warm-up",
                    "plan": plan_str(res, T)},
-        # one launch per step: the average launch duration over the timed region is the time
-        # per step (kernel plus the dispatch gap between graph nodes)
-        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"{name}_T{T}"),
-                     "launch_us_mean": round(ms * 1e3, 3), "bytes_per_launch": ab,
-                     "more_replays_us": extra_replays},
+        # one launch per step.  ms_per_step (and value) include the one-off cost of launching
+        # the graph of --steps launches; achieved divides the bytes by the kernel's marginal
+        # time per launch (a 2 x --steps graph against the --steps one, graph replays only),
+        # the duration a kernel trace of this command reports
+        "roofline": {"bound": "hbm", "achieved": round(ab / (launch_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ab / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"{name}_T{T}"),
+                     "launch_us_mean": round(launch_us, 3), "bytes_per_launch": ab,
+                     "per_step_us": round(ms * 1e3, 3), "more_replays_us": extra_replays,
+                     "launch_us_method": "eager launches" if args.eager_only else
+                                         f"(median time of a {2 * args.steps}-launch graph - median time of the "
+                                         f"{args.steps}-launch graph) / {args.steps}"},
         "us_per_call": round(ms * 1e3, 3),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
     }

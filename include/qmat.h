@@ -8,8 +8,8 @@
  *  - Groupwise Q4 / Q5 / Q6 ("Qwen3.8-27B for NInfer on the RTX 3090", section "What is
  *    different from the upstream artifact"): every run of 64 weights along a row (along
  *    K) shares one IEEE binary16 scale; each weight is that scale times a b-bit two's
- *    complement code c in [-2^(b-1), 2^(b-1)-1].  Scales may be negative (that is how a
- *    group reaches the most negative code).
+ *    complement code c in [-2^(b-1), 2^(b-1)-1].  A negative scale is legal; it lets a group
+ *    whose largest weight is positive map it to -2^(b-1), the code without a positive twin.
  *        w[i][j] = fp32(scale[i][j/64]) * code[i][j]            (exact in fp32)
  *    Groupwise Q8 is the same definition with 8-bit codes in [-128, 127]: the cards' format
  *    tables store the token embedding, the upstream output head and several projections so.

@@ -14,8 +14,8 @@
  *  - Groupwise Qb weights ("Qwen3.8-27B for NInfer on the RTX 3090", section
  *    "What is different from the upstream artifact"): each run of 64 weights
  *    along a row has one FP16 scale; a weight is scale times a two's-complement
- *    code; scales may be negative so that a group can use the most negative code
- *    (-8 for 4 bits, -16 for 5 bits).  The upstream encoder there picks
+ *    code; a negative scale is legal (it lets a group map a positive largest weight to
+ *    -2^(b-1): -8 for 4 bits, -16 for 5 bits).  The upstream encoder there picks
  *    scale = absmax / qmax and the nearest code.  The same cards store the token
  *    embedding, the upstream output head and several projections as groupwise Q8
  *    (the "Token embedding / output head" and "Attention ... projections" rows of
@@ -350,11 +350,12 @@ int qo_rtn_encode(int bits, int64_t ngroups, const double *w, int8_t *codes, uin
 /* ---------------------------------------------------------------- grouped search encoder */
 
 /* The "grouped_search" encoder of "Qwen3.8-27B for NInfer on the RTX 3090" ("What is
- * different from the upstream artifact"): each group's FP16 scale is chosen among 50
- * candidates as the one with the least importance-weighted squared error
- * sum_j h_j (w_j - s c_j)^2, where h_j is the importance of input channel j (the mean squared
- * activation of that channel: an imatrix); scales may be negative, which lets a group use the
- * most negative code.
+ * different from the upstream artifact").  For each 64-weight group a fixed set of 50 FP16
+ * scales is tried, and the kept one minimises E(s) = sum_j h_j (w_j - s c_j)^2, c_j being w_j/s
+ * rounded and clamped to the code range and h_j >= 0 a per-input-channel weight (the page
+ * derives it from the channel's mean squared activation).  The set holds both signs of every
+ * magnitude, so that a group whose largest weight is positive can
+ * map it to -2^(b-1), the code without a positive twin.
  *
  * The page does not list the candidates.  Reading: with a = max_j |w_j|, the 25 magnitudes
  * a / (qmax + i/24), i = 0..24, run from upstream's a/qmax (the group's largest weight lands

@@ -3,12 +3,14 @@
 //  - RTN (upstream's encoder, "Qwen3.8-27B for NInfer on the RTX 3090", "What is different from
 //    the upstream artifact"): per 64-weight group, scale = max|w| / qmax stored as FP16, codes
 //    the nearest integers to w / scale.
-//  - Grouped search (the same section: that artifact's encoder): each group's FP16 scale is the
-//    one of 50 candidates with the least importance-weighted squared error
-//    sum_j h_j (w_j - s c_j)^2, h_j the importance of input channel j; scales may be negative
-//    so that a group can use the most negative code.  The candidates (the page does not list
-//    them) are +-a / (qmax + i/24), i = 0..24, a = max|w|: from upstream's a/qmax to the full
-//    range a/2^(b-1), each magnitude with both signs, in the order +m0, -m0, +m1, -m1, ...
+//  - Grouped search (the same section: that artifact's encoder): 50 FP16 scales are tried per
+//    group and the one with the smallest E(s) = sum_j h_j (w_j - s c_j)^2 is kept, c_j the
+//    rounded, clamped code of w_j / s and h_j >= 0 a weight per input channel.  Both signs of
+//    each magnitude are tried (with a negative scale a group whose largest weight is positive
+//    maps it to -2^(b-1), the code without a positive twin).
+//    The magnitudes (the page does not list them) are a / (qmax + i/24), i = 0..24,
+//    a = max|w|: from upstream's a/qmax to the full range a/2^(b-1), tried in the order
+//    +m0, -m0, +m1, -m1, ...
 //  - Row-scaled FP8 ("Qwen3.8-27B NVFP4 for NInfer", "Artifact": a tensor encoded locally as
 //    row-scaled FP8): r = fl32(max|w| / 448), bytes the nearest E4M3 values (even ties,
 //    saturating at +-448) to fl32(w / r).
