@@ -107,8 +107,8 @@ __device__ __forceinline__ float ordered_sum(int S, Load load)
 // partner's value, adds it (fp32 addition is commutative, so the sum has the same bits
 // whichever side arrives second), clears the word for the next call and carries the sum to the
 // next level.  Whoever completes the root writes y.  Every element meets independently: no
-// counters, barriers or fences, one memory round trip per tree level, and the same bits on
-// every run of the same plan.
+// counters, barriers or fences, one memory round trip per tree level (a thread with several
+// elements sends two up together), and the same bits on every run of the same plan.
 template <typename ForEach>
 __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *red, ForEach for_each)
 {
@@ -137,21 +137,21 @@ __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *
     // the tile's node words: one level slot [node][t][row of the region] per tree node
     uint64_t *nodes = a.nodes + s.wsoff;
     const int64_t nstride = (int64_t)a.T * s.wsld;
-    for (int e = threadIdx.x; e < n; e += nthr) {
-        const int t = e / kTileRows, r = e - t * kTileRows;
-        if (row0 + r >= a.M) continue;  // padding rows: skipped by every split alike
+    if (n <= nthr) {
+        // at most one element per thread
+        const int e = threadIdx.x, t = e / kTileRows, r = e - t * kTileRows;
+        if (e >= n || row0 + r >= a.M) return;  // padding rows: skipped by every split alike
         float v = red[e];
         for (int w = 1; w < s.nw; ++w) v += red[w * n + e];
         const int64_t wd = (int64_t)t * s.wsld + s.wsrow + r;
         int p = s.sp, m = s.S;
         int64_t base = 0;
-        bool done = false;
         while (m > 1) {
             if ((p ^ 1) < m) {
                 uint64_t *slot = nodes + (base + (p >> 1)) * nstride + wd;
                 const uint64_t old = __hip_atomic_exchange(slot, (1ull << 32) | __builtin_bit_cast(uint32_t, v),
                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if ((old >> 32) == 0) { done = true; break; }
+                if ((old >> 32) == 0) return;
                 v = __builtin_bit_cast(float, (uint32_t)old) + v;
                 __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -159,7 +159,65 @@ __device__ __forceinline__ void finish(const RunArgs &a, const Slice &s, float *
             p >>= 1;
             m = (m + 1) >> 1;
         }
-        if (!done) a.y[(int64_t)t * a.ldy + row0 + r] = v;
+        a.y[(int64_t)t * a.ldy + row0 + r] = v;
+        return;
+    }
+    // more elements than threads (T > 8 with 8 waves): a thread takes them two at a time, e and
+    // e + nthr, and both go up the tree together (both exchanges of a level in flight at once:
+    // one round trip per level for the pair)
+    for (int e0 = threadIdx.x; e0 < n; e0 += 2 * nthr) {
+        const int e1 = e0 + nthr;
+        const int t0 = e0 / kTileRows, r0 = e0 - t0 * kTileRows;
+        const int t1 = e1 / kTileRows, r1 = e1 - t1 * kTileRows;
+        bool on0 = row0 + r0 < a.M;
+        bool on1 = e1 < n && row0 + r1 < a.M;
+        float v0 = 0.f, v1 = 0.f;
+        if (on0) {
+            v0 = red[e0];
+            for (int w = 1; w < s.nw; ++w) v0 += red[w * n + e0];
+        }
+        if (on1) {
+            v1 = red[e1];
+            for (int w = 1; w < s.nw; ++w) v1 += red[w * n + e1];
+        }
+        const int64_t wd0 = (int64_t)t0 * s.wsld + s.wsrow + r0;
+        const int64_t wd1 = on1 ? (int64_t)t1 * s.wsld + s.wsrow + r1 : wd0;
+        int p = s.sp, m = s.S;
+        int64_t base = 0;
+        while (m > 1) {
+            if ((p ^ 1) < m) {
+                uint64_t *slot0 = nodes + (base + (p >> 1)) * nstride + wd0;
+                uint64_t *slot1 = nodes + (base + (p >> 1)) * nstride + wd1;
+                uint64_t o0 = 0, o1 = 0;
+                if (on0)
+                    o0 = __hip_atomic_exchange(slot0, (1ull << 32) | __builtin_bit_cast(uint32_t, v0), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                if (on1)
+                    o1 = __hip_atomic_exchange(slot1, (1ull << 32) | __builtin_bit_cast(uint32_t, v1), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                if (on0) {
+                    if ((o0 >> 32) == 0) {
+                        on0 = false;
+                    } else {
+                        v0 = __builtin_bit_cast(float, (uint32_t)o0) + v0;
+                        __hip_atomic_store(slot0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+                if (on1) {
+                    if ((o1 >> 32) == 0) {
+                        on1 = false;
+                    } else {
+                        v1 = __builtin_bit_cast(float, (uint32_t)o1) + v1;
+                        __hip_atomic_store(slot1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+            base += m >> 1;
+            p >>= 1;
+            m = (m + 1) >> 1;
+        }
+        if (on0) a.y[(int64_t)t0 * a.ldy + row0 + r0] = v0;
+        if (on1) a.y[(int64_t)t1 * a.ldy + row0 + r1] = v1;
     }
 }
 
