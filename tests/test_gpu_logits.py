@@ -347,3 +347,29 @@ def test_run_logits_on_a_split_plan_and_errors():
     wq.qmat_logits_destroy(e2)
     wq.qmat_logits_destroy(e)
     qm.close()
+
+
+def test_candidate_overflow_paths():
+    """Logits that overflow both kernels' candidate buffers: every block of 2048 rows holds 63
+    rows of one equal top value, so at k = 64 the block pass keeps more than 256 candidates
+    (its sorting-network path) and the merge more than 1024 (its own sorting-network path).
+    The top-k must still equal the oracle's sort, ties by row."""
+    M, T, k = 40 * 2048, 2, 64  # 40 whole blocks of 2048 rows
+    rng = np.random.default_rng(4)
+    y = rng.standard_normal((T, M)).astype(np.float32)
+    for t in range(T):
+        for b0 in range(0, M, 2048):
+            n = min(2048, M - b0)
+            rows = b0 + rng.choice(n, size=min(63, n), replace=False)
+            y[t, rows] = 100.0 + t
+    e = wq.qmat_logits_create(M, T, k)
+    say("logits candidate overflow")
+    lse, vals, ids = _run(e, y, k)
+    rv, ri = oracle.topk(y, k)
+    assert np.array_equal(vals.astype(np.float64), rv) and np.array_equal(ids.astype(np.int64), ri)
+    ref = oracle.logsumexp(y)
+    assert np.all(np.abs(lse.astype(np.float64) - ref) <= _lse_tol(ref))
+    lse2, vals2, ids2 = _run(e, y, 20)
+    rv, ri = oracle.topk(y, 20)
+    assert np.array_equal(vals2.astype(np.float64), rv) and np.array_equal(ids2.astype(np.int64), ri)
+    wq.qmat_logits_destroy(e)
