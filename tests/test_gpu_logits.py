@@ -373,3 +373,18 @@ def test_candidate_overflow_paths():
     rv, ri = oracle.topk(y, 20)
     assert np.array_equal(vals2.astype(np.float64), rv) and np.array_equal(ids2.astype(np.int64), ri)
     wq.qmat_logits_destroy(e)
+
+
+def test_many_rounds_per_block():
+    """4M rows: 512 blocks of 8192 rows, four rounds of loads per block (each lane's running
+    sum carried across rounds); top-k and log-sum-exp against the oracle as above."""
+    M, T, k = 4 << 20, 2, 20
+    e = wq.qmat_logits_create(M, T, k)
+    say("logits many rounds per block")
+    y = qi.logits(T, M, seed=9)
+    lse, vals, ids = _run(e, y, k)
+    ref = oracle.logsumexp(y)
+    assert np.all(np.abs(lse.astype(np.float64) - ref) <= _lse_tol(ref)), (lse, ref)
+    rv, ri = oracle.topk(y, k)
+    assert np.array_equal(vals.astype(np.float64), rv) and np.array_equal(ids.astype(np.int64), ri)
+    wq.qmat_logits_destroy(e)

@@ -295,7 +295,9 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
     const int r1 = r0 + a.rpb < a.M ? r0 + a.rpb : a.M;
     if (threadIdx.x == 0) s_count[0] = 0;
 
-    float m = -INFINITY, s = 0.f;
+    float m = -INFINITY;  // the lane's running max
+    double s = 0.0;       // sum of exp(y - m) over the lane's rows: in double, so that blocks of
+                          // many rounds (large M) add no fp32 rounding per round
     int ntop = 0;        // entries in s_top, the block's best keys so far (best first)
     uint64_t theta = 0;  // the k-th of them (0 while there are fewer)
     int rr = 0;  // round index mod 3
@@ -322,11 +324,11 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
         for (int j = 1; j < kPerLane; ++j) mr = fmaxf(mr, v[j]);
         if (mr > -INFINITY) {
             const float mn = fmaxf(m, mr);
-            float acc = m == -INFINITY ? 0.f : s * exp_nonpos(m - mn);
+            float acc = 0.f;
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j) acc += exp_nonpos(v[j] - mn);
+            s = (m == -INFINITY ? 0.0 : s * (double)exp_nonpos(m - mn)) + (double)acc;
             m = mn;
-            s = acc;
         }
         if (k == 0) continue;
         uint64_t key[kPerLane];
@@ -390,10 +392,11 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
     }
 
     // block partial: (max, sum) of the 4 waves, the k best keys and the k-th
-    wave_lse(m, s);
+    float sf = (float)s;
+    wave_lse(m, sf);
     if (lane == 0) {
         s_m[w] = m;
-        s_s[w] = s;
+        s_s[w] = sf;
     }
     __syncthreads();
     if (w == 0) {
