@@ -221,19 +221,28 @@ template <typename F> __device__ __forceinline__ void wave_lse(F &m, F &s)
 
 // ---------------------------------------------------------------------------- rank selection
 
-// The number of keys in s[0..n) above `key` (LDS broadcast reads, two keys each, eight in flight:
-// the compares are independent, unlike the steps of a sort).
+// The number of keys in s[0..n) above `key`: LDS broadcast reads of two keys each, eight in
+// flight, counted into four independent sums (the compares do not wait on each other, unlike
+// the steps of a sort, and the sums do not form one long chain).
 __device__ __forceinline__ int rank_in(const uint64_t *s, int n, uint64_t key)
 {
     const ulonglong2 *p = reinterpret_cast<const ulonglong2 *>(s);
-    int r = 0;
-#pragma unroll 8
-    for (int i = 0; i < n / 2; ++i) {
-        const ulonglong2 q = p[i];
-        r += (int)(q.x > key) + (int)(q.y > key);
+    const int np = n >> 1;
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0, i = 0;
+#pragma unroll 2
+    for (; i + 4 <= np; i += 4) {
+        const ulonglong2 q0 = p[i], q1 = p[i + 1], q2 = p[i + 2], q3 = p[i + 3];
+        r0 += (int)(q0.x > key) + (int)(q0.y > key);
+        r1 += (int)(q1.x > key) + (int)(q1.y > key);
+        r2 += (int)(q2.x > key) + (int)(q2.y > key);
+        r3 += (int)(q3.x > key) + (int)(q3.y > key);
     }
-    if (n & 1) r += (int)(s[n - 1] > key);
-    return r;
+    for (; i < np; ++i) {
+        const ulonglong2 q = p[i];
+        r0 += (int)(q.x > key) + (int)(q.y > key);
+    }
+    if (n & 1) r0 += (int)(s[n - 1] > key);
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Each thread appends its keys at or above th (and non-zero) to s_cand at offset `at0` +
