@@ -602,7 +602,7 @@ struct qmat_logits {
     int64_t M;
     int max_T, max_k;
     int B;                // row blocks per token
-    float2 *part_lse;     // [max_T][B] block states
+    float2 *part_lse;     // [max_T][B][kLogitsWaves] wave states
     uint64_t *part_list;  // [max_T][B][max(max_k, 1)] block lists
     uint64_t *part_kth;   // [max_T][B] blocks' k-th keys
     float *ybuf;          // [max_T][M] logits for qmat_run_logits without y
@@ -633,7 +633,7 @@ int qmat_logits_create(qmat_logits_t *e, int64_t M, int max_T, int max_k)
     }
     h->B = logits_blocks(M);
     const size_t nt = (size_t)max_T;
-    if (hipMalloc(&h->part_lse, nt * h->B * sizeof(float2)) != hipSuccess ||
+    if (hipMalloc(&h->part_lse, nt * h->B * kLogitsWaves * sizeof(float2)) != hipSuccess ||
         hipMalloc(&h->part_list, nt * h->B * (max_k > 0 ? max_k : 1) * sizeof(uint64_t)) != hipSuccess ||
         hipMalloc(&h->part_kth, nt * h->B * sizeof(uint64_t)) != hipSuccess ||
         hipMalloc(&h->ybuf, nt * M * sizeof(float)) != hipSuccess) {

@@ -8,6 +8,7 @@
 namespace qmatk {
 
 constexpr int kMaxBlocks = 512;  // row blocks per token at most
+constexpr int kLogitsWaves = 4;  // waves per block of the first kernel, one (max, sum) state each
 
 struct LogitsArgs {
     const float *y;         // fp32 logits, row t at y + t * ldy, M entries
@@ -17,7 +18,7 @@ struct LogitsArgs {
     float *lse;             // [T] or null
     float *vals;            // [T][k]
     int32_t *ids;           // [T][k]
-    float2 *part_lse;       // per (token, block): (max, sum of exp(y - max))   [T][B]
+    float2 *part_lse;       // per (token, block, wave): (max, sum of exp(y - max))   [T][B][kLogitsWaves]
     uint64_t *part_list;    // per (token, block): the k best keys, best first  [T][B][k]
     uint64_t *part_kth;     // per (token, block): the k-th best key (0: none)  [T][B]
     int B, rpb;             // blocks per token (<= kMaxBlocks), rows per block (B * rpb >= M)
@@ -37,7 +38,7 @@ inline int logits_blocks(int64_t M)
 hipError_t launch_logits(const LogitsArgs &a, hipStream_t stream);
 
 struct MergeArgs {
-    const float2 *lse_part;  // [T][G]
+    const float2 *lse_part;  // [T][G][kLogitsWaves]
     const uint64_t *kth;     // [T][G]
     const uint64_t *list;    // [T][G][k]
     int G, k;

@@ -15,22 +15,23 @@
 //
 // Kernel 1, grid (B, T), 4 waves: block b of token t streams rows [b*rpb, (b+1)*rpb) in rounds
 // of 8 rows per lane, the next round's loads in flight while one round is processed.  Each lane
-// keeps an online (max, sum of exp(y - max)).  For the top k the block keeps its k best keys in
-// wave 0 (sorted across the lanes, lane i the i-th best) and a threshold theta, the k-th of them:
-// a round's keys below theta cannot reach the top k, and usually none or a few are above it, so
-// they are collected in LDS and one sort and merge takes them.  The first round seeds theta
-// with the k-th best of the block's lane maxima (k distinct rows reach it): sorting the lane
-// maxima costs one sort per wave and a merge of the four, and it leaves about k candidates
-// where an empty list would take every key of the round.  Rounds with more than 64 candidates
-// (many equal values, adversarial orders) take them in every wave and merge the waves' lists.
-// The block writes (max, sum), its k best keys and its k-th key.
+// keeps an online (max, sum of exp(y - max)), the sum across rounds in double.  For the top k
+// the block keeps its k best keys in LDS and theta, the k-th of them: a key below theta cannot
+// reach the top k.  The first round seeds theta with the largest of the waves' k-th best lane
+// maxima (k distinct rows reach it).  Each round the list and the keys at or above theta
+// (usually a few dozen) go to LDS, and each candidate's rank among them, counted from LDS
+// broadcast reads, is its place in the new list: independent compares instead of the dependent
+// steps of a sort.  Rounds with more than 256 candidates (adversarial orders) take them with
+// wave sorting networks and a merge of the waves' lists.  Each wave writes its (max, sum); the
+// block writes its k best keys and its k-th key.
 //
-// Kernel 2, one block per token: the largest k-th key over the blocks, tau, is reached by k
-// rows, so every key of the token's top k is at or above it, and only keys at or above tau can
-// contribute; every block's list is loaded in one round of loads, the keys at or above tau
-// (usually about k) are collected and sorted once.  The block states combine in double in a
-// fixed order.  The candidate set is exact and the order total, so the output is deterministic:
-// no atomics on global memory, nothing to reset between calls.
+// Kernel 2, one block per token, after kernel 1 (the kernel boundary makes its stores visible):
+// tau is the larger of two keys that k distinct rows reach, the largest k-th key of a block and
+// the k-th best of the blocks' best keys, so every key of the token's top k is at or above it.
+// Every block's list is loaded in one round of loads; the keys at or above tau (usually about
+// k) are ranked the same way.  The waves' states combine in double in a fixed order.  The
+// candidate set is exact and the order total, so the output is deterministic: no atomics on
+// global memory, nothing to reset between calls.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -212,10 +213,10 @@ template <typename F> __device__ __forceinline__ F wave_sum(F v)
 // The log-sum-exp state (max, sum of exp(v - max)) of the whole wave from the lanes' states: the
 // wave max, one exponential per lane to rescale its sum, then a sum over the lanes, in a fixed
 // order.  Every lane ends with the wave's state.
-template <typename F> __device__ __forceinline__ void wave_lse(F &m, F &s)
+__device__ __forceinline__ void wave_lse(float &m, float &s)
 {
-    const F mx = wave_max(m);
-    s = wave_sum(m == -INFINITY ? F(0) : s * exp(m - mx));
+    const float mx = wave_max(m);
+    s = wave_sum(m == -INFINITY ? 0.f : s * exp_nonpos(m - mx));
     m = mx;
 }
 
@@ -267,7 +268,7 @@ __device__ __forceinline__ void append_at_or_above(const uint64_t (&key)[N], uin
 
 // ---------------------------------------------------------------------------- kernel 1
 
-constexpr int kWaves = 4;                    // waves per block
+constexpr int kWaves = kLogitsWaves;         // waves per block
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPerLane = 8;                  // rows per lane per round
 constexpr int kRound = kPerLane * kThreads;  // rows per round
@@ -293,7 +294,6 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
     __shared__ uint64_t s_top[64];
     __shared__ __align__(16) uint64_t s_lm[kWaves][64];
     __shared__ uint64_t s_thw[kWaves];
-    __shared__ float s_m[kWaves], s_s[kWaves];
     __shared__ int s_count[3];  // round r counts in s_count[r % 3]
     __shared__ int s_ntop;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -400,23 +400,15 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
         theta = ntop == k ? s_top[k - 1] : 0ull;
     }
 
-    // block partial: (max, sum) of the 4 waves, the k best keys and the k-th
+    // block partial: each wave's (max, sum), the k best keys and the k-th (s_top was last
+    // written before a barrier)
     float sf = (float)s;
     wave_lse(m, sf);
-    if (lane == 0) {
-        s_m[w] = m;
-        s_s[w] = sf;
-    }
-    __syncthreads();
-    if (w == 0) {
-        float mm = lane < kWaves ? s_m[lane] : -INFINITY, ss = lane < kWaves ? s_s[lane] : 0.f;
-        wave_lse(mm, ss);
-        const int64_t tb = (int64_t)t * a.B + b;
-        if (lane == 0) a.part_lse[tb] = make_float2(mm, ss);
-        if (k > 0) {
-            if (lane < k) a.part_list[tb * k + lane] = lane < ntop ? s_top[lane] : 0ull;
-            if (lane == 0) a.part_kth[tb] = ntop == k ? s_top[k - 1] : 0ull;
-        }
+    const int64_t tb = (int64_t)t * a.B + b;
+    if (lane == 0) a.part_lse[tb * kWaves + w] = make_float2(m, sf);
+    if (w == 0 && k > 0) {
+        if (lane < k) a.part_list[tb * k + lane] = lane < ntop ? s_top[lane] : 0ull;
+        if (lane == 0) a.part_kth[tb] = ntop == k ? s_top[k - 1] : 0ull;
     }
 }
 
@@ -425,7 +417,8 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
 constexpr int kMWaves = 4;
 constexpr int kMThreads = 64 * kMWaves;
 constexpr int kMPer = 16;                               // list entries per thread per round of loads
-constexpr int kMPerBlock = kMaxBlocks / kMThreads;      // blocks (states, heads) per thread at most
+constexpr int kMPerBlock = kMaxBlocks / kMThreads;      // blocks (heads, k-th keys) per thread at most
+constexpr int kMPerState = kMPerBlock * kWaves;         // wave states per thread at most
 constexpr int kMCand = 1024;                            // candidates ranked at once
 
 __global__ __launch_bounds__(kMThreads) void logits_merge_kernel(MergeArgs a)
@@ -452,13 +445,18 @@ __global__ __launch_bounds__(kMThreads) void logits_merge_kernel(MergeArgs a)
 
     // every load at once: the block states, k-th keys and best keys (thread i0 takes blocks
     // i0, i0 + 256), and the first kMPer entries of the lists per thread
-    float2 p[kMPerBlock];
+    float2 p[kMPerState];
     uint64_t kth = 0, head[kMPerBlock];
     const uint64_t *lists = a.list + (int64_t)t * n;
+    const int ns = G * kWaves;
+#pragma unroll
+    for (int q = 0; q < kMPerState; ++q) {
+        const int i = i0 + kMThreads * q;
+        p[q] = i < ns ? a.lse_part[(int64_t)t * ns + i] : make_float2(-INFINITY, 0.f);
+    }
 #pragma unroll
     for (int q = 0; q < kMPerBlock; ++q) {
         const int i = i0 + kMThreads * q;
-        p[q] = i < G ? a.lse_part[(int64_t)t * G + i] : make_float2(-INFINITY, 0.f);
         const uint64_t kq = k > 0 && i < G ? a.kth[(int64_t)t * G + i] : 0ull;
         kth = kq > kth ? kq : kth;
         head[q] = k > 0 && i < G ? lists[(int64_t)i * k] : 0ull;
@@ -474,7 +472,7 @@ __global__ __launch_bounds__(kMThreads) void logits_merge_kernel(MergeArgs a)
     // a difference, summed in double in a fixed order)
     float mt = p[0].x;
 #pragma unroll
-    for (int q = 1; q < kMPerBlock; ++q) mt = fmaxf(mt, p[q].x);
+    for (int q = 1; q < kMPerState; ++q) mt = fmaxf(mt, p[q].x);
     mt = wave_max(mt);
     kth = wave_max(kth);
     if (lane == 0) {
@@ -494,27 +492,32 @@ __global__ __launch_bounds__(kMThreads) void logits_merge_kernel(MergeArgs a)
     }
     double term = 0.0;
 #pragma unroll
-    for (int q = 0; q < kMPerBlock; ++q)
+    for (int q = 0; q < kMPerState; ++q)
         term += p[q].x == -INFINITY ? 0.0 : (double)p[q].y * (double)expf(p[q].x - mstar);
     const double sw = wave_sum(term);
     if (lane == 0) s_sum[w] = sw;
 
     if (k > 0) {
         // tau: the larger of two keys that k distinct rows reach, the largest k-th entry of a
-        // list and the k-th best of the lists' best keys (tight when the lists are many); the
-        // latter from the best keys that are among the k best of their group of 64
+        // list and the k-th best of the lists' best keys (tight when the lists are many): up
+        // to 256 lists each best key is ranked among all of them; beyond, among its group of
+        // 64 first, and the group winners among each other
+        if (G <= kMThreads) {
+            if (i0 < G && head[0] != 0 && rank_in(s_h, G, head[0]) == k - 1) s_th = head[0];
+        } else {
 #pragma unroll
-        for (int q = 0; q < kMPerBlock; ++q) {
-            const int i = i0 + kMThreads * q;
-            if (i < G && head[q] != 0) {
-                const int g0 = i & ~63, gn = G - g0 < 64 ? G - g0 : 64;
-                if (rank_in(s_h + g0, gn, head[q]) < k) s_hc[atomicAdd(&s_hcount, 1)] = head[q];
+            for (int q = 0; q < kMPerBlock; ++q) {
+                const int i = i0 + kMThreads * q;
+                if (i < G && head[q] != 0) {
+                    const int g0 = i & ~63, gn = G - g0 < 64 ? G - g0 : 64;
+                    if (rank_in(s_h + g0, gn, head[q]) < k) s_hc[atomicAdd(&s_hcount, 1)] = head[q];
+                }
             }
+            __syncthreads();
+            const int Ch = s_hcount;
+            for (int c = i0; c < Ch; c += kMThreads)
+                if (rank_in(s_hc, Ch, s_hc[c]) == k - 1) s_th = s_hc[c];
         }
-        __syncthreads();
-        const int Ch = s_hcount;
-        for (int c = i0; c < Ch; c += kMThreads)
-            if (rank_in(s_hc, Ch, s_hc[c]) == k - 1) s_th = s_hc[c];
         __syncthreads();
         tau = s_th > tau ? s_th : tau;
         // candidates: the entries at or above tau
