@@ -34,11 +34,13 @@ struct Plan {
 // MFMA kernel.
 //  - Matrices of at least 2048 row tiles: one tile per workgroup, never split; 4 waves share a
 //    tile's k units at T = 1 (a single token leaves registers for two units in flight), 1 wave
-//    otherwise.  From 10 tokens (9 for the 8-bit formats) a wave streams two neighbouring
-//    tiles with one unit in flight, loading each activation fragment once for both (measured
-//    on 248320 x 5120 heads: 1-3% faster at T = 10-11, 2-5% at T = 12, 5-14% at T = 16, and for
-//    FP8 and Q8 2% at T = 9; up to 7% slower at small T, where the fragment loads are cheaper
-//    than the halved number of units in flight per tile).
+//    otherwise.  From a format's crossover a wave streams two neighbouring tiles with one unit
+//    in flight, loading each activation fragment once for both.  With at least 3072 tiles:
+//    FP8 from T = 2, Q8 from 6, Q5 from 9, Q4 and Q6 from 10 (measured on 248320 x 5120 heads,
+//    pair against one tile per wave: FP8 1-3% faster at T = 2-8, Q8 1-2% at T = 6-8, Q5 2% at
+//    T = 9; Q4 and Q6 0.3-9% slower up to T = 9; every format slower at T = 1; above the
+//    crossovers 1-14% faster, the most at T = 16).  Fewer tiles (the 131072-row proposal head:
+//    pairs 1.6% slower at T = 8): the 8-bit formats from T = 9, the others from 10.
 //  - At least one tile per compute unit: 4 waves per workgroup, two units in flight up to T = 4
 //    and one above (from T = 12 the multi-token accumulators of a two-unit ring leave too few
 //    resident waves: 25-30% slower; at T = 2-4 the ring is 6-7% faster, T = 6-8 tie).  When
@@ -65,7 +67,15 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
         Plan p{route, 2, 1, 1, 0, 1};
         if (NT >= 2048) {
             p.waves = Tl == 1 ? 4 : 1;
-            if (Tl >= (fmt == kFmtFp8 || fmt == kFmtQ8 ? 9 : 10)) {
+            // two tiles per wave from the token count where sharing the activation fragments
+            // outweighs having half as many workgroups (sweeps on 248320 x 5120 heads; a
+            // 2048-tile head keeps more workgroups up to T = 8)
+            const bool many = NT >= 3072;
+            const int pair_from = fmt == kFmtFp8 ? (many ? 2 : 9)
+                                  : fmt == kFmtQ8 ? (many ? 6 : 9)
+                                  : fmt == 5      ? (many ? 9 : 10)
+                                                  : 10;
+            if (Tl >= pair_from) {
                 p.tiles = 2;
                 p.depth = 1;
             }

@@ -536,8 +536,7 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
 // split: the S workgroups of pair p own tiles 2p and 2p + 1 (the second absent for the last
 // pair of an odd tile count; its loads then repeat the first tile and nothing is stored for
 // it).  Per tile the arithmetic, the wave and k split of its units and the reduction (through
-// that tile's own workspace rows and arrival counter) are those of mfma_kernel, so both
-// kernels give the same bits.
+// that tile's own tree words) are those of mfma_kernel, so both kernels give the same bits.
 template <int NB> struct PairUnit {
     u32x4_t c[2][NB];
     u32x4_t sc[2];
