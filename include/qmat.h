@@ -268,15 +268,16 @@ void qmat_destroy(qmat_t handle);
  *   top_ids[t][]  = their rows i, or index[i] when an index map is given (the indexed 131,072-row
  *                   proposal head whose rows stand for vocabulary ids; the candidate top-k reads
  *                   either it or the full head: "Qwen3.8-27B for NInfer on the RTX 3090", run
- *                   notes).  Slots beyond M hold (-inf, -1).
- * One pass over y; the result is deterministic.  y must be finite. */
+ *                   notes).  Slots beyond M hold (-inf, -1).  -0 is returned as +0.
+ * Two kernels: one pass over y by row blocks, then one merge per token; the result is
+ * deterministic.  y must be finite. */
 typedef struct qmat_logits *qmat_logits_t;
 
 /* An epilogue handle for M rows, up to max_T tokens (1..16) and top-k up to max_k (0..64).  It
- * owns a device workspace, allocated here: per token and row block (up to 512 blocks of about
- * 4096 rows) a (max, sum) state and max_k (value, row) pairs, and max_T * M floats of logits for
- * qmat_run_logits called without y.  Nothing in it needs resetting between calls; calls sharing
- * a handle must be ordered.
+ * owns a device workspace, allocated here: per token and row block (blocks of 2048 rows, at most
+ * 512: beyond 2^20 rows the blocks grow) four (max, sum) states, max_k (value, row) keys and the
+ * k-th key, and max_T * M floats of logits for qmat_run_logits called without y.  Nothing in it
+ * needs resetting between calls; calls sharing a handle must be ordered.
  * Errors: QMAT_EINVAL (null pointer), QMAT_ESHAPE (M outside [1, 2^30], max_T, max_k),
  * QMAT_ENOMEM, QMAT_EHIP. */
 int qmat_logits_create(qmat_logits_t *handle, int64_t M, int max_T, int max_k);
