@@ -19,8 +19,9 @@ graph included); its roofline divides the bytes by the kernel's marginal time pe
 a graph of twice the launches timed against it.  The other decode lines run in two rounds,
 the second in reverse order (every pair of lines is timed A-B-B-A), each round timing three
 replays of a graph of at least 50 launches; the reported time is the median over all
-replays, with the per-round medians beside it.  All decode lines run before the epilogue,
-prefill and read-probe lines.
+replays, with the per-round medians beside it.  Every decode line also reports the event time
+of single eager launches, each alone on an idle stream (median, 10th and 90th percentile of
+40).  All decode lines run before the epilogue, prefill and read-probe lines.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -158,15 +159,44 @@ def plan_str(res, T, route=0):
             f"splits={p.splits}{tail}{tiles}")
 
 
-def line(res, T, us_list, per_round):
-    """A decode line from per-launch times (µs) of all timed replays."""
+def line(res, T, us_list, per_round, single):
+    """A decode line from per-launch times (µs) of all timed replays, with the single-launch
+    event times beside it."""
     wl = res.wl
     ab = alg_bytes(wl.fmt, wl.M, wl.K, T)
     us = float(np.median(us_list))
     return {"us_per_call": round(us, 3), "us_min": round(min(us_list), 3), "us_max": round(max(us_list), 3),
             "us_round_medians": [round(v, 3) for v in per_round], "timed_replays": len(us_list),
             "GBps": round(ab / us / 1e3, 1), "pct_hbm_peak": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 2),
-            "bytes": ab, "plan": plan_str(res, T)}
+            "bytes": ab, "plan": plan_str(res, T), "single_launch_us": single}
+
+
+SINGLE_WARM = 20   # eager launches before the single-launch timings of a line
+SINGLE_N = 40      # single launches timed per line
+
+
+def single_launch(res, T):
+    """Each of SINGLE_N eager launches alone on an idle stream, bracketed by events and
+    synchronized after: median, 10th and 90th percentile of the event time (µs).  This is the
+    latency of one call on its own (dispatch and ramp-up included), beside the back-to-back
+    average of the graph replays."""
+    import torch
+    import weight_only_quant_amd as wq
+    hs, x, y = res.handles, res.x[:T], res.y[:T]
+    stream = torch.cuda.current_stream()
+    for i in range(SINGLE_WARM):
+        wq.qmat_run(hs[i % len(hs)], x, y, T=T)
+    torch.cuda.synchronize()
+    us = []
+    for i in range(SINGLE_N):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        wq.qmat_run(hs[(SINGLE_WARM + i) % len(hs)], x, y, T=T)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) * 1e3)
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"median": round(float(p50), 3), "p10": round(float(p10), 3), "p90": round(float(p90), 3), "n": SINGLE_N}
 
 
 def measure_decode(lines, steps):
@@ -188,7 +218,11 @@ def measure_decode(lines, steps):
             times[i] += us
             rounds[i].append(float(np.median(us)))
             log(f"[bench] round {r} {res.name} T={T}: {np.median(us):.3f} us/call")
-    return {i: line(lines[i][0], lines[i][1], times[i], rounds[i]) for i in range(len(lines))}
+    single = {}
+    for i, (res, T) in enumerate(lines):
+        single[i] = single_launch(res, T)
+        log(f"[bench] single launch {res.name} T={T}: {single[i]}")
+    return {i: line(lines[i][0], lines[i][1], times[i], rounds[i], single[i]) for i in range(len(lines))}
 
 
 def measure_epilogue(res, T, k, warm_s=WARM_S, n=MIN_CALLS, with_product=False):
@@ -481,6 +515,7 @@ def main():
                                          f"{args.steps}-launch graph) / {args.steps}"},
         "us_per_call": round(ms * 1e3, 3),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "single_launch_us": single_launch(res, T),
     }
     extra = {}
     if args.eager_only:

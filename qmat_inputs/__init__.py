@@ -128,6 +128,10 @@ CONFIGS: Dict[str, tuple] = {
     # the 131,072-row proposal head kept in the upstream 8-bit encoding, whose rows stand for
     # vocabulary ids through an index map
     "q8_proposal_head_131072x5120": (Q8, 131072, 5120, [1, 8, 16], 0.0005),
+    # one GPU's share of an 8-way split: the Q6 head cut into row slices (248320 / 8 rows each)
+    # and the Q5 down projection cut along K (17408 / 8 inputs each, partial sums added after)
+    "q6_head_shard_31040x5120": (Q6, 31040, 5120, [1, 8], 0.005),
+    "q5_down_kshard_5120x2176": (Q5, 5120, 2176, [1, 4], 0.01),
 }
 
 

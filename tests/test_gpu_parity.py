@@ -278,6 +278,31 @@ def test_pair_plan_on_head_sized_matrix(fmt, T, NT):
     qm.close()
 
 
+@pytest.mark.parametrize("fmt,K,T", [(5, 2176, 1), (5, 2176, 4), (4, 2176, 8), (8, 1152, 2)])
+def test_short_k_plan_one_unit_slices(fmt, K, T):
+    # a few hundred row tiles of very short K: the automatic plan splits every tile until each
+    # wave holds one k unit at most (some waves empty), and matches the oracle on every row and
+    # a plan with fewer, fuller slices to rounding
+    M = 5120 - 9
+    wl = _workload(fmt, M, K, T, 47 + K)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    NU = K // 128
+    p = wq.qmat_get_plan(qm.handle, T)
+    say(f"short K fmt={fmt} K={K} T={T} auto plan {p.as_tuple()}")
+    assert p.route == wq.QMAT_ROUTE_MFMA and p.tail_tiles == 0 and p.splits > 1
+    assert -(-NU // (p.splits * p.waves)) == 1 and p.splits * p.waves >= NU
+    xd = _x_dev(wl.x)
+    y = torch.full((T, M), float("nan"), device="cuda")
+    y1 = torch.full((T, M), float("nan"), device="cuda")
+    wq.qmat_run(qm.handle, xd, y, T=T)
+    wq.qmat_run_plan(qm.handle, xd, y1, wq.qmat_plan(p.route, 1, 4, 1, 0, 1, 1), T=T)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    _check_y(y, wl, f"short K fmt={fmt} K={K} T={T}")
+    torch.testing.assert_close(y, y1, rtol=1e-5, atol=1e-5)
+    qm.close()
+
+
 def test_run_plan_rejects_bad_fields():
     say("run_plan errors")
     wl = _workload(4, 130, 256, 1, 5)

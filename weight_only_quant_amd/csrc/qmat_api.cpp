@@ -57,7 +57,11 @@ struct Plan {
 //    slower on every shape).  4 waves per workgroup with two units in flight up to T = 4, 8
 //    waves with one unit beyond (a two-unit ring in 8-wave workgroups would leave room for only
 //    one workgroup per compute unit); but when 4 waves would get fewer than 8 units each (short
-//    K, e.g. 5120), 8 waves with one unit in flight at every T (2-3% faster at T = 1-4).
+//    K, e.g. 5120), 8 waves with one unit in flight at every T (2-3% faster at T = 1-4).  A
+//    wave's k units are a contiguous slice of the tile's NU units cut into splits x waves slices,
+//    and the longest slice sets the tile's time: on very short K the splits go as far as one
+//    unit per slice, some slices left empty (5120 x 2176, 17 units: 3 splits x 8 waves 7% faster
+//    than 2 x 8, whose one two-unit slice doubles the longest; 4 x 8 slower again).
 //
 // Vector-ALU kernel (explicit requests only): two units in flight, 4 waves per workgroup,
 // single-wave workgroups for wide matrices, splits up to about 4 waves per compute unit.
@@ -101,10 +105,13 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
             const int64_t target_waves = 8LL * cus;
             int64_t splits = (target_waves + NT * p.waves - 1) / (NT * p.waves);
             if (splits > 3) splits = 3;
-            if (splits > NU / p.waves) splits = NU / p.waves;
+            // a tile's longest slice (k units of one wave) is ceil(NU / (splits * waves)): allow
+            // the split that brings it to one unit even when some slices are then empty
+            if (splits > (NU + p.waves - 1) / p.waves) splits = (NU + p.waves - 1) / p.waves;
             if (splits < 1) splits = 1;
             p.splits = (int)splits;
-            while (p.waves > 1 && NU < (int64_t)p.waves * p.splits) p.waves /= 2;
+            // fewer waves while that keeps every slice at one unit at most
+            while (p.waves > 1 && 2 * NU <= (int64_t)p.waves * p.splits) p.waves /= 2;
             if (p.waves == 8) p.depth = 1;
         }
         return p;
