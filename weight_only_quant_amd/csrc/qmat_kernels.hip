@@ -444,10 +444,19 @@ __device__ __forceinline__ void mfma_step(const Unit<NB, XN> &U, f32x4_t (&D)[4]
     mfma_step_w<FMT, KA, NB>(U.c, U.x[KA], D);
 }
 
-// A operand: 16 tokens x 32 k (lane l: token l % 16, k octet l / 16); B operand: 32 k x 16 rows
-// of the tile (lane l: row 16*m + l % 16, the same k octet) — exactly the packed layout.
-// D[m]: lane l holds tokens 4*(l/16) + r (r = 0..3) of row 16*m + l % 16.  TR: how many of the
-// four r components can hold a real token (1 when T == 1: only token 0, in lanes 0..15).
+// A operand: 16 token slots x 32 k (lane l: slot l % 16, k octet l / 16); B operand: 32 k x 16
+// rows of the tile (lane l: row 16*m + l % 16, the same k octet) — exactly the packed layout.
+// D[m]: lane l holds slots 4*(l/16) + r (r = 0..3) of row 16*m + l % 16.
+//
+// Token t sits in slot 4*(t / TR) + t % TR, so that the tokens of a launch fill only the first
+// TR of every lane's four D components: TR = 1 up to 4 tokens, 2 up to 8, 4 up to 16.  A lane
+// then applies TR group scales per row group and unit instead of four, and keeps TR
+// accumulators per row group (the MFMA's other components are computed and dropped).
+template <int TR> __device__ __forceinline__ int slot_token(int slot)
+{
+    return (slot & 3) < TR ? TR * (slot >> 2) + (slot & 3) : 16;  // 16: no token
+}
+
 template <int FMT, int D_, int TR>
 __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
 {
@@ -455,9 +464,9 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
     extern __shared__ float red[];
     const Slice s = make_slice(a);
     const uint32_t lane = threadIdx.x & 63;
-    const int tok = lane & 15, oct = lane >> 4;
-    // A rows of tokens >= T only feed D rows that are never stored: those lanes read the
-    // activations through a buffer resource at an offset past its end, which returns zeros
+    const int tok = slot_token<TR>(lane & 15), oct = lane >> 4;
+    // A rows of slots without a token only feed D rows that are never stored: those lanes read
+    // the activations through a buffer resource at an offset past its end, which returns zeros
     // without a memory request (at T = 1, 15 lanes in 16)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.x), (short)0, 2 * a.T * a.K, kRawBufferWord3);
@@ -519,7 +528,7 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int r = 0; r < TR; ++r) acc[m][r] *= rs[m];
-    const int t0 = 4 * oct, rr = lane & 15;
+    const int t0 = TR * oct, rr = lane & 15;
     finish(a, s, red, [&](auto put) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -543,15 +552,15 @@ template <int NB> struct PairUnit {
     u32x4_t x[4];
 };
 
-template <int FMT, int D_>
+template <int FMT, int D_, int TR>
 __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
 {
-    constexpr int NB = Fmt<FMT>::NB, TR = 4;
+    constexpr int NB = Fmt<FMT>::NB;
     extern __shared__ float red[];
     const Slice s = make_slice(a);  // no trailing tiles: s.tile is the pair index
     const int pair = s.tile;
     const uint32_t lane = threadIdx.x & 63;
-    const int tok = lane & 15, oct = lane >> 4;
+    const int tok = slot_token<TR>(lane & 15), oct = lane >> 4;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.x), (short)0, 2 * a.T * a.K, kRawBufferWord3);
     const uint32_t xoff = tok < a.T ? 2u * (uint32_t)(tok * a.K) + 16u * oct : kPastEnd;
@@ -619,7 +628,7 @@ __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
             }
         });
 
-    const int t0 = 4 * oct, rr = lane & 15;
+    const int t0 = TR * oct, rr = lane & 15;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         Slice si = s;
@@ -707,10 +716,17 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a)
 
 template <int FMT, int D> static const void *run_kernel_d(int route, int T, int tiles)
 {
-    if (tiles == 2) return route == kRouteMfma ? reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D>) : nullptr;
-    if (route == kRouteMfma)
-        return T == 1 ? reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 1>)
+    if (route == kRouteMfma) {
+        // token slots per lane and row group: 1 up to 4 tokens, 2 up to 8, 4 up to 16
+        if (tiles == 2)
+            return T <= 4 ? reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D, 1>)
+                 : T <= 8 ? reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D, 2>)
+                          : reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D, 4>);
+        return T <= 4 ? reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 1>)
+             : T <= 8 ? reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 2>)
                       : reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 4>);
+    }
+    if (tiles == 2) return nullptr;
     switch (T) {
     case 1: return reinterpret_cast<const void *>(&valu_kernel<FMT, 1, D>);
     case 2: return reinterpret_cast<const void *>(&valu_kernel<FMT, 2, D>);
