@@ -41,9 +41,10 @@ struct Plan {
 //    T = 9; Q4 and Q6 0.3-9% slower up to T = 9; every format slower at T = 1; above the
 //    crossovers 1-14% faster, the most at T = 16).  Fewer tiles (the 131072-row proposal head:
 //    pairs 1.6% slower at T = 8): the 8-bit formats from T = 9, the others from 10.
-//  - At least one tile per compute unit: 4 waves per workgroup, two units in flight up to T = 4
-//    and one above (from T = 12 the multi-token accumulators of a two-unit ring leave too few
-//    resident waves: 25-30% slower; at T = 2-4 the ring is 6-7% faster, T = 6-8 tie).  When
+//  - At least one tile per compute unit: 4 waves per workgroup, two units in flight up to T = 8
+//    and one above.  Up to 8 tokens a lane keeps at most two accumulators per row group; from
+//    T = 9 it keeps four, and a two-unit ring then leaves too few resident waves (25-30% slower
+//    at T = 12-16).  Gate+up, ring against one unit: 3% faster at T = 4, 4-5% at T = 6-8.  When
 //    the tile count is not a multiple of the compute-unit count, the leftover tiles would form a
 //    second, nearly empty round of workgroups on a few compute units (measured: 34816 rows take
 //    4 us longer than 32768).  Those trailing tiles are instead split along K over up to 8
@@ -53,11 +54,12 @@ struct Plan {
 //    fill), as long as the whole tiles themselves fit in one round.
 //  - Fewer tiles than compute units: every tile split along K across workgroups until about 8
 //    waves per compute unit exist, at most 3 ways (every split adds a round of partial-sum
-//    traffic and a last-arrival reduction at the end of the kernel; 4 and more splits measured
-//    slower on every shape).  4 waves per workgroup with two units in flight up to T = 4, 8
-//    waves with one unit beyond (a two-unit ring in 8-wave workgroups would leave room for only
-//    one workgroup per compute unit); but when 4 waves would get fewer than 8 units each (short
-//    K, e.g. 5120), 8 waves with one unit in flight at every T (2-3% faster at T = 1-4).  A
+//    traffic and a level of the reduction tree at the end of the kernel; 4 and more splits
+//    measured slower on every shape).  4 waves per workgroup with two units in flight up to
+//    T = 8 (Q5 down at T = 6 / 8: 6% / 3% faster than 8 waves with one unit), 8 waves with one
+//    unit beyond (a two-unit ring in 8-wave workgroups would leave room for only one workgroup
+//    per compute unit); but when 4 waves would get fewer than 8 units each (short K, e.g.
+//    5120), 8 waves with one unit in flight at every T (2-3% faster at T = 1-4, 10% at 8).  A
 //    wave's k units are a contiguous slice of the tile's NU units cut into splits x waves slices,
 //    and the longest slice sets the tile's time: on very short K the splits go as far as one
 //    unit per slice, some slices left empty (5120 x 2176, 17 units: 3 splits x 8 waves 7% faster
@@ -85,7 +87,7 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
             }
         } else if (NT >= cus) {
             p.waves = 4;
-            p.depth = Tl <= 4 ? 2 : 1;
+            p.depth = Tl <= 8 ? 2 : 1;
             while (p.waves > 1 && NU < (int64_t)p.waves) p.waves /= 2;
             const int64_t rem = NT % cus;
             if (rem > 0) {
@@ -101,7 +103,7 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
             }
         } else {
             const bool short_k = NU < 8LL * 4 * 3;  // < 8 units per wave with 4 waves and 3 splits
-            p.waves = Tl <= 4 && !short_k ? 4 : 8;
+            p.waves = Tl <= 8 && !short_k ? 4 : 8;
             const int64_t target_waves = 8LL * cus;
             int64_t splits = (target_waves + NT * p.waves - 1) / (NT * p.waves);
             if (splits > 3) splits = 3;
