@@ -578,6 +578,37 @@ def test_zero_and_sparse_codes(fmt):
         _check_y(y, qi.Workload("s", fmt, M, K, T, codes, wl.scales, wl.x), f"sparse {route}")
 
 
+@pytest.mark.parametrize("T", [1, 4, 8, 12])
+def test_q4_offset_operands_on_zero_and_sparse_rows(T):
+    # Q4 reaches the matrix cores as offset-binary operands (code + 8) / 512 up to 8 tokens, the
+    # offset taken out per group by subtracting the same MFMA sum over a constant operand.  Rows
+    # of zero codes must still give exactly 0, and rows that are 90-99% zero codes must stay
+    # within the tolerance next to activations with large outlier channels (256x on 1% of K)
+    M, K = 96, 2048
+    wl = _workload(4, M, K, T, 77 + T)
+    rng = np.random.default_rng(9 + T)
+    codes = wl.codes.copy()
+    codes[:16] = 0
+    for i in range(16, M):
+        keep = 0.10 if i < 56 else 0.01
+        codes[i, rng.random(K) >= keep] = 0
+    x = torch.from_numpy(wl.x.view(np.int16).copy()).view(torch.bfloat16).float()
+    outl = rng.choice(K, K // 100, replace=False)
+    x[:, outl] *= 256.0
+    xb = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    scales = wl.scales.copy()
+    scales[:16] = np.float16(1000.0).view(np.uint16)
+    qm = wq.QMat(4, codes, scales)
+    y = torch.full((T, M), float("nan"), device="cuda")
+    wq.qmat_run(qm.handle, _x_dev(xb), y, T=T)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert np.all(got[:, :16] == 0)
+    worst = _check_y(y, qi.Workload("q4s", 4, M, K, T, codes, scales, xb), f"q4 sparse rows T={T}")
+    say(f"q4 sparse rows T={T}: worst ratio {worst:.3g}")
+    qm.close()
+
+
 # FP8 row scales the API accepts (any finite fp32) that the seeded workloads never produce:
 # negative, +0, -0, subnormal, the smallest normal and large magnitudes
 FP8_EDGE_ROW_SCALES = np.array([-0.0123, 0.0, -0.0, 1.0e-40, -3.0e-42, 2.0 ** -126, -1.0e30, 7.5e29,

@@ -40,7 +40,9 @@ __device__ __forceinline__ void load_weight_blocks(const RunArgs &a, int tile, i
 // global memory into LDS (shared by its 4 waves, double-buffered, one barrier per unit) while
 // each wave streams its tile's packed unit one unit ahead.  Per 64-group and 16-row slice m,
 // two MFMAs sum code * x into P and the group scale enters once per (token, row):
-// acc += scale * P (exact products, fp32 sums, as on the small-T routes).  Row-scaled FP8 has no group scale: the MFMA
+// acc += scale * P (exact products, fp32 sums, as on the small-T routes; the signed operands,
+// since removing Q4's offset would cost a subtraction per (token, row, group)).  Row-scaled FP8
+// has no group scale: the MFMA
 // accumulates straight into acc and the row scale is applied at the end.
 //
 // Two workgroups per CU (at most 256 vector registers per lane) so that one wave's unpack and
@@ -154,11 +156,12 @@ __global__ __launch_bounds__(256, kGemmTB <= 64 ? 2 : 1) void gemm_kernel(RunArg
                 for (int n = 0; n < NTB; ++n)
                     A[ks][n] = *reinterpret_cast<const bf16x8_t *>(
                         &xb[(16 * n + tl) * kUnitK + 8 * ((4 * (2 * g + ks) + oct) ^ tl)]);
+
 #define QMAT_GEMM_SLICE(MM, G)                                                                          \
     {                                                                                                   \
         uint32_t b0[4], b1[4];                                                                          \
-        bf16x8_of<FMT, 2 * (G), MM>(W, b0);                                                             \
-        bf16x8_of<FMT, 2 * (G) + 1, MM>(W, b1);                                                         \
+        bf16x8_signed<FMT, 2 * (G), MM>(W, b0);                                                         \
+        bf16x8_signed<FMT, 2 * (G) + 1, MM>(W, b1);                                                     \
         const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, (u32x4_t){b0[0], b0[1], b0[2], b0[3]});        \
         const bf16x8_t B1 = __builtin_bit_cast(bf16x8_t, (u32x4_t){b1[0], b1[1], b1[2], b1[3]});        \
         if constexpr (FMT == 8) {                                                                       \
@@ -215,7 +218,8 @@ __global__ __launch_bounds__(256, kGemmTB <= 64 ? 2 : 1) void gemm_kernel(RunArg
         if (u + 1 < u1) step(u + 1, wb, wa);
     }
     if (!has_tile) return;
-    f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
+    constexpr float kF = Fmt<FMT>::kSignedToCode;
+    f32x4_t rs = (f32x4_t){kF, kF, kF, kF};
     if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)tile * 16 + tl];
 #pragma unroll
     for (int m = 0; m < 4; ++m)

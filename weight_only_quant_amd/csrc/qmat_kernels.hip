@@ -10,7 +10,13 @@
 // described in qmat_layout.h.  Template parameter FMT is the format id (9 = Q8).
 //
 // Every code is turned into an exact small float before any product is formed:
-//   Q4   v_cvt_off_f32_i4 reads a two's-complement nibble as code/16 (SDWA picks the byte);
+//   Q4   on the matrix cores up to 8 tokens: the stored offset-binary nibble (code + 8) is
+//        masked into a byte that v_cvt_scalef32_pk_bf16_fp8 reads as (code + 8) * 2^-9, two
+//        per instruction; each group's product sum then subtracts the same MFMA sum over a
+//        constant operand 8 * 2^-9 (q4_group_offset), which is exactly the sum of the offsets
+//        for a group of zero codes;
+//        elsewhere v_cvt_off_f32_i4 reads the nibble with its top bit flipped (two's
+//        complement) as code/16 (SDWA picks the byte);
 //   Q5/6 the code is assembled in the top bits of a byte and v_cvt_f32_i32 with SDWA sign
 //        extension reads it as 8*code or 4*code;
 //   Q8   the same SDWA convert reads each stored byte as the code;
@@ -18,7 +24,8 @@
 // These values are exact in bf16, so bf16(code) * bf16(x) is an exact product; dot products
 // accumulate in fp32 (v_dot2c_f32_bf16 on the vector ALU, or the 16x16x32 bf16 MFMA), and the
 // per-group scale (times the power of two of the code encoding) is applied once per 64-group.
-// No offset-binary tricks: a row with sparse or zero codes has no cancellation error.
+// The Q4 offset costs accuracy only on rows whose codes are almost all zero: its rounding
+// scales with the group's sum of activations instead of its sum of products.
 //
 // Work split: a wave owns one 64-row tile and a contiguous range of 128-wide k units.  NW waves
 // of a workgroup split a tile's units and reduce through LDS; S workgroups split further and
@@ -326,7 +333,7 @@ __device__ __forceinline__ void valu_step(const Unit<NB, XN> &U, float (&p)[4][T
 {
     const uint32_t *W = reinterpret_cast<const uint32_t *>(U.c);
     uint32_t b[4];
-    bf16x8_of<FMT, KA, MM>(W, b);
+    bf16x8_signed<FMT, KA, MM>(W, b);
 #pragma unroll
     for (int t = 0; t < TT; ++t)
 #pragma unroll
@@ -392,7 +399,8 @@ __global__ __launch_bounds__(512) void valu_kernel(RunArgs a)
         });
 
     // the code encoding's power of two (groupwise) or the row scale (FP8), once per row
-    f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
+    constexpr float kF = Fmt<FMT>::kSignedToCode;
+    f32x4_t rs = (f32x4_t){kF, kF, kF, kF};
     if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)s.tile * 16 + (lane & 15)];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(512) void valu_kernel(RunArgs a)
 
 // One 32-wide k step of a tile: the four 16-row slices' codes (blocks c) times the activation
 // fragment xa, accumulated into D.
-template <int FMT, int KA, int NB>
+template <int FMT, int KA, int NB, bool OFF>
 __device__ __forceinline__ void mfma_step_w(const u32x4_t (&c)[NB], const u32x4_t &xa, f32x4_t (&D)[4])
 {
     const uint32_t *W = reinterpret_cast<const uint32_t *>(c);
@@ -430,7 +438,8 @@ __device__ __forceinline__ void mfma_step_w(const u32x4_t (&c)[NB], const u32x4_
 #define QMAT_MFMA_ROW(MM)                                                                       \
     {                                                                                           \
         uint32_t b[4];                                                                          \
-        bf16x8_of<FMT, KA, MM>(W, b);                                                           \
+        if constexpr (OFF) bf16x8_of<FMT, KA, MM>(W, b);                                        \
+        else bf16x8_signed<FMT, KA, MM>(W, b);                                                  \
         const bf16x8_t B = __builtin_bit_cast(bf16x8_t, (u32x4_t){b[0], b[1], b[2], b[3]});     \
         D[MM] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, D[MM], 0, 0, 0);                 \
     }
@@ -438,11 +447,16 @@ __device__ __forceinline__ void mfma_step_w(const u32x4_t (&c)[NB], const u32x4_
 #undef QMAT_MFMA_ROW
 }
 
-template <int FMT, int KA, int NB, int XN>
+template <int FMT, int KA, bool OFF, int NB, int XN>
 __device__ __forceinline__ void mfma_step(const Unit<NB, XN> &U, f32x4_t (&D)[4])
 {
-    mfma_step_w<FMT, KA, NB>(U.c, U.x[KA], D);
+    mfma_step_w<FMT, KA, NB, OFF>(U.c, U.x[KA], D);
 }
+
+// Whether an MFMA kernel with TR token slots per lane uses the offset Q4 operands (two extra
+// matrix instructions and TR subtractions per row slice and group) or the signed ones: offset
+// where the shorter unpack pays for that, up to 8 tokens.
+template <int FMT, int TR> constexpr bool mfma_offset() { return Fmt<FMT>::kOffset != 0.0f && TR < 4; }
 
 // A operand: 16 token slots x 32 k (lane l: slot l % 16, k octet l / 16); B operand: 32 k x 16
 // rows of the tile (lane l: row 16*m + l % 16, the same k octet) — exactly the packed layout.
@@ -471,6 +485,7 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.x), (short)0, 2 * a.T * a.K, kRawBufferWord3);
     const uint32_t xoff = tok < a.T ? 2u * (uint32_t)(tok * a.K) + 16u * oct : kPastEnd;
+    constexpr bool OFF = mfma_offset<FMT, TR>();
     f32x4_t acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -495,10 +510,10 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
         [&]() {},
         [&](const Unit<NB, XN> &U, int) {
             if constexpr (FMT == 8) {
-                mfma_step<FMT, 0>(U, acc);
-                mfma_step<FMT, 1>(U, acc);
-                mfma_step<FMT, 2>(U, acc);
-                mfma_step<FMT, 3>(U, acc);
+                mfma_step<FMT, 0, OFF>(U, acc);
+                mfma_step<FMT, 1, OFF>(U, acc);
+                mfma_step<FMT, 2, OFF>(U, acc);
+                mfma_step<FMT, 3, OFF>(U, acc);
             } else {
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
@@ -506,11 +521,18 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
 #pragma unroll
                     for (int m = 0; m < 4; ++m) P[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
                     if (g == 0) {
-                        mfma_step<FMT, 0>(U, P);
-                        mfma_step<FMT, 1>(U, P);
+                        mfma_step<FMT, 0, OFF>(U, P);
+                        mfma_step<FMT, 1, OFF>(U, P);
                     } else {
-                        mfma_step<FMT, 2>(U, P);
-                        mfma_step<FMT, 3>(U, P);
+                        mfma_step<FMT, 2, OFF>(U, P);
+                        mfma_step<FMT, 3, OFF>(U, P);
+                    }
+                    if constexpr (OFF) {
+                        const f32x4_t o = q4_group_offset(U.x[2 * g], U.x[2 * g + 1]);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+#pragma unroll
+                            for (int r = 0; r < TR; ++r) P[m][r] -= o[r];
                     }
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
@@ -522,7 +544,8 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
             }
         });
 
-    f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
+    constexpr float kF = OFF ? Fmt<FMT>::kToCode : Fmt<FMT>::kSignedToCode;
+    f32x4_t rs = (f32x4_t){kF, kF, kF, kF};
     if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)s.tile * 16 + (lane & 15)];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -565,6 +588,7 @@ __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
         const_cast<uint16_t *>(a.x), (short)0, 2 * a.T * a.K, kRawBufferWord3);
     const uint32_t xoff = tok < a.T ? 2u * (uint32_t)(tok * a.K) + 16u * oct : kPastEnd;
     const int tile0 = 2 * pair, tile1 = 2 * pair + 1 < a.NT ? 2 * pair + 1 : 2 * pair;
+    constexpr bool OFF = mfma_offset<FMT, TR>();
     f32x4_t acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -597,13 +621,19 @@ __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
         },
         [&]() {},
         [&](const PairUnit<NB> &U, int) {
+            // the Q4 offset sums depend on the activations only: once for both tiles
+            f32x4_t o[2] = {(f32x4_t){0.f, 0.f, 0.f, 0.f}, (f32x4_t){0.f, 0.f, 0.f, 0.f}};
+            if constexpr (OFF) {
+                o[0] = q4_group_offset(U.x[0], U.x[1]);
+                o[1] = q4_group_offset(U.x[2], U.x[3]);
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 if constexpr (FMT == 8) {
-                    mfma_step_w<FMT, 0, NB>(U.c[i], U.x[0], acc[i]);
-                    mfma_step_w<FMT, 1, NB>(U.c[i], U.x[1], acc[i]);
-                    mfma_step_w<FMT, 2, NB>(U.c[i], U.x[2], acc[i]);
-                    mfma_step_w<FMT, 3, NB>(U.c[i], U.x[3], acc[i]);
+                    mfma_step_w<FMT, 0, NB, OFF>(U.c[i], U.x[0], acc[i]);
+                    mfma_step_w<FMT, 1, NB, OFF>(U.c[i], U.x[1], acc[i]);
+                    mfma_step_w<FMT, 2, NB, OFF>(U.c[i], U.x[2], acc[i]);
+                    mfma_step_w<FMT, 3, NB, OFF>(U.c[i], U.x[3], acc[i]);
                 } else {
 #pragma unroll
                     for (int g = 0; g < 2; ++g) {
@@ -611,11 +641,17 @@ __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
 #pragma unroll
                         for (int m = 0; m < 4; ++m) P[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
                         if (g == 0) {
-                            mfma_step_w<FMT, 0, NB>(U.c[i], U.x[0], P);
-                            mfma_step_w<FMT, 1, NB>(U.c[i], U.x[1], P);
+                            mfma_step_w<FMT, 0, NB, OFF>(U.c[i], U.x[0], P);
+                            mfma_step_w<FMT, 1, NB, OFF>(U.c[i], U.x[1], P);
                         } else {
-                            mfma_step_w<FMT, 2, NB>(U.c[i], U.x[2], P);
-                            mfma_step_w<FMT, 3, NB>(U.c[i], U.x[3], P);
+                            mfma_step_w<FMT, 2, NB, OFF>(U.c[i], U.x[2], P);
+                            mfma_step_w<FMT, 3, NB, OFF>(U.c[i], U.x[3], P);
+                        }
+                        if constexpr (OFF) {
+#pragma unroll
+                            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                                for (int r = 0; r < TR; ++r) P[m][r] -= o[g][r];
                         }
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
@@ -635,7 +671,8 @@ __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
         si.tile = tile0 + i;
         si.wsrow = si.tile * kTileRows;
         if (si.tile >= a.NT) break;  // uniform over the workgroup
-        f32x4_t rs = (f32x4_t){Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode, Fmt<FMT>::kToCode};
+        constexpr float kF = OFF ? Fmt<FMT>::kToCode : Fmt<FMT>::kSignedToCode;
+        f32x4_t rs = (f32x4_t){kF, kF, kF, kF};
         if constexpr (FMT == 8) rs = reinterpret_cast<const f32x4_t *>(a.scales)[(int64_t)si.tile * 16 + (lane & 15)];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -671,14 +708,15 @@ __device__ __forceinline__ void dequant_step(const DequantArgs &a, const uint32_
             out[2 * i + 1] = rs[MM] * __builtin_bit_cast(float, b[i] & 0xFFFF0000u);
         }
     } else {
-        // the exact bf16 operands both routes feed to their products, decoded back to the code
+        // the exact bf16 operands the matrix-core products take, decoded back to the code
+        // (u * kToCode - kOffset: both steps exact)
         uint32_t b[4];
         bf16x8_of<FMT, KA, MM>(W, b);
         const float sc_f = group_scale(sc, KA >> 1, MM);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t hb = (i & 1) ? (b[i >> 1] & 0xFFFF0000u) : (b[i >> 1] << 16);
-            out[i] = sc_f * (__builtin_bit_cast(float, hb) * Fmt<FMT>::kToCode);
+            out[i] = sc_f * (__builtin_bit_cast(float, hb) * Fmt<FMT>::kToCode - Fmt<FMT>::kOffset);
         }
     }
     float *dst = a.w + (int64_t)row * a.K + k;

@@ -11,8 +11,10 @@
 // kernels.  Concatenating a lane's slots of one unit gives 4*NB dwords W[0 .. 4*NB-1]
 // (W[4*j + d] = dword d of block j):
 //
-//   Q4  (NB 4): W[4*kappa + m] holds the 8 codes of row m, e in bits [4e+3 : 4e], two's
-//               complement nibbles.
+//   Q4  (NB 4): W[4*kappa + m] holds the 8 codes of row m: byte i has e = i in bits [3:0]
+//               and e = 4 + i in bits [7:4], each as the offset-binary nibble code + 8 (the
+//               two's complement nibble with its top bit flipped), so that masking the low or
+//               the high nibbles leaves bytes that read as E4M3 values (code + 8) * 2^-9.
 //   Q5  (NB 5): W[5*kappa + 0..4] = X0 X1 X2 X3 E.  Output dword o (0..7) carries the codes of
 //               row o/2, e = 4*(o%2) + i in byte i, each byte = code << 3 (a signed byte worth
 //               8*code).  O_d = X_d & 0xF8F8F8F8 for d < 4; for d < 4 the low 3 bits of each byte
