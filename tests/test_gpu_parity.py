@@ -278,6 +278,27 @@ def test_pair_plan_on_head_sized_matrix(fmt, T, NT):
     qm.close()
 
 
+def test_trailing_split_plan_on_gate_up_rows():
+    # 544 row tiles on 256 compute units: the 32 trailing tiles are split along K, 8 ways at
+    # T = 1 and 4 ways from T = 2; the result matches the oracle on sampled and trailing rows
+    M, K = 34816 - 5, 1024
+    wl = _workload(4, M, K, 8, 93)
+    qm = wq.QMat(4, wl.codes, wl.scales)
+    for T, st in ((1, 8), (4, 4), (8, 4), (12, 4)):
+        p = wq.qmat_get_plan(qm.handle, T)
+        say(f"gate+up rows T={T} auto plan {p.as_tuple()}")
+        assert (p.tail_tiles, p.tail_splits) == (32, st)
+    for T in (1, 8):
+        xd = _x_dev(wl.x[:T])
+        y = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run(qm.handle, xd, y, T=T)
+        torch.cuda.synchronize()
+        assert not torch.isnan(y).any()
+        sub = qi.Workload(wl.name, 4, M, K, T, wl.codes, wl.scales, wl.x[:T])
+        _check_y(y, sub, f"gate+up rows T={T}", rows=sorted(set(_sample_rows(M, n=300, seed=4)) | set(range(M - 2100, M))))
+    qm.close()
+
+
 @pytest.mark.parametrize("fmt,K,T", [(5, 2176, 1), (5, 2176, 4), (4, 2176, 8), (8, 1152, 2)])
 def test_short_k_plan_one_unit_slices(fmt, K, T):
     # a few hundred row tiles of very short K: the automatic plan splits every tile until each

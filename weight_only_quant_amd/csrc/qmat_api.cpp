@@ -48,10 +48,10 @@ struct Plan {
 //    the tile count is not a multiple of the compute-unit count, the leftover tiles would form a
 //    second, nearly empty round of workgroups on a few compute units (measured: 34816 rows take
 //    4 us longer than 32768).  Those trailing tiles are instead split along K over up to 8
-//    workgroups each, enough to give every compute unit a share, and dispatched first.  The
-//    short trailing workgroups may run beyond one round of resident workgroups (two-unit rings
-//    at T = 2-4 leave room for two 4-wave workgroups per compute unit, which the whole tiles
-//    fill), as long as the whole tiles themselves fit in one round.
+//    workgroups each at T = 1, up to 4 from T = 2, and dispatched first (34816 rows: 8 splits
+//    best at T = 1, 4 splits 1.3% faster at T = 4 and 8, where each piece's tree carries
+//    several tokens).  The short trailing workgroups may run beyond one round of resident
+//    workgroups, as long as the whole tiles themselves fit in one round.
 //  - Fewer tiles than compute units: every tile split along K across workgroups until about 8
 //    waves per compute unit exist, at most 3 ways (every split adds a round of partial-sum
 //    traffic and a level of the reduction tree at the end of the kernel; 4 and more splits
@@ -93,7 +93,7 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
             if (rem > 0) {
                 const int64_t resident = (int64_t)run_blocks_per_cu(fmt, kRouteMfma, p.depth, Tl, p.waves, (int)NU, 1) * cus;
                 int64_t st = cus / rem;
-                if (st > 8) st = 8;
+                if (st > (Tl == 1 ? 8 : 4)) st = Tl == 1 ? 8 : 4;
                 if (st > NU) st = NU;
                 if (NT - rem > resident) st = 1;
                 if (st > 1) {
