@@ -250,7 +250,7 @@ def test_run_pair_plans(fmt, T):
 
 
 @pytest.mark.parametrize("fmt,T,NT", [(4, 16, 2049), (5, 10, 2049), (6, 12, 2049), (8, 16, 2049), (8, 9, 2049),
-                                      (qi.Q8, 13, 2049), (5, 9, 3073), (8, 2, 3073), (qi.Q8, 6, 3073)])
+                                      (qi.Q8, 13, 2049), (5, 9, 3073), (8, 2, 3073), (qi.Q8, 9, 3073)])
 def test_pair_plan_on_head_sized_matrix(fmt, T, NT):
     # the automatic plan of a matrix of >= 2048 row tiles at verify-sized T streams two tiles
     # per wave; with an odd tile count and a ragged last tile it matches the oracle on sampled
@@ -262,8 +262,8 @@ def test_pair_plan_on_head_sized_matrix(fmt, T, NT):
     say(f"head-sized fmt={fmt} T={T} auto plan {p.as_tuple()}")
     assert p.route == wq.QMAT_ROUTE_MFMA and p.tiles == 2 and p.splits == 1 and p.tail_tiles == 0
     # two tiles per wave from each format's crossover, one below: with >= 3072 tiles FP8 2, Q8
-    # 6, Q5 9, Q4 and Q6 10; with fewer the 8-bit formats 9, the others 10
-    first = {8: 2, qi.Q8: 6, 5: 9}.get(fmt, 10) if NT >= 3072 else (9 if fmt in (8, qi.Q8) else 10)
+    # and Q5 9, Q4 and Q6 10; with fewer the 8-bit formats 9, the others 10
+    first = {8: 2, qi.Q8: 9, 5: 9}.get(fmt, 10) if NT >= 3072 else (9 if fmt in (8, qi.Q8) else 10)
     assert [wq.qmat_get_plan(qm.handle, t).tiles for t in range(1, 17)] == [1] * (first - 1) + [2] * (17 - first)
     xd = _x_dev(wl.x)
     y = torch.full((T, M), float("nan"), device="cuda")

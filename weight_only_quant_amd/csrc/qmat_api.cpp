@@ -36,11 +36,12 @@ struct Plan {
 //    tile's k units at T = 1 (a single token leaves registers for two units in flight), 1 wave
 //    otherwise.  From a format's crossover a wave streams two neighbouring tiles with one unit
 //    in flight, loading each activation fragment once for both.  With at least 3072 tiles:
-//    FP8 from T = 2, Q8 from 6, Q5 from 9, Q4 and Q6 from 10 (measured on 248320 x 5120 heads,
-//    pair against one tile per wave: FP8 1-3% faster at T = 2-8, Q8 1-2% at T = 6-8, Q5 2% at
-//    T = 9; Q4 and Q6 0.3-9% slower up to T = 9; every format slower at T = 1; above the
-//    crossovers 1-14% faster, the most at T = 16).  Fewer tiles (the 131072-row proposal head:
-//    pairs 1.6% slower at T = 8): the 8-bit formats from T = 9, the others from 10.
+//    FP8 from T = 2, Q8 and Q5 from 9, Q4 and Q6 from 10 (measured on 248320 x 5120 heads,
+//    pair against one tile per wave: FP8 0-3% faster at T = 2-8; Q8 2-3% slower at T = 6-8
+//    since tokens up to 8 fill only two accumulator slots per lane; Q5 2% faster at T = 9; Q4
+//    and Q6 0.3-9% slower up to T = 9; every format slower at T = 1; above the crossovers
+//    1-14% faster, the most at T = 16).  Fewer tiles (the 131072-row proposal head: pairs 1.6%
+//    slower at T = 8): the 8-bit formats from T = 9, the others from 10.
 //  - At least one tile per compute unit: 4 waves per workgroup, two units in flight up to T = 8
 //    and one above.  Up to 8 tokens a lane keeps at most two accumulators per row group; from
 //    T = 9 it keeps four, and a two-unit ring then leaves too few resident waves (25-30% slower
@@ -78,7 +79,7 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
             // 2048-tile head keeps more workgroups up to T = 8)
             const bool many = NT >= 3072;
             const int pair_from = fmt == kFmtFp8 ? (many ? 2 : 9)
-                                  : fmt == kFmtQ8 ? (many ? 6 : 9)
+                                  : fmt == kFmtQ8 ? 9
                                   : fmt == 5      ? (many ? 9 : 10)
                                                   : 10;
             if (Tl >= pair_from) {
