@@ -69,8 +69,19 @@ typedef enum {
     QMAT_ROUTE_AUTO = 0, /* the library's choice for (format, shape, T) */
     QMAT_ROUTE_VALU = 1, /* vector-ALU dot products; T > 4 runs as several passes */
     QMAT_ROUTE_MFMA = 2, /* bf16 matrix-core tiles (16 tokens x 16 rows x 32 k) */
-    QMAT_ROUTE_GEMM = 3  /* prefill-sized T: 64-token x 256-row matrix-core tiles, activations
+    QMAT_ROUTE_GEMM = 3, /* prefill-sized T: 64-token x 256-row matrix-core tiles, activations
                             staged in LDS; the automatic route for T > 16 */
+    QMAT_ROUTE_MFMA_OFFSET = 4 /* QMAT_ROUTE_MFMA, except that Q4 codes up to 8 tokens reach
+                            the matrix cores as offset-binary operands (code + 8) read by the FP8
+                            converter, and each group's sum over a constant operand takes the
+                            offset out again: 3-5% faster on Q4 at T <= 8 (every other format
+                            and T runs the same kernels as QMAT_ROUTE_MFMA).  Groups of zero codes
+                            stay exact, but the fp32 rounding scales with the sum of |x| over a
+                            group instead of the sum of |code * x|, so the error bound
+                            1e-4 * sum|w x| + 1e-6 holds only while a row's products are not
+                            dwarfed by activations that meet zero codes (measured 15-48x over the
+                            bound on rows of half zero codes with 2^18x larger activations on
+                            them).  Explicit requests only. */
 } qmat_route;
 
 typedef struct qmat *qmat_t;
@@ -203,7 +214,8 @@ int qmat_run_static(int fmt, int64_t M, int64_t K, const void *packed_dev, size_
  * same y for the same inputs run after run (different plans may differ in the last bits: the
  * summation order differs). */
 typedef struct {
-    int route;       /* QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA, or QMAT_ROUTE_GEMM (then only splits is
+    int route;       /* QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA, QMAT_ROUTE_MFMA_OFFSET or QMAT_ROUTE_GEMM
+                        (then only splits is
                         read: the k splits of every 64-token x 256-row tile, 1..16) */
     int depth;       /* 128-wide k units each wave keeps in flight: 1 or 2 */
     int waves;       /* waves per workgroup: 1, 2, 4 or 8 */
@@ -212,7 +224,7 @@ typedef struct {
     int tail_splits; /* workgroups per trailing tile: >= 1 (not read when tail_tiles == 0) */
     int tiles;       /* row tiles per wave: 0 or 1 (one), or 2 (a wave streams the same k units
                         of two neighbouring tiles and loads each activation fragment once for
-                        both; QMAT_ROUTE_MFMA with tail_tiles == 0 only) */
+                        both; the MFMA routes with tail_tiles == 0 only) */
 } qmat_plan;
 
 /* qmat_run with the automatic plan for (route, T) changed by the nonzero arguments, for tests

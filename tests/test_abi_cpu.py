@@ -50,6 +50,18 @@ def _pack_raw(fmt, M, K, codes, scales, out_bytes=None):
     return st
 
 
+def test_binding_enum_values_match_the_header():
+    # every QMAT_* enumerator of include/qmat.h has the same value in the binding
+    import re
+    text = open(os.path.join(ROOT, "include", "qmat.h")).read()
+    found = dict((n, int(v)) for n, v in re.findall(r"\b(QMAT_[A-Z0-9_]+)\s*=\s*(-?\d+)", text))
+    assert {"QMAT_ROUTE_MFMA_OFFSET", "QMAT_ROUTE_GEMM", "QMAT_Q8", "QMAT_ESIZE"} <= set(found)
+    for name, value in found.items():
+        if hasattr(wq, name):
+            assert getattr(wq, name) == value, name
+    assert wq.QMAT_ROUTE_MFMA_OFFSET == found["QMAT_ROUTE_MFMA_OFFSET"]
+
+
 def test_packed_bytes_invalid_is_zero():
     assert wq.qmat_packed_bytes(3, 64, 128) == 0
     assert wq.qmat_packed_bytes(4, 0, 128) == 0

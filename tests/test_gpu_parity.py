@@ -601,10 +601,11 @@ def test_zero_and_sparse_codes(fmt):
 
 @pytest.mark.parametrize("T", [1, 4, 8, 12])
 def test_q4_offset_operands_on_zero_and_sparse_rows(T):
-    # Q4 reaches the matrix cores as offset-binary operands (code + 8) / 512 up to 8 tokens, the
-    # offset taken out per group by subtracting the same MFMA sum over a constant operand.  Rows
-    # of zero codes must still give exactly 0, and rows that are 90-99% zero codes must stay
-    # within the tolerance next to activations with large outlier channels (256x on 1% of K)
+    # QMAT_ROUTE_MFMA_OFFSET: Q4 reaches the matrix cores as offset-binary operands
+    # (code + 8) / 512 up to 8 tokens, the offset taken out per group by subtracting the same
+    # MFMA sum over a constant operand.  Rows of zero codes must still give exactly 0, and rows
+    # that are 90-99% zero codes stay within the tolerance next to activations with outlier
+    # channels of 256x on 1% of K (not adversarial: the outliers fall on codes of any value)
     M, K = 96, 2048
     wl = _workload(4, M, K, T, 77 + T)
     rng = np.random.default_rng(9 + T)
@@ -621,13 +622,80 @@ def test_q4_offset_operands_on_zero_and_sparse_rows(T):
     scales[:16] = np.float16(1000.0).view(np.uint16)
     qm = wq.QMat(4, codes, scales)
     y = torch.full((T, M), float("nan"), device="cuda")
-    wq.qmat_run(qm.handle, _x_dev(xb), y, T=T)
+    wq.qmat_run_ex(qm.handle, _x_dev(xb), y, T, route=wq.QMAT_ROUTE_MFMA_OFFSET)
     torch.cuda.synchronize()
     got = y.cpu().numpy()
     assert np.all(got[:, :16] == 0)
     worst = _check_y(y, qi.Workload("q4s", 4, M, K, T, codes, scales, xb), f"q4 sparse rows T={T}")
     say(f"q4 sparse rows T={T}: worst ratio {worst:.3g}")
     qm.close()
+
+
+def test_default_route_keeps_the_bound_on_adversarial_q4_rows():
+    # rows with half their codes zero, activations of 2^12 exactly on those zero codes and 2^-6
+    # elsewhere: sum|w x| only sees the small products.  The automatic route (two's complement
+    # operands) keeps the bound at T = 1-8, one and two tiles per wave; the offset-operand
+    # route's sums see the large activations, and its ratio to the bound is reported only.
+    M, K = 128, 1024
+    rng = np.random.default_rng(123)
+    codes = rng.integers(1, 8, (M, K)).astype(np.int8) * np.where(rng.random((M, K)) < 0.5, -1, 1).astype(np.int8)
+    zero = rng.random(K) < 0.5
+    codes[:, zero] = 0
+    scales = np.full((M, K // 64), np.float16(0.5)).view(np.uint16)
+    qm = wq.QMat(4, codes, scales)
+    for T in (1, 4, 8):
+        x = np.where(zero, 2.0 ** 12, 2.0 ** -6).astype(np.float32)[None, :].repeat(T, 0)
+        x *= np.where(rng.random((T, K)) < 0.5, -1.0, 1.0)
+        xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        wl = qi.Workload("adv", 4, M, K, T, codes, scales, xb)
+        ya = torch.full((T, M), float("nan"), device="cuda")
+        yp = torch.full((T, M), float("nan"), device="cuda")
+        yo = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run(qm.handle, _x_dev(xb), ya, T=T)
+        wq.qmat_run_plan(qm.handle, _x_dev(xb), yp, wq.qmat_plan(wq.QMAT_ROUTE_MFMA, 1, 2, 1, 0, 1, 2), T=T)
+        wq.qmat_run_ex(qm.handle, _x_dev(xb), yo, T, route=wq.QMAT_ROUTE_MFMA_OFFSET)
+        torch.cuda.synchronize()
+        worst = _check_y(ya, wl, f"automatic route T={T}")
+        _check_y(yp, wl, f"automatic route pair plan T={T}")
+        y_ref, A = oracle.gemv(4, codes, scales, xb)
+        _, off_worst, _ = oracle.check(yo.cpu().numpy().astype(np.float64), y_ref, A)
+        say(f"adversarial Q4 T={T}: automatic route worst ratio {worst:.3g}, offset-operand route {off_worst:.3g}")
+    qm.close()
+
+
+@pytest.mark.parametrize("fmt", [4, 5, 8])
+def test_offset_route_parity_and_shared_kernels(fmt):
+    # QMAT_ROUTE_MFMA_OFFSET: in tolerance on random inputs, one tile per wave and two (the
+    # same bits), and bit-exact on exact-arithmetic inputs at every T; for every format but Q4,
+    # and for Q4 above 8 tokens, it runs the automatic route's kernels (the same bits)
+    M, K = 200, 1536
+    for T in (1, 3, 6, 8, 12):
+        wl = _workload(fmt, M, K, T, 300 + T)
+        qm = wq.QMat(fmt, wl.codes, wl.scales)
+        yo = torch.full((T, M), float("nan"), device="cuda")
+        ya = torch.full((T, M), float("nan"), device="cuda")
+        y1 = torch.full((T, M), float("nan"), device="cuda")
+        y2 = torch.full((T, M), float("nan"), device="cuda")
+        wq.qmat_run_ex(qm.handle, _x_dev(wl.x), yo, T, route=wq.QMAT_ROUTE_MFMA_OFFSET)
+        wq.qmat_run(qm.handle, _x_dev(wl.x), ya, T=T)
+        p = wq.qmat_get_plan(qm.handle, T, wq.QMAT_ROUTE_MFMA_OFFSET)
+        assert p.route == wq.QMAT_ROUTE_MFMA_OFFSET
+        wq.qmat_run_plan(qm.handle, _x_dev(wl.x), y1, wq.qmat_plan(wq.QMAT_ROUTE_MFMA_OFFSET, 1, 2, 1, 0, 1, 1), T=T)
+        wq.qmat_run_plan(qm.handle, _x_dev(wl.x), y2, wq.qmat_plan(wq.QMAT_ROUTE_MFMA_OFFSET, 1, 2, 1, 0, 1, 2), T=T)
+        torch.cuda.synchronize()
+        _check_y(yo, wl, f"offset fmt={fmt} T={T}")
+        assert torch.equal(y1, y2)
+        if fmt != 4 or T > 8:
+            assert torch.equal(yo, ya)
+        qm.close()
+        ex = _exact_workload(fmt, 130, 1024, T, 7 + T)
+        qe = wq.QMat(fmt, ex.codes, ex.scales)
+        ye = torch.empty((T, 130), device="cuda")
+        wq.qmat_run_ex(qe.handle, _x_dev(ex.x), ye, T, route=wq.QMAT_ROUTE_MFMA_OFFSET)
+        torch.cuda.synchronize()
+        y_ref, _ = oracle.gemv(fmt, ex.codes, ex.scales, ex.x)
+        assert np.array_equal(ye.cpu().numpy().astype(np.float64), y_ref)
+        qe.close()
 
 
 # FP8 row scales the API accepts (any finite fp32) that the seeded workloads never produce:

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libqmat.so")
 
 QMAT_OK, QMAT_EINVAL, QMAT_ESHAPE, QMAT_ERANGE, QMAT_ESIZE, QMAT_EHIP, QMAT_ENOMEM = range(7)
 QMAT_Q4, QMAT_Q5, QMAT_Q6, QMAT_FP8_E4M3_ROW, QMAT_Q8 = 4, 5, 6, 8, 9
-QMAT_ROUTE_AUTO, QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA, QMAT_ROUTE_GEMM = 0, 1, 2, 3
+QMAT_ROUTE_AUTO, QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA, QMAT_ROUTE_GEMM, QMAT_ROUTE_MFMA_OFFSET = 0, 1, 2, 3, 4
 QMAT_ENCODE_RTN, QMAT_ENCODE_GROUPED_SEARCH = 0, 1
 FORMATS = (QMAT_Q4, QMAT_Q5, QMAT_Q6, QMAT_FP8_E4M3_ROW, QMAT_Q8)
 MAX_T = 16

@@ -25,7 +25,8 @@ namespace {
 
 struct Plan {
     int route, depth, waves, splits, tail_tiles, tail_splits;
-    int tiles = 1;  // row tiles per wave (2: mfma_pair_kernel)
+    int tiles = 1;            // row tiles per wave (2: mfma_pair_kernel)
+    bool offset_ops = false;  // MFMA route: Q4 up to 8 tokens as offset-binary operands
 };
 
 // Launch shape for one (route, tokens-per-launch), from graph-timed sweeps of depth x waves x
@@ -401,7 +402,7 @@ int run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const Plan &p, vo
         a.S = p.splits;
         a.NTt = p.tail_tiles;
         a.St = tail_splits;
-        const hipError_t e = launch_run(h->fmt, p.route, p.depth, a, p.waves, p.tiles, st);
+        const hipError_t e = launch_run(h->fmt, p.route, p.depth, a, p.waves, p.tiles, p.offset_ops, st);
         if (e != hipSuccess) return fail(QMAT_EHIP, "qmat_run: launch failed: %s", hipGetErrorString(e));
     }
     return ok();
@@ -413,7 +414,8 @@ int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int
                 void *stream)
 {
     if (!h) return fail(QMAT_EINVAL, "qmat_run: null handle");
-    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_GEMM) return fail(QMAT_EINVAL, "qmat_run: bad route %d", route);
+    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA_OFFSET)
+        return fail(QMAT_EINVAL, "qmat_run: bad route %d", route);
     if (route == QMAT_ROUTE_GEMM || (route == QMAT_ROUTE_AUTO && T > kMaxT))
         return run_gemm(h, x_dev, y_dev, T, splits, stream);
     if (T < 0 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_run: T=%d outside [0,%d] on this route", T, kMaxT);
@@ -424,6 +426,7 @@ int qmat_run_ex(qmat_t h, const void *x_dev, float *y_dev, int T, int route, int
     if (depth < 0 || depth > kMaxDepth) return fail(QMAT_EINVAL, "qmat_run: depth must be 0..%d", kMaxDepth);
     const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
     Plan p = h->plan[r - 1][T];
+    p.offset_ops = route == QMAT_ROUTE_MFMA_OFFSET;
     if (depth) p.depth = depth;
     if (waves) p.waves = waves;
     if (splits) {
@@ -442,17 +445,20 @@ int qmat_run_plan(qmat_t h, const void *x_dev, float *y_dev, int T, const qmat_p
         if (plan->splits < 1) return fail(QMAT_EINVAL, "qmat_run_plan: splits must be >= 1");
         return run_gemm(h, x_dev, y_dev, T, plan->splits, stream);
     }
-    if (plan->route != QMAT_ROUTE_VALU && plan->route != QMAT_ROUTE_MFMA)
-        return fail(QMAT_EINVAL, "qmat_run_plan: route must be QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA or QMAT_ROUTE_GEMM");
+    if (plan->route != QMAT_ROUTE_VALU && plan->route != QMAT_ROUTE_MFMA && plan->route != QMAT_ROUTE_MFMA_OFFSET)
+        return fail(QMAT_EINVAL,
+                    "qmat_run_plan: route must be QMAT_ROUTE_VALU, QMAT_ROUTE_MFMA, QMAT_ROUTE_MFMA_OFFSET or QMAT_ROUTE_GEMM");
     const Plan p{plan->route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma, plan->depth, plan->waves, plan->splits,
-                 plan->tail_tiles, plan->tail_splits, plan->tiles == 0 ? 1 : plan->tiles};
+                 plan->tail_tiles, plan->tail_splits, plan->tiles == 0 ? 1 : plan->tiles,
+                 plan->route == QMAT_ROUTE_MFMA_OFFSET};
     return run_plan(h, x_dev, y_dev, T, p, stream);
 }
 
 int qmat_get_plan(qmat_t h, int T, int route, qmat_plan *plan)
 {
     if (!h || !plan) return fail(QMAT_EINVAL, "qmat_get_plan: null argument");
-    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_GEMM) return fail(QMAT_EINVAL, "qmat_get_plan: bad route %d", route);
+    if (route < QMAT_ROUTE_AUTO || route > QMAT_ROUTE_MFMA_OFFSET)
+        return fail(QMAT_EINVAL, "qmat_get_plan: bad route %d", route);
     if (route == QMAT_ROUTE_GEMM || (route == QMAT_ROUTE_AUTO && T > kMaxT)) {
         if (T < 1 || T > kGemmMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kGemmMaxT);
         *plan = qmat_plan{QMAT_ROUTE_GEMM, 1, 4, gemm_auto_splits(h->NT, h->NU, T, h->cus, h->ws_floats), 0, 1, 1};
@@ -461,7 +467,7 @@ int qmat_get_plan(qmat_t h, int T, int route, qmat_plan *plan)
     if (T < 1 || T > kMaxT) return fail(QMAT_ESHAPE, "qmat_get_plan: T=%d outside [1,%d]", T, kMaxT);
     const int r = route == QMAT_ROUTE_AUTO ? auto_route(h->fmt, T) : route == QMAT_ROUTE_VALU ? kRouteValu : kRouteMfma;
     const Plan &p = h->plan[r - 1][T];
-    plan->route = r == kRouteValu ? QMAT_ROUTE_VALU : QMAT_ROUTE_MFMA;
+    plan->route = r == kRouteValu ? QMAT_ROUTE_VALU : route == QMAT_ROUTE_MFMA_OFFSET ? QMAT_ROUTE_MFMA_OFFSET : QMAT_ROUTE_MFMA;
     plan->depth = p.depth;
     plan->waves = p.waves;
     plan->splits = p.splits;

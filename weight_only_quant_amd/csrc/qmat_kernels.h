@@ -51,7 +51,10 @@ constexpr int kValuMaxT = 4;
 constexpr int kMaxDepth = 2;
 // tiles: row tiles per wave, 1 or 2 (2: MFMA route and a.NTt == 0 only; the grid is then
 // ceil(NT / 2) * S workgroups).
-hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, int tiles, hipStream_t stream);
+// offset_ops: on the MFMA route, Q4 up to 8 tokens takes offset-binary operands (every other
+// case, and every case without it, takes two's complement operands).
+hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, int tiles, bool offset_ops,
+                      hipStream_t stream);
 hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t stream);
 
 

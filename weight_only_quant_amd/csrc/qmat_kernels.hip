@@ -454,9 +454,13 @@ __device__ __forceinline__ void mfma_step(const Unit<NB, XN> &U, f32x4_t (&D)[4]
 }
 
 // Whether an MFMA kernel with TR token slots per lane uses the offset Q4 operands (two extra
-// matrix instructions and TR subtractions per row slice and group) or the signed ones: offset
-// where the shorter unpack pays for that, up to 8 tokens.
-template <int FMT, int TR> constexpr bool mfma_offset() { return Fmt<FMT>::kOffset != 0.0f && TR < 4; }
+// matrix instructions and TR subtractions per row slice and group, 7 instead of 13 unpack
+// instructions per 8 codes): only when the launch asks for them (OFS), and only up to 8 tokens,
+// where the shorter unpack pays for the rest.
+template <int FMT, int TR, bool OFS> constexpr bool mfma_offset()
+{
+    return Fmt<FMT>::kOffset != 0.0f && TR < 4 && OFS;
+}
 
 // A operand: 16 token slots x 32 k (lane l: slot l % 16, k octet l / 16); B operand: 32 k x 16
 // rows of the tile (lane l: row 16*m + l % 16, the same k octet) — exactly the packed layout.
@@ -471,7 +475,7 @@ template <int TR> __device__ __forceinline__ int slot_token(int slot)
     return (slot & 3) < TR ? TR * (slot >> 2) + (slot & 3) : 16;  // 16: no token
 }
 
-template <int FMT, int D_, int TR>
+template <int FMT, int D_, int TR, bool OFS>
 __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
 {
     constexpr int NB = Fmt<FMT>::NB, XN = 4;
@@ -485,7 +489,7 @@ __global__ __launch_bounds__(512) void mfma_kernel(RunArgs a)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.x), (short)0, 2 * a.T * a.K, kRawBufferWord3);
     const uint32_t xoff = tok < a.T ? 2u * (uint32_t)(tok * a.K) + 16u * oct : kPastEnd;
-    constexpr bool OFF = mfma_offset<FMT, TR>();
+    constexpr bool OFF = mfma_offset<FMT, TR, OFS>();
     f32x4_t acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -575,7 +579,7 @@ template <int NB> struct PairUnit {
     u32x4_t x[4];
 };
 
-template <int FMT, int D_, int TR>
+template <int FMT, int D_, int TR, bool OFS>
 __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
 {
     constexpr int NB = Fmt<FMT>::NB;
@@ -588,7 +592,7 @@ __global__ __launch_bounds__(512) void mfma_pair_kernel(RunArgs a)
         const_cast<uint16_t *>(a.x), (short)0, 2 * a.T * a.K, kRawBufferWord3);
     const uint32_t xoff = tok < a.T ? 2u * (uint32_t)(tok * a.K) + 16u * oct : kPastEnd;
     const int tile0 = 2 * pair, tile1 = 2 * pair + 1 < a.NT ? 2 * pair + 1 : 2 * pair;
-    constexpr bool OFF = mfma_offset<FMT, TR>();
+    constexpr bool OFF = mfma_offset<FMT, TR, OFS>();
     f32x4_t acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -752,18 +756,25 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a)
 
 // ------------------------------------------------------------------ launchers
 
-template <int FMT, int D> static const void *run_kernel_d(int route, int T, int tiles)
+// The MFMA kernel for T tokens: token slots per lane and row group 1 up to 4 tokens, 2 up to 8,
+// 4 up to 16; the offset operands (ofs) only change the Q4 kernels up to 8 tokens, so the other
+// formats and T share one instantiation.
+template <int FMT, int D, int TR> static const void *mfma_kernel_for(int tiles, bool ofs)
 {
-    if (route == kRouteMfma) {
-        // token slots per lane and row group: 1 up to 4 tokens, 2 up to 8, 4 up to 16
-        if (tiles == 2)
-            return T <= 4 ? reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D, 1>)
-                 : T <= 8 ? reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D, 2>)
-                          : reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D, 4>);
-        return T <= 4 ? reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 1>)
-             : T <= 8 ? reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 2>)
-                      : reinterpret_cast<const void *>(&mfma_kernel<FMT, D, 4>);
-    }
+    constexpr bool kOfsDiffers = mfma_offset<FMT, TR, true>();
+    if (ofs && kOfsDiffers)
+        return tiles == 2 ? reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D, TR, kOfsDiffers>)
+                          : reinterpret_cast<const void *>(&mfma_kernel<FMT, D, TR, kOfsDiffers>);
+    return tiles == 2 ? reinterpret_cast<const void *>(&mfma_pair_kernel<FMT, D, TR, false>)
+                      : reinterpret_cast<const void *>(&mfma_kernel<FMT, D, TR, false>);
+}
+
+template <int FMT, int D> static const void *run_kernel_d(int route, int T, int tiles, bool ofs)
+{
+    if (route == kRouteMfma)
+        return T <= 4 ? mfma_kernel_for<FMT, D, 1>(tiles, ofs)
+             : T <= 8 ? mfma_kernel_for<FMT, D, 2>(tiles, ofs)
+                      : mfma_kernel_for<FMT, D, 4>(tiles, ofs);
     if (tiles == 2) return nullptr;
     switch (T) {
     case 1: return reinterpret_cast<const void *>(&valu_kernel<FMT, 1, D>);
@@ -774,23 +785,23 @@ template <int FMT, int D> static const void *run_kernel_d(int route, int T, int 
     }
 }
 
-template <int FMT> static const void *run_kernel(int route, int T, int depth, int tiles)
+template <int FMT> static const void *run_kernel(int route, int T, int depth, int tiles, bool ofs)
 {
     switch (depth) {
-    case 1: return run_kernel_d<FMT, 1>(route, T, tiles);
-    case 2: return run_kernel_d<FMT, 2>(route, T, tiles);
+    case 1: return run_kernel_d<FMT, 1>(route, T, tiles, ofs);
+    case 2: return run_kernel_d<FMT, 2>(route, T, tiles, ofs);
     default: return nullptr;
     }
 }
 
-static const void *run_kernel_for(int fmt, int route, int T, int depth, int tiles)
+static const void *run_kernel_for(int fmt, int route, int T, int depth, int tiles, bool ofs)
 {
     switch (fmt) {
-    case 4: return run_kernel<4>(route, T, depth, tiles);
-    case 5: return run_kernel<5>(route, T, depth, tiles);
-    case 6: return run_kernel<6>(route, T, depth, tiles);
-    case 8: return run_kernel<8>(route, T, depth, tiles);
-    case 9: return run_kernel<9>(route, T, depth, tiles);
+    case 4: return run_kernel<4>(route, T, depth, tiles, ofs);
+    case 5: return run_kernel<5>(route, T, depth, tiles, ofs);
+    case 6: return run_kernel<6>(route, T, depth, tiles, ofs);
+    case 8: return run_kernel<8>(route, T, depth, tiles, ofs);
+    case 9: return run_kernel<9>(route, T, depth, tiles, ofs);
     default: return nullptr;
     }
 }
@@ -803,10 +814,11 @@ static size_t run_lds_bytes(int waves, int T, bool shared)
 }
 
 
-hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, int tiles, hipStream_t st)
+hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves, int tiles, bool offset_ops,
+                      hipStream_t st)
 {
     if (tiles == 2 && a.NTt != 0) return hipErrorInvalidValue;
-    const void *k = run_kernel_for(fmt, route, a.T, depth, tiles);
+    const void *k = run_kernel_for(fmt, route, a.T, depth, tiles, offset_ops);
     if (!k) return hipErrorInvalidValue;
     RunArgs arg = a;
     void *args[] = {&arg};
@@ -818,7 +830,7 @@ hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves
 
 int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int NU, int S)
 {
-    const void *k = run_kernel_for(fmt, route, T, depth, 1);
+    const void *k = run_kernel_for(fmt, route, T, depth, 1, false);
     int n = 0;
     if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 64 * waves, run_lds_bytes(waves, T, S > 1)) !=
                   hipSuccess)
