@@ -5,7 +5,8 @@ dot products, group scales, reductions, write y) on resident device buffers.  Th
 workload is the Q4 fused MLP gate+up projection (two 17408 x 5120 matrices as one
 M=34816, K=5120 matrix) at T=1; the other benchmark shapes (Q6 vocab head, Q5 down
 projection with split-K, FP8 row-scaled head and projection, the 8-bit heads, the small Q4
-case) at each of their token counts are reported in "extra".
+case) at each of their token counts are reported in "extra", and so is the gate+up matrix on the
+explicit offset-operand route (QMAT_ROUTE_MFMA_OFFSET, "_offset_route").
 
 Throughput is algorithmic bytes (packed codes + scales read once, x read, y written) per
 second.  Matrices smaller than 512 MB rotate over enough device copies to exceed 512 MB so
@@ -98,9 +99,9 @@ class Resident:
 
 class Timed:
     """n launches of one decode workload captured in one HIP graph (rotating over the
-    resident copies), replayed on the current stream."""
+    resident copies), replayed on the current stream; route 0 is the automatic route."""
 
-    def __init__(self, res, T, n):
+    def __init__(self, res, T, n, route=0):
         import gc
         import torch
         import weight_only_quant_amd as wq
@@ -112,7 +113,10 @@ class Timed:
         self.g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.g):
             for i in range(n):
-                wq.qmat_run(hs[i % len(hs)], x, y, T=T)
+                if route:
+                    wq.qmat_run_ex(hs[i % len(hs)], x, y, T, route=route)
+                else:
+                    wq.qmat_run(hs[i % len(hs)], x, y, T=T)
         torch.cuda.synchronize()
 
     def warm(self, seconds):
@@ -155,11 +159,11 @@ def plan_str(res, T, route=0):
     p = wq.qmat_get_plan(res.handles[0], T, route)
     tail = f" tail_tiles={p.tail_tiles} tail_splits={p.tail_splits}" if p.tail_tiles else ""
     tiles = f" tiles={p.tiles}" if p.tiles > 1 else ""
-    return (f"{'valu' if p.route == wq.QMAT_ROUTE_VALU else 'mfma'} depth={p.depth} waves={p.waves} "
-            f"splits={p.splits}{tail}{tiles}")
+    name = {wq.QMAT_ROUTE_VALU: "valu", wq.QMAT_ROUTE_MFMA_OFFSET: "mfma-offset"}.get(p.route, "mfma")
+    return f"{name} depth={p.depth} waves={p.waves} splits={p.splits}{tail}{tiles}"
 
 
-def line(res, T, us_list, per_round, single):
+def line(res, T, us_list, per_round, single, route=0):
     """A decode line from per-launch times (µs) of all timed replays, with the single-launch
     event times beside it."""
     wl = res.wl
@@ -168,14 +172,14 @@ def line(res, T, us_list, per_round, single):
     return {"us_per_call": round(us, 3), "us_min": round(min(us_list), 3), "us_max": round(max(us_list), 3),
             "us_round_medians": [round(v, 3) for v in per_round], "timed_replays": len(us_list),
             "GBps": round(ab / us / 1e3, 1), "pct_hbm_peak": round(100 * ab / us / 1e3 / HBM_PEAK_GBS, 2),
-            "bytes": ab, "plan": plan_str(res, T), "single_launch_us": single}
+            "bytes": ab, "plan": plan_str(res, T, route), "single_launch_us": single}
 
 
 SINGLE_WARM = 20   # eager launches before the single-launch timings of a line
 SINGLE_N = 40      # single launches timed per line
 
 
-def single_launch(res, T):
+def single_launch(res, T, route=0):
     """Each of SINGLE_N eager launches alone on an idle stream, bracketed by events and
     synchronized after: median, 10th and 90th percentile of the event time (µs).  This is the
     latency of one call on its own (dispatch and ramp-up included), beside the back-to-back
@@ -184,14 +188,20 @@ def single_launch(res, T):
     import weight_only_quant_amd as wq
     hs, x, y = res.handles, res.x[:T], res.y[:T]
     stream = torch.cuda.current_stream()
+    def run(h):
+        if route:
+            wq.qmat_run_ex(h, x, y, T, route=route)
+        else:
+            wq.qmat_run(h, x, y, T=T)
+
     for i in range(SINGLE_WARM):
-        wq.qmat_run(hs[i % len(hs)], x, y, T=T)
+        run(hs[i % len(hs)])
     torch.cuda.synchronize()
     us = []
     for i in range(SINGLE_N):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        wq.qmat_run(hs[(SINGLE_WARM + i) % len(hs)], x, y, T=T)
+        run(hs[(SINGLE_WARM + i) % len(hs)])
         b.record(stream)
         torch.cuda.synchronize()
         us.append(a.elapsed_time(b) * 1e3)
@@ -200,18 +210,18 @@ def single_launch(res, T):
 
 
 def measure_decode(lines, steps):
-    """Every (Resident, T) in `lines`, ROUNDS rounds alternating forward / reverse order; each
-    round warms the line for WARM_S and times REPLAYS replays of a graph of >= MIN_CALLS
+    """Every (Resident, T, route) in `lines`, ROUNDS rounds alternating forward / reverse order;
+    each round warms the line for WARM_S and times REPLAYS replays of a graph of >= MIN_CALLS
     launches."""
     times = {i: [] for i in range(len(lines))}
     rounds = {i: [] for i in range(len(lines))}
     for r in range(ROUNDS):
         order = range(len(lines)) if r % 2 == 0 else reversed(range(len(lines)))
         for i in order:
-            res, T = lines[i]
+            res, T, route = lines[i]
             # every rotation copy at least once per replay (the small matrix has thousands)
             n = max(MIN_CALLS, steps, min(len(res.handles), 4096))
-            tm = Timed(res, T, n)
+            tm = Timed(res, T, n, route)
             tm.warm(WARM_S)
             us = [tm.time_once() * 1e3 for _ in range(REPLAYS)]
             tm.close()
@@ -219,10 +229,10 @@ def measure_decode(lines, steps):
             rounds[i].append(float(np.median(us)))
             log(f"[bench] round {r} {res.name} T={T}: {np.median(us):.3f} us/call")
     single = {}
-    for i, (res, T) in enumerate(lines):
-        single[i] = single_launch(res, T)
-        log(f"[bench] single launch {res.name} T={T}: {single[i]}")
-    return {i: line(lines[i][0], lines[i][1], times[i], rounds[i], single[i]) for i in range(len(lines))}
+    for i, (res, T, route) in enumerate(lines):
+        single[i] = single_launch(res, T, route)
+        log(f"[bench] single launch {res.name} T={T} route={route}: {single[i]}")
+    return {i: line(lines[i][0], lines[i][1], times[i], rounds[i], single[i], lines[i][2]) for i in range(len(lines))}
 
 
 def measure_epilogue(res, T, k, warm_s=WARM_S, n=MIN_CALLS, with_product=False):
@@ -403,7 +413,7 @@ def main():
     ap.add_argument("--profile-lines", default=None,
                     help="only run these decode lines (name:T,...), --warmup then --steps eager launches "
                          "each, for counter profilers")
-    ap.add_argument("--route", choices=("auto", "valu", "mfma"), default="auto",
+    ap.add_argument("--route", choices=("auto", "valu", "mfma", "offset"), default="auto",
                     help="small-T route of the --profile-lines launches")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -428,7 +438,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wq.lib()
     if args.profile_lines:
-        route = {"auto": wq.QMAT_ROUTE_AUTO, "valu": wq.QMAT_ROUTE_VALU, "mfma": wq.QMAT_ROUTE_MFMA}[args.route]
+        route = {"auto": wq.QMAT_ROUTE_AUTO, "valu": wq.QMAT_ROUTE_VALU, "mfma": wq.QMAT_ROUTE_MFMA,
+                 "offset": wq.QMAT_ROUTE_MFMA_OFFSET}[args.route]
         for item in args.profile_lines.split(","):
             pname, pT = item.split(":")
             pT = int(pT)
@@ -531,13 +542,17 @@ def main():
         names = [n for n in names if n in args.only.split(",")]
     for n in names:
         residents[n] = Resident(n)
-    lines = [(res, T2) for T2 in qi.CONFIGS[name][3] if T2 != T]
+    lines = [(res, T2, 0) for T2 in qi.CONFIGS[name][3] if T2 != T]
     for n in names:
-        lines += [(residents[n], T2) for T2 in qi.CONFIGS[n][3]]
+        lines += [(residents[n], T2, 0) for T2 in qi.CONFIGS[n][3]]
+    # the explicit offset-operand route (QMAT_ROUTE_MFMA_OFFSET) on the Q4 gate+up matrix,
+    # beside the automatic route's lines
+    lines += [(res, T2, wq.QMAT_ROUTE_MFMA_OFFSET) for T2 in qi.CONFIGS[name][3]]
     results = measure_decode(lines, args.steps)
-    for i, (r, T2) in enumerate(lines):
-        extra[f"{r.name}_T{T2}"] = results[i]
-        log(f"[bench] {r.name} T={T2}: {results[i]}")
+    for i, (r, T2, route) in enumerate(lines):
+        key = f"{r.name}_T{T2}" + ("_offset_route" if route else "")
+        extra[key] = results[i]
+        log(f"[bench] {key}: {results[i]}")
 
     # the output-head epilogue on the Q6 head's logits (the last product left them in y)
     if "q6_head_248320x5120" in residents:
