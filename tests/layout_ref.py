@@ -41,9 +41,10 @@ def unpack(fmt, M, K, blob):
             rows = (64 * t_idx + 16 * m + r16[None, None, :])  # [NT,1,64]
             for e in range(8):
                 if fmt == 4:
-                    # byte e % 4, low nibble for e < 4 and high nibble above, offset binary
+                    # byte e % 4, low nibble for e < 4 and high nibble above, two's complement
                     n = W[..., 4 * ka + m]
-                    v = ((n >> np.uint32(8 * (e % 4) + 4 * (e // 4))) & np.uint32(0xF)).astype(np.int32) - 8
+                    v = ((n >> np.uint32(8 * (e % 4) + 4 * (e // 4))) & np.uint32(0xF)).astype(np.int32)
+                    v = np.where(v >= 8, v - 16, v)
                 elif fmt == 5:
                     o = 2 * m + e // 4
                     i = e % 4

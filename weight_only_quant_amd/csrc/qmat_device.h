@@ -81,12 +81,11 @@ template <int FMT, int KA, int MM>
 __device__ __forceinline__ void codes8(const uint32_t *W, float (&f)[8])
 {
     if constexpr (FMT == 4) {
-        // e = i sits in bits [3:0] of byte i, e = 4 + i in bits [7:4], offset binary: flipping
-        // every nibble's top bit gives two's complement nibbles, which v_cvt_off_f32_i4 reads
-        // (the low four bits of the byte SDWA selects) as code/16; the high nibbles take one
+        // e = i sits in bits [3:0] of byte i, e = 4 + i in bits [7:4]; v_cvt_off_f32_i4 reads
+        // the low four bits of the byte SDWA selects as code/16, so the high nibbles take one
         // rotate (a rotate rather than a shift keeps h opaque to the compiler, so its bytes are
         // SDWA-selected too instead of being re-extracted from n)
-        const uint32_t n = W[4 * KA + MM] ^ 0x88888888u, h = __builtin_amdgcn_alignbit(n, n, 4);
+        const uint32_t n = W[4 * KA + MM], h = __builtin_amdgcn_alignbit(n, n, 4);
         f[0] = nib_lo<0>(n); f[1] = nib_lo<1>(n);
         f[2] = nib_lo<2>(n); f[3] = nib_lo<3>(n);
         f[4] = nib_lo<0>(h); f[5] = nib_lo<1>(h);
@@ -143,11 +142,12 @@ template <bool SEL> __device__ __forceinline__ uint32_t e4m3_pair(uint32_t w)
 // (code + kOffset) / kToCode, FP8 the E4M3 value.
 //
 // Q4: the E4M3 bytes 0..15 are the values v * 2^-9 (0..7 subnormal, 8..15 the first normal
-// binade), so a byte holding an offset-binary nibble v = code + 8 converts to (code + 8) / 512
-// with no arithmetic; masking the low and the high nibbles of a dword gives the 8 bytes, and
-// the converter turns two of them into a bf16 pair per instruction: 7 instructions per 8 codes
-// against 13 for signed nibble converts and packs.  The +8 is taken out of each group's product
-// sum (q4_group_offset).
+// binade), so a byte holding the offset-binary nibble v = code + 8 (the two's complement nibble
+// with its top bit flipped) converts to (code + 8) / 512 with no arithmetic; one XOR and masks
+// of the low and the high nibbles of a dword give the 8 bytes, and the converter turns two of
+// them into a bf16 pair per instruction: 8 instructions per 8 codes against 13 for signed
+// nibble converts and packs.  The +8 is taken out of each group's product sum
+// (q4_group_offset).
 template <int FMT, int KA, int MM>
 __device__ __forceinline__ void bf16x8_of(const uint32_t *W, uint32_t (&b)[4])
 {
@@ -159,7 +159,7 @@ __device__ __forceinline__ void bf16x8_of(const uint32_t *W, uint32_t (&b)[4])
             b[2 * h + 1] = e4m3_pair<true>(w);
         }
     } else if constexpr (FMT == 4) {
-        const uint32_t n = W[4 * KA + MM];
+        const uint32_t n = W[4 * KA + MM] ^ 0x88888888u;
         const uint32_t lo = n & 0x0F0F0F0Fu, hi = (n >> 4) & 0x0F0F0F0Fu;
         b[0] = e4m3_pair<false>(lo);
         b[1] = e4m3_pair<true>(lo);

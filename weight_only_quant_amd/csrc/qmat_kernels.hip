@@ -10,13 +10,12 @@
 // described in qmat_layout.h.  Template parameter FMT is the format id (9 = Q8).
 //
 // Every code is turned into an exact small float before any product is formed:
-//   Q4   on the matrix cores up to 8 tokens: the stored offset-binary nibble (code + 8) is
-//        masked into a byte that v_cvt_scalef32_pk_bf16_fp8 reads as (code + 8) * 2^-9, two
-//        per instruction; each group's product sum then subtracts the same MFMA sum over a
-//        constant operand 8 * 2^-9 (q4_group_offset), which is exactly the sum of the offsets
-//        for a group of zero codes;
-//        elsewhere v_cvt_off_f32_i4 reads the nibble with its top bit flipped (two's
-//        complement) as code/16 (SDWA picks the byte);
+//   Q4   v_cvt_off_f32_i4 reads a two's-complement nibble as code/16 (SDWA picks the byte);
+//        on request (the offset-operand route, up to 8 tokens) the nibble with its top bit
+//        flipped (code + 8) is masked into a byte that v_cvt_scalef32_pk_bf16_fp8 reads as
+//        (code + 8) * 2^-9, two per instruction, and each group's product sum then subtracts
+//        the same MFMA sum over a constant operand 8 * 2^-9 (q4_group_offset), which is exactly
+//        the sum of the offsets for a group of zero codes;
 //   Q5/6 the code is assembled in the top bits of a byte and v_cvt_f32_i32 with SDWA sign
 //        extension reads it as 8*code or 4*code;
 //   Q8   the same SDWA convert reads each stored byte as the code;
@@ -24,8 +23,8 @@
 // These values are exact in bf16, so bf16(code) * bf16(x) is an exact product; dot products
 // accumulate in fp32 (v_dot2c_f32_bf16 on the vector ALU, or the 16x16x32 bf16 MFMA), and the
 // per-group scale (times the power of two of the code encoding) is applied once per 64-group.
-// The Q4 offset costs accuracy only on rows whose codes are almost all zero: its rounding
-// scales with the group's sum of activations instead of its sum of products.
+// The Q4 offset operands round at the size of the group's sum of activations instead of its
+// sum of products, so they are an explicit request and not the automatic route.
 //
 // Work split: a wave owns one 64-row tile and a contiguous range of 128-wide k units.  NW waves
 // of a workgroup split a tile's units and reduce through LDS; S workgroups split further and

@@ -12,9 +12,9 @@
 // (W[4*j + d] = dword d of block j):
 //
 //   Q4  (NB 4): W[4*kappa + m] holds the 8 codes of row m: byte i has e = i in bits [3:0]
-//               and e = 4 + i in bits [7:4], each as the offset-binary nibble code + 8 (the
-//               two's complement nibble with its top bit flipped), so that masking the low or
-//               the high nibbles leaves bytes that read as E4M3 values (code + 8) * 2^-9.
+//               and e = 4 + i in bits [7:4], two's complement nibbles (flipping every
+//               nibble's top bit and masking the low or the high nibbles leaves bytes that read
+//               as E4M3 values (code + 8) * 2^-9: the offset-operand route).
 //   Q5  (NB 5): W[5*kappa + 0..4] = X0 X1 X2 X3 E.  Output dword o (0..7) carries the codes of
 //               row o/2, e = 4*(o%2) + i in byte i, each byte = code << 3 (a signed byte worth
 //               8*code).  O_d = X_d & 0xF8F8F8F8 for d < 4; for d < 4 the low 3 bits of each byte

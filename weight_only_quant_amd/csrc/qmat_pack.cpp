@@ -49,12 +49,10 @@ void pack_tile(const PackSrc &p, int64_t tile, uint8_t *out)
             memset(W, 0, sizeof(W));
             for (int ka = 0; ka < 4; ++ka) {
                 if (fmt == 4) {
-                    // byte i: e = i in bits [3:0], e = 4 + i in bits [7:4], offset binary
-                    // (the two's complement nibble with its top bit flipped: code + 8)
+                    // byte i: e = i in bits [3:0], e = 4 + i in bits [7:4], two's complement
                     for (int m = 0; m < 4; ++m) {
                         uint32_t n = 0;
-                        for (int i = 0; i < 4; ++i)
-                            n |= ((c(m, ka, i) ^ 8u) | ((c(m, ka, 4 + i) ^ 8u) << 4)) << (8 * i);
+                        for (int i = 0; i < 4; ++i) n |= (c(m, ka, i) | (c(m, ka, 4 + i) << 4)) << (8 * i);
                         W[4 * ka + m] = n;
                     }
                 } else if (fmt == 5) {
