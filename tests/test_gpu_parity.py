@@ -663,6 +663,37 @@ def test_default_route_keeps_the_bound_on_adversarial_q4_rows():
     qm.close()
 
 
+@pytest.mark.parametrize("fmt", [5, 6, 8, qi.Q8])
+@pytest.mark.parametrize("T", [1, 8, 16])
+def test_automatic_route_keeps_the_bound_next_to_large_activations_on_zero_codes(fmt, T):
+    # the same adversarial input for every other format: zero codes (FP8: +0 and -0 bytes)
+    # under activations of 2^12, small products elsewhere; a zero code contributes an exact 0
+    # on the signed operands, so the bound holds however large its activation
+    M, K = 96, 1024
+    rng = np.random.default_rng(200 + fmt + T)
+    zero = rng.random(K) < 0.5
+    if fmt == 8:
+        mag = rng.integers(0x20, 0x58, (M, K)).astype(np.uint8)
+        codes = mag | np.where(rng.random((M, K)) < 0.5, 0x80, 0x00).astype(np.uint8)
+        codes[:, zero] = np.where(rng.random((M, int(zero.sum()))) < 0.5, 0x00, 0x80).astype(np.uint8)
+        scales = np.full(M, 0.25, np.float32)
+    else:
+        qmax = (1 << (qi.code_bits(fmt) - 1)) - 1
+        codes = rng.integers(1, qmax + 1, (M, K)).astype(np.int8) * np.where(rng.random((M, K)) < 0.5, -1, 1).astype(np.int8)
+        codes[:, zero] = 0
+        scales = np.full((M, K // 64), np.float16(0.5)).view(np.uint16)
+    x = np.where(zero, 2.0 ** 12, 2.0 ** -6).astype(np.float32)[None, :].repeat(T, 0)
+    x *= np.where(rng.random((T, K)) < 0.5, -1.0, 1.0)
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    qm = wq.QMat(fmt, codes, scales)
+    y = torch.full((T, M), float("nan"), device="cuda")
+    wq.qmat_run(qm.handle, _x_dev(xb), y, T=T)
+    torch.cuda.synchronize()
+    worst = _check_y(y, qi.Workload("adv", fmt, M, K, T, codes, scales, xb), f"adversarial fmt={fmt} T={T}")
+    say(f"adversarial fmt={fmt} T={T}: worst ratio {worst:.3g}")
+    qm.close()
+
+
 @pytest.mark.parametrize("fmt", [4, 5, 8])
 def test_offset_route_parity_and_shared_kernels(fmt):
     # QMAT_ROUTE_MFMA_OFFSET: in tolerance on random inputs, one tile per wave and two (the
