@@ -128,6 +128,18 @@ def test_run_parity_small(route, fmt, M, K):
 
 
 @pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
+def test_valu_plan_depth(fmt):
+    # the vector-ALU route keeps two k units in flight per wave only where both fit in
+    # registers: one token per pass, or two for the 4-, 5- and 6-bit formats (the parity test
+    # above runs every T through these plans)
+    wl = _workload(fmt, 200, 320, 1, 5)
+    qm = wq.QMat(fmt, wl.codes, wl.scales)
+    two = 1 if fmt in (8, qi.Q8) else 2
+    assert [wq.qmat_get_plan(qm.handle, T, wq.QMAT_ROUTE_VALU).depth for T in range(1, 17)] == [2] * two + [1] * (16 - two)
+    qm.close()
+
+
+@pytest.mark.parametrize("fmt", [4, 5, 6, 8, qi.Q8])
 @pytest.mark.parametrize("route,T", [("valu", 1), ("valu", 4), ("mfma", 1), ("mfma", 9)])
 def test_run_split_shapes_agree(fmt, route, T):
     # every (depth, waves, splits) launch shape gives an in-tolerance result; each is
