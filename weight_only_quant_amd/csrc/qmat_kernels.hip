@@ -453,7 +453,7 @@ __device__ __forceinline__ void mfma_step(const Unit<NB, XN> &U, f32x4_t (&D)[4]
 }
 
 // Whether an MFMA kernel with TR token slots per lane uses the offset Q4 operands (two extra
-// matrix instructions and TR subtractions per row slice and group, 7 instead of 13 unpack
+// matrix instructions and TR subtractions per row slice and group, 8 instead of 13 unpack
 // instructions per 8 codes): only when the launch asks for them (OFS), and only up to 8 tokens,
 // where the shorter unpack pays for the rest.
 template <int FMT, int TR, bool OFS> constexpr bool mfma_offset()
