@@ -122,8 +122,8 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
     }
     Plan p{route, 2, NT >= 2048 ? 1 : 4, 1, 0, 1};
     // two units in flight only while they fit in registers: from 3 tokens per pass (2 for the
-    // 8-bit formats) a second unit spills, and one unit in flight ran 10-40% faster (Q4 gate+up,
-    // Q6 and FP8 heads)
+    // 8-bit formats) a second unit spills 32-477 VGPRs and one unit in flight ran 10-40% faster
+    // (Q4 gate+up, Q6 and FP8 heads); Q6 at 2 tokens spills 8 and keeps two (4% faster)
     if (Tl >= 3 || (Tl == 2 && (fmt == kFmtFp8 || fmt == kFmtQ8))) p.depth = 1;
     while (p.waves > 1 && NU < 2 * p.waves) p.waves /= 2;
     const int64_t target_waves = 4LL * cus;
