@@ -67,8 +67,9 @@ struct Plan {
 //    unit per slice, some slices left empty (5120 x 2176, 17 units: 3 splits x 8 waves 7% faster
 //    than 2 x 8, whose one two-unit slice doubles the longest; 4 x 8 slower again).
 //
-// Vector-ALU kernel (explicit requests only): two units in flight, 4 waves per workgroup,
-// single-wave workgroups for wide matrices, splits up to about 4 waves per compute unit.
+// Vector-ALU kernel (explicit requests only): two units in flight while they fit in registers
+// (below), 4 waves per workgroup, single-wave workgroups for wide matrices, splits up to about
+// 4 waves per compute unit.
 Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
 {
     if (route == kRouteMfma) {
