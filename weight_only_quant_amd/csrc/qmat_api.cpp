@@ -94,7 +94,7 @@ Plan make_plan(int fmt, int route, int Tl, int64_t NT, int64_t NU, int cus)
             while (p.waves > 1 && NU < (int64_t)p.waves) p.waves /= 2;
             const int64_t rem = NT % cus;
             if (rem > 0) {
-                const int64_t resident = (int64_t)run_blocks_per_cu(fmt, kRouteMfma, p.depth, Tl, p.waves, (int)NU, 1) * cus;
+                const int64_t resident = (int64_t)run_blocks_per_cu(fmt, kRouteMfma, p.depth, Tl, p.waves, 1) * cus;
                 int64_t st = cus / rem;
                 if (st > (Tl == 1 ? 8 : 4)) st = Tl == 1 ? 8 : 4;
                 if (st > NU) st = NU;

@@ -60,6 +60,6 @@ hipError_t launch_dequant(int fmt, const DequantArgs &a, hipStream_t stream);
 
 // Workgroups of (64 * waves) threads of the product kernel for (fmt, route, T) that one compute
 // unit holds at once (0 on error).
-int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int NU, int S);
+int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int S);
 
 }  // namespace qmatk

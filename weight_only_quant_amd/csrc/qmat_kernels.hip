@@ -827,7 +827,7 @@ hipError_t launch_run(int fmt, int route, int depth, const RunArgs &a, int waves
                            st);
 }
 
-int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int NU, int S)
+int run_blocks_per_cu(int fmt, int route, int depth, int T, int waves, int S)
 {
     const void *k = run_kernel_for(fmt, route, T, depth, 1, false);
     int n = 0;

@@ -139,13 +139,6 @@ template <int S = 32> __device__ __forceinline__ void wave_clean(uint64_t &key, 
     }
 }
 
-// the same sort best first: the stages up to 32 leave a bitonic 64-sequence, cleaned downwards
-__device__ __forceinline__ void wave_sort_best_first(uint64_t &key, int lane)
-{
-    wave_sort<2, 32>(key, lane);
-    wave_clean(key, lane);
-}
-
 // L (sorted, best first) := the 64 best of L and Q, with Q sorted worst first: lane by lane the
 // better of the two is the upper half of a bitonic sequence, which one clean sorts
 __device__ __forceinline__ void wave_merge(uint64_t &list, uint64_t q, int lane)
@@ -365,14 +358,14 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
         // ago) are past the previous barrier, and the next round counts after this one.
         const int rn = rr == 2 ? 0 : rr + 1;
         if (threadIdx.x == 0) s_count[rn] = 0;
-        if (threadIdx.x < ntop) s_cand[threadIdx.x] = s_top[threadIdx.x];
+        if ((int)threadIdx.x < ntop) s_cand[threadIdx.x] = s_top[threadIdx.x];
         append_at_or_above(key, theta, s_cand, kCand, &s_count[rr], ntop);
         __syncthreads();
         const int C = ntop + s_count[rr];
         rr = rn;
         if (C == ntop) continue;  // nothing new; s_cand and s_top were only read
         if (C <= kCand) {
-            if (threadIdx.x < C) {
+            if ((int)threadIdx.x < C) {
                 const uint64_t c = s_cand[threadIdx.x];
                 const int r = rank_in(s_cand, C, c);
                 if (r < k) s_top[r] = c;
