@@ -6,7 +6,6 @@
 Small shapes span several 64-row tiles with a ragged last tile and odd group counts; the full
 benchmark shapes are checked on every row in the launch configuration the benchmark uses.
 """
-import os
 import sys
 
 import numpy as np

@@ -3,7 +3,6 @@ through the C ABI: two calls in a row, the second with a smaller input, on matri
 automatic plans split K across workgroups (narrow matrices, leftover row tiles) and on the
 prefill route; results must match qmat_run bit for bit (same plan, same kernels, same
 summation tree) and the oracle within the product tolerance."""
-import ctypes
 import sys
 
 import numpy as np
