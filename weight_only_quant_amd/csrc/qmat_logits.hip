@@ -17,8 +17,9 @@
 // of 8 rows per lane, the next round's loads in flight while one round is processed.  Each lane
 // keeps an online (max, sum of exp(y - max)), the sum across rounds in double.  For the top k
 // the block keeps its k best keys in LDS and theta, the k-th of them: a key below theta cannot
-// reach the top k.  The first round seeds theta with the largest of the waves' k-th best lane
-// maxima (k distinct rows reach it).  Each round the list and the keys at or above theta
+// reach the top k.  The first round seeds theta from the lane maxima: per wave the largest value
+// that k of them reach (a binary search over the value's bits, one vote per bit), the largest
+// over the waves (k distinct rows reach it).  Each round the list and the keys at or above theta
 // (usually a few dozen) go to LDS, and each candidate's rank among them, counted from LDS
 // broadcast reads, is its place in the new list: independent compares instead of the dependent
 // steps of a sort.  Rounds with more than 256 candidates (adversarial orders) take them with
@@ -27,7 +28,9 @@
 //
 // Kernel 2, one block per token, after kernel 1 (the kernel boundary makes its stores visible):
 // tau is the larger of two keys that k distinct rows reach, the largest k-th key of a block and
-// the k-th best of the blocks' best keys, so every key of the token's top k is at or above it.
+// a key that k of the blocks' best keys reach (their k-th best, or for k <= 32 the largest over
+// the waves of the value k of a wave's best keys reach), so every key of the token's top k is at
+// or above it.
 // Every block's list is loaded in one round of loads; the keys at or above tau (usually about
 // k) are ranked the same way.  The waves' states combine in double in a fixed order.  The
 // candidate set is exact and the order total, so the output is deterministic: no atomics on
@@ -340,14 +343,20 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
             key[j] = row < r1 ? make_key(v[j], row) : 0ull;
         }
         if (base == r0) {
-            // theta := the largest over the waves of the k-th best lane maximum of the wave
+            // theta := over the waves, the largest value part that at least k lane maxima of the
+            // wave reach (a binary search over its 32 bits, one compare and vote per bit), as
+            // the smallest key with that value part: k distinct rows reach it
             uint64_t mx = key[0];
 #pragma unroll
             for (int j = 1; j < kPerLane; ++j) mx = key[j] > mx ? key[j] : mx;
-            s_lm[w][lane] = mx;
-            if (lane == 0) s_thw[w] = 0;
-            __syncthreads();
-            if (rank_in(s_lm[w], 64, mx) == k - 1) s_thw[w] = mx;  // empty lane maxima tie at 0
+            const uint32_t mv = (uint32_t)(mx >> 32);  // 0 for an empty lane
+            uint32_t tv = 0;
+#pragma unroll
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t c = tv | (1u << bit);
+                if (__popcll(__ballot(mv >= c)) >= k) tv = c;
+            }
+            if (lane == 0) s_thw[w] = (uint64_t)tv << 32;
             __syncthreads();
             theta = s_thw[0];
 #pragma unroll
@@ -424,6 +433,7 @@ __global__ __launch_bounds__(kMThreads) void logits_merge_kernel(MergeArgs a)
     __shared__ double s_sum[kMWaves];
     __shared__ uint64_t s_kth[kMWaves];
     __shared__ uint64_t s_th;
+    __shared__ uint64_t s_hw[kMWaves];
     __shared__ int s_count, s_hcount;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t = blockIdx.x;
@@ -492,10 +502,31 @@ __global__ __launch_bounds__(kMThreads) void logits_merge_kernel(MergeArgs a)
 
     if (k > 0) {
         // tau: the larger of two keys that k distinct rows reach, the largest k-th entry of a
-        // list and the k-th best of the lists' best keys (tight when the lists are many): up
-        // to 256 lists each best key is ranked among all of them; beyond, among its group of
-        // 64 first, and the group winners among each other
-        if (G <= kMThreads) {
+        // list and a key that k of the lists' best keys reach (tight when the lists are many):
+        // up to 256 lists and k <= 32 a search per wave; up to 256 lists otherwise each best
+        // key is ranked among all of them; beyond, among its group of 64 first, and the group
+        // winners among each other
+        if (G <= kMThreads && k <= 32) {
+            // per wave, the largest value part that k of its lists' best keys reach (a binary
+            // search over the 32 bits, one compare and vote per bit); the largest over the waves.
+            // With up to 64 lists per wave this stays tight for k up to about half of them (at
+            // k = 64 a wave's bound would be its smallest best key).
+            const uint32_t hv = (uint32_t)(head[0] >> 32);  // 0: no list here, or an empty one
+            uint32_t tv = 0;
+#pragma unroll
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t c = tv | (1u << bit);
+                if (__popcll(__ballot(hv >= c)) >= k) tv = c;
+            }
+            if (lane == 0) s_hw[w] = (uint64_t)tv << 32;
+            __syncthreads();
+            if (i0 == 0) {
+                uint64_t th = s_hw[0];
+#pragma unroll
+                for (int i = 1; i < kMWaves; ++i) th = s_hw[i] > th ? s_hw[i] : th;
+                s_th = th;
+            }
+        } else if (G <= kMThreads) {
             if (i0 < G && head[0] != 0 && rank_in(s_h, G, head[0]) == k - 1) s_th = head[0];
         } else {
 #pragma unroll
