@@ -349,21 +349,23 @@ def test_run_logits_on_a_split_plan_and_errors():
     qm.close()
 
 
-def test_candidate_overflow_paths():
-    """Logits that overflow both kernels' candidate buffers: every block of 2048 rows holds 63
-    rows of one equal top value, so at k = 64 the block pass keeps more than 256 candidates
-    (its sorting-network path) and the merge more than 1024 (its own sorting-network path).
-    The top-k must still equal the oracle's sort, ties by row."""
+@pytest.mark.parametrize("n_equal", [63, 300])
+def test_candidate_overflow_paths(n_equal):
+    """Logits that overflow the kernels' candidate buffers: every block of 2048 rows holds
+    n_equal rows of one equal top value.  With 63, at k = 64 the merge keeps 2521 candidates
+    (more than its 1024: its sorting-network path); with 300 the block pass keeps 300 at k = 20
+    and at k = 64 (more than its 256: its sorting-network path).  The top-k must still equal
+    the oracle's sort, ties by row."""
     M, T, k = 40 * 2048, 2, 64  # 40 whole blocks of 2048 rows
     rng = np.random.default_rng(4)
     y = rng.standard_normal((T, M)).astype(np.float32)
     for t in range(T):
         for b0 in range(0, M, 2048):
             n = min(2048, M - b0)
-            rows = b0 + rng.choice(n, size=min(63, n), replace=False)
+            rows = b0 + rng.choice(n, size=min(n_equal, n), replace=False)
             y[t, rows] = 100.0 + t
     e = wq.qmat_logits_create(M, T, k)
-    say("logits candidate overflow")
+    say(f"logits candidate overflow, {n_equal} equal values per block")
     lse, vals, ids = _run(e, y, k)
     rv, ri = oracle.topk(y, k)
     assert np.array_equal(vals.astype(np.float64), rv) and np.array_equal(ids.astype(np.int64), ri)

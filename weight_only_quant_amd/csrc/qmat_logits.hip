@@ -17,9 +17,10 @@
 // of 8 rows per lane, the next round's loads in flight while one round is processed.  Each lane
 // keeps an online (max, sum of exp(y - max)), the sum across rounds in double.  For the top k
 // the block keeps its k best keys in LDS and theta, the k-th of them: a key below theta cannot
-// reach the top k.  The first round seeds theta from the lane maxima: per wave the largest value
-// that k of them reach (a binary search over the value's bits, one vote per bit), the largest
-// over the waves (k distinct rows reach it).  Each round the list and the keys at or above theta
+// reach the top k.  The first round seeds theta: per wave the largest value that k of its lane
+// maxima reach (for k > 32, k of all its keys), found by a binary search over the value's bits
+// with one vote per bit and key; the largest over the waves (k distinct rows reach it).  Each
+// round the list and the keys at or above theta
 // (usually a few dozen) go to LDS, and each candidate's rank among them, counted from LDS
 // broadcast reads, is its place in the new list: independent compares instead of the dependent
 // steps of a sort.  Rounds with more than 256 candidates (adversarial orders) take them with
@@ -284,6 +285,8 @@ __device__ __forceinline__ void block_tree_merge(uint64_t (*s_list)[64], uint64_
     }
 }
 
+// BIG_K (k > 32): the seed counts all of a wave's keys (below)
+template <bool BIG_K>
 __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
 {
     __shared__ __align__(16) uint64_t s_cand[kCand];
@@ -351,10 +354,26 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LogitsArgs a)
             for (int j = 1; j < kPerLane; ++j) mx = key[j] > mx ? key[j] : mx;
             const uint32_t mv = (uint32_t)(mx >> 32);  // 0 for an empty lane
             uint32_t tv = 0;
+            if constexpr (!BIG_K) {
 #pragma unroll
-            for (int bit = 31; bit >= 0; --bit) {
-                const uint32_t c = tv | (1u << bit);
-                if (__popcll(__ballot(mv >= c)) >= k) tv = c;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t c = tv | (1u << bit);
+                    if (__popcll(__ballot(mv >= c)) >= k) tv = c;
+                }
+            } else {
+                // for large k the lane maxima alone give a loose bound (at k = 64 their
+                // smallest): count all of the wave's keys instead
+                uint32_t kv[kPerLane];
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j) kv[j] = (uint32_t)(key[j] >> 32);
+#pragma unroll
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t c = tv | (1u << bit);
+                    int n = 0;
+#pragma unroll
+                    for (int j = 0; j < kPerLane; ++j) n += __popcll(__ballot(kv[j] >= c));
+                    if (n >= k) tv = c;
+                }
             }
             if (lane == 0) s_thw[w] = (uint64_t)tv << 32;
             __syncthreads();
@@ -604,7 +623,9 @@ hipError_t launch_logits(const LogitsArgs &a, hipStream_t st)
         return hipErrorInvalidValue;
     LogitsArgs arg = a;
     void *args[] = {&arg};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&logits_kernel), dim3((unsigned)a.B, (unsigned)a.T),
+    const void *k1 = a.k > 32 ? reinterpret_cast<const void *>(&logits_kernel<true>)
+                              : reinterpret_cast<const void *>(&logits_kernel<false>);
+    hipError_t e = hipLaunchKernel(k1, dim3((unsigned)a.B, (unsigned)a.T),
                                    dim3(kThreads), args, 0, st);
     if (e != hipSuccess) return e;
     MergeArgs m;
