@@ -57,7 +57,9 @@ def _run(e, y, k, index=None, ldy_pad=0):
 @pytest.mark.parametrize("M", [1, 5, 63, 64, 1000, 4097, 70001, 248320])
 def test_lse_topk_exact_on_synthetic_logits(M):
     e = wq.qmat_logits_create(M, 16, 64)
-    for T, k, seed, pad in [(1, 1, 1, 0), (3, 7, 2, 5), (8, 20, 3, 0), (16, 64, 4, 3), (2, 0, 5, 0)]:
+    # k = 32 / 33: the two sides of the switch to the seeds and bounds built for large k
+    for T, k, seed, pad in [(1, 1, 1, 0), (3, 7, 2, 5), (8, 20, 3, 0), (16, 64, 4, 3), (2, 0, 5, 0),
+                            (4, 32, 6, 1), (5, 33, 7, 0)]:
         say(f"logits M={M} T={T} k={k} pad={pad}")
         y = qi.logits(T, M, seed=seed + M)
         lse, vals, ids = _run(e, y, k, ldy_pad=pad)
